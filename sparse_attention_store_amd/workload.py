@@ -1,0 +1,142 @@
+"""Device-resident DSA layer state for a workload, and the layer steps through libdsa.
+
+Allocates the paged caches (one index-K cache per full layer, one latent cache per
+layer, one page table for all), fills them from the seeded device generator through the
+library's own store kernels, prepares the per-step query tensors, and runs a full or
+shared layer as a sequence of C-ABI calls on the current stream.  Plumbing only: every
+step of the method runs in libdsa's kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import dsa_inputs as gi
+
+from . import dsa
+
+LN_EPS = 1e-6
+ROPE_THETA = 10000.0
+SM_SCALE = 1.0 / 16.0      # 1 / sqrt(256), the MLA softmax scale
+TOPK = 2048
+
+
+def _runs(req: np.ndarray, pos: np.ndarray):
+    """Split (req, pos) rows into runs of consecutive positions of one request."""
+    start = 0
+    n = len(pos)
+    for i in range(1, n + 1):
+        if i == n or req[i] != req[i - 1] or pos[i] != pos[i - 1] + 1:
+            yield start, i
+            start = i
+
+
+class DeviceLayer:
+    def __init__(self, w: gi.Workload, device="cuda", latent_layers=None, k_overrides=None,
+                 populate_chunk_tokens: int = 1 << 18):
+        self.w = w
+        self.device = device
+        self.seed = w.seed
+        self.pages = dsa.Pages(torch.from_numpy(w.page_table).to(device), w.num_pages)
+        self.token_base = w.token_base
+        self.k_overrides = k_overrides or {}           # position (request 0) -> bf16[128] host
+        R = w.R
+        self.rows = dsa.Rows(torch.from_numpy(w.row_req).to(device), torch.from_numpy(w.row_pos).to(device),
+                             w.max_pos, w.rows_per_req)
+        self.layers = list(range(w.n_layers)) if latent_layers is None else list(latent_layers)
+        self.index_cache = {l: torch.zeros((w.num_pages, dsa.INDEX_PAGE_BYTES), dtype=torch.uint8, device=device)
+                            for l in w.full_layers}
+        self.latent_cache = {l: torch.zeros((w.num_pages, dsa.LATENT_PAGE_BYTES), dtype=torch.uint8, device=device)
+                             for l in self.layers}
+        self._chunk = populate_chunk_tokens
+        self.populate()
+        # per-step inputs
+        self.k_new = self._gen_token_rows(gi.T_RAW_K, 128, w.row_req, w.row_pos, override=True)
+        self.q_idx = self._gen(gi.T_IDX_Q, 0, R * 32 * 128).view(R, 32, 128)
+        self.w_head = torch.empty((R, 32), dtype=torch.float32, device=device)
+        gi.dev_uniform_f32(self.seed, gi.T_W, 0, R * 32, gi.w_scale(), self.w_head.data_ptr(), self._stream())
+        self.q_mla = {l: self._gen(gi.T_MLA_Q, l * R * 64 * 576, R * 64 * 576).view(R, 64, 576) for l in self.layers}
+        # outputs and workspaces
+        self.stride = dsa.dsa_logits_stride(w.max_pos)
+        self.q8 = torch.empty((R, 32, 128), dtype=torch.uint8, device=device)
+        self.qs = torch.empty((R, 32), dtype=torch.float32, device=device)
+        self.logits = torch.empty((R, self.stride), dtype=torch.float32, device=device)
+        self.idx = torch.empty((R, TOPK), dtype=torch.int32, device=device)
+        self.out = {l: torch.empty((R, 64, 512), dtype=torch.int16, device=device) for l in self.layers}
+        self.lse = {l: torch.empty((R, 64), dtype=torch.float32, device=device) for l in self.layers}
+        nt = dsa.dsa_topk_workspace_size(R, self.stride, TOPK)
+        self.ws_topk = torch.empty(max(nt, 256), dtype=torch.uint8, device=device)
+        nm = dsa.dsa_sparse_mla_workspace_size(R, TOPK)
+        self.ws_mla = torch.empty(max(nm, 256), dtype=torch.uint8, device=device) if nm else None
+
+    # ------------------------------------------------------------------ generation
+    def _stream(self):
+        return torch.cuda.current_stream().cuda_stream
+
+    def _gen(self, tid: int, start: int, n: int) -> torch.Tensor:
+        t = torch.empty(n, dtype=torch.int16, device=self.device)     # bf16 bit patterns
+        gi.dev_normal_bf16(self.seed, tid, start, n, t.data_ptr(), self._stream())
+        return t
+
+    def _gen_token_rows(self, tid: int, width: int, req: np.ndarray, pos: np.ndarray, override=False):
+        out = torch.empty((len(pos), width), dtype=torch.int16, device=self.device)
+        for a, b in _runs(req, pos):
+            start = (int(self.token_base[req[a]]) + int(pos[a])) * width
+            gi.dev_normal_bf16(self.seed, tid, start, (b - a) * width, out[a:b].data_ptr(), self._stream())
+        if override and self.k_overrides:
+            for i in range(len(pos)):
+                if req[i] == 0 and int(pos[i]) in self.k_overrides:
+                    out[i] = torch.from_numpy(self.k_overrides[int(pos[i])].view(np.int16)).to(self.device)
+        return out
+
+    def populate(self):
+        """Store every context position of every request into all caches."""
+        w = self.w
+        for b in range(w.B):
+            L = int(w.ctx[b])
+            for p0 in range(0, L, self._chunk):
+                p1 = min(L, p0 + self._chunk)
+                n = p1 - p0
+                req = torch.full((n,), b, dtype=torch.int32, device=self.device)
+                pos = torch.arange(p0, p1, dtype=torch.int32, device=self.device)
+                rows = dsa.Rows(req, pos, p1 - 1)
+                for l in w.full_layers:
+                    k = self._gen(gi.T_RAW_K, (int(self.token_base[b]) + p0) * 128, n * 128).view(n, 128)
+                    if b == 0 and self.k_overrides:
+                        for p, v in self.k_overrides.items():
+                            if p0 <= p < p1:
+                                k[p - p0] = torch.from_numpy(v.view(np.int16)).to(self.device)
+                    dsa.dsa_index_k_store(k, rows, self.pages, self.index_cache[l], LN_EPS, ROPE_THETA)
+                for l in self.layers:
+                    kv = self._gen(gi.T_LATENT0 + l, (int(self.token_base[b]) + p0) * 576, n * 576).view(n, 576)
+                    dsa.dsa_latent_store(kv, rows, self.pages, self.latent_cache[l])
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------ layer steps
+    def tok_rows(self) -> dsa.Rows:
+        return self.rows
+
+    def full_layer(self, layer: int = 0):
+        """Index-K store of the step's tokens, q quantisation, indexer logits, top-k, sparse MLA."""
+        dsa.dsa_index_k_store(self.k_new, self.rows, self.pages, self.index_cache[layer], LN_EPS, ROPE_THETA)
+        dsa.dsa_quant_fp8(self.q_idx, self.q8, self.qs)
+        dsa.dsa_indexer_logits(self.q8, self.qs, self.w_head, self.rows, self.pages, self.index_cache[layer],
+                               self.logits)
+        dsa.dsa_topk(self.logits, self.rows, TOPK, self.idx, self.ws_topk)
+        self.mla(layer)
+
+    def mla(self, layer: int):
+        fn = dsa.dsa_sparse_mla_prefill if self.w.rows_per_req > 64 else dsa.dsa_sparse_mla_decode
+        fn(self.q_mla[layer], self.rows, self.pages, self.latent_cache[layer], self.idx, self.out[layer],
+           self.lse[layer], self.ws_mla, SM_SCALE)
+
+    def shared_layer(self, layer: int):
+        """A shared layer reuses the last full layer's top-k tensor as is (same device pointer)."""
+        self.mla(layer)
+
+    def group_step(self):
+        for l in self.layers:
+            if l in self.w.full_layers:
+                self.full_layer(l)
+            else:
+                self.shared_layer(l)
