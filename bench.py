@@ -1,0 +1,206 @@
+"""Benchmark: one DSA layer group on one MI355X, speculative-verify decode at 128K context.
+
+Workload: 64 requests x 6 query rows (causal drafts at positions 131,066..131,071), context
+131,072 tokens, 64-token pages under a random page permutation; a 4-layer group in the
+pages' full/shared pattern (layer 0 full: index-K store of the step's tokens, q quantise,
+indexer logits, top-2048, sparse MLA; layers 1-3 shared: sparse MLA reusing layer 0's
+top-k tensor).  Every layer has its own 5.5 GB latent cache; the full layer its own
+1.1 GB index-K cache.  Inputs are seeded synthetic N(0,1) / U(0,1) at the pages' shapes,
+generated in HBM before timing.
+
+One step = one pass of that 4-layer group.  value = query tokens x layers / s (the rate at
+which query tokens pass through DSA layers); per-kernel times come from HIP events on the
+stream the kernels run on, over the whole timed region.
+
+Prints one JSON line.  --gpus N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA layer query-tokens/s at 128K ctx; indexer-cache HBM GB/s (% of peak)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA, published
+MLA_BYTES_PER_ROW = 2048 * 656 + 64 * 576 * 2 + 64 * 512 * 2 + 2048 * 4   # 1,490,944 B
+MLA_FLOPS_PER_ROW = 2 * 64 * 2048 * (576 + 512)                            # 285,212,672
+
+
+def indexer_bytes(ctx, rows):
+    """Algorithmic bytes of one indexer-logits launch: every visible key once (128 B + 4 B
+    scale), the page-table entries, and per row the fp8 query, its scales and head weights."""
+    import numpy as np
+    L = np.asarray(ctx, dtype=np.int64)
+    return int((132 * L + 4 * ((L + 63) // 64)).sum() + rows * (32 * 128 + 32 * 4 + 32 * 4))
+
+
+def cpu_baseline(w, n_layers):
+    """The oracle (as it stands) on one request of the workload, full layer + shared layers."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import dsa_inputs as gi
+    import oracle as orc
+
+    b = 0
+    rows = np.where(w.row_req == b)[0]
+    L = int(w.ctx[b])
+    npg = (L + 63) // 64
+    pt = np.arange(npg, dtype=np.int32)[None, :]       # compact pool for the one request
+    req = np.zeros(len(rows), np.int32)
+    pos = w.row_pos[rows]
+    # setup (not timed): this request's index-K cache from its raw keys
+    kraw = gi.normal_bf16(w.seed, gi.T_RAW_K, int(w.token_base[b]) * 128, L * 128).reshape(L, 128)
+    icache = np.zeros((npg, 8448), np.uint8)
+    orc.index_k_store(kraw, np.zeros(L, np.int32), np.arange(L, dtype=np.int32), pt, icache)
+    R = w.R
+    q = gi.normal_bf16(w.seed, gi.T_IDX_Q, int(rows[0]) * 32 * 128, len(rows) * 32 * 128)
+    wt = gi.uniform_f32(w.seed, gi.T_W, int(rows[0]) * 32, len(rows) * 32, gi.w_scale()).reshape(-1, 32)
+    qm = [gi.normal_bf16(w.seed, gi.T_MLA_Q, (l * R + int(rows[0])) * 64 * 576, len(rows) * 64 * 576)
+          for l in range(n_layers)]
+    knew = gi.normal_bf16(w.seed, gi.T_RAW_K, (int(w.token_base[b]) + int(pos[0])) * 128, len(rows) * 128)
+    t0 = time.perf_counter()
+    orc.index_k_store(knew.reshape(-1, 128), req, pos, pt, icache)
+    q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+    lg = orc.indexer_logits(q8.reshape(-1, 32, 128), qs.reshape(-1, 32), wt, req, pos, pt, icache)
+    idx, _ = orc.topk(lg, pos, 2048)
+    t_idx = time.perf_counter() - t0
+    # latent records of the selected positions only (setup, not timed)
+    sel = np.unique(idx[idx >= 0])
+    t_mla = 0.0
+    for l in range(n_layers):
+        kv = gi.normal_bf16_at(w.seed, gi.T_LATENT0 + l,
+                               ((int(w.token_base[b]) + sel)[:, None] * 576 + np.arange(576)[None, :]).ravel())
+        lcache = np.zeros((npg, 64 * 656), np.uint8)
+        orc.latent_store(kv.reshape(-1, 576), np.zeros(len(sel), np.int32), sel.astype(np.int32), pt, lcache)
+        t1 = time.perf_counter()
+        orc.sparse_mla(qm[l].reshape(-1, 64, 576), req, pos, pt, lcache, idx, 1.0 / 16.0)
+        t_mla += time.perf_counter() - t1
+    dt = t_idx + t_mla
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {"value": len(rows) * n_layers / dt, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"1 of {w.B} requests ({len(rows)} rows at {L} ctx): store + quant + logits + top-k + "
+                      f"{n_layers} sparse-MLA layers; {dt:.2f} s (indexer part {t_idx:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dsa_inputs as gi
+    from sparse_attention_store_amd import dsa
+    from sparse_attention_store_amd.workload import DeviceLayer
+
+    torch.cuda.set_device(0)
+    w = gi.config(2)
+    t0 = time.time()
+    D = DeviceLayer(w)
+    print(f"[bench] workload ready in {time.time() - t0:.1f} s: {w.B} requests x {w.rows_per_req} rows, "
+          f"ctx {int(w.ctx[0])}, {w.num_pages} pages, {len(D.layers)} layers", file=sys.stderr, flush=True)
+    if a.copy_probe:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    stream = torch.cuda.current_stream()
+    names = ["store", "quant", "logits", "topk", "mla0"] + [f"mla{l}" for l in D.layers[1:]]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        dsa.dsa_index_k_store(D.k_new, D.rows, D.pages, D.index_cache[0], 1e-6, 10000.0)
+        mark(1)
+        dsa.dsa_quant_fp8(D.q_idx, D.q8, D.qs)
+        mark(2)
+        dsa.dsa_indexer_logits(D.q8, D.qs, D.w_head, D.rows, D.pages, D.index_cache[0], D.logits)
+        mark(3)
+        dsa.dsa_topk(D.logits, D.rows, 2048, D.idx, D.ws_topk)
+        mark(4)
+        for j, l in enumerate(D.layers):
+            D.mla(l)          # layer 0 full, later layers shared: same idx tensor
+            mark(5 + j)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    nev = 5 + len(D.layers)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(a.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(a.steps):
+        step(evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / a.steps
+    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(a.steps)])) * 1e3
+           for i, n in enumerate(names)}                                   # microseconds
+    R, nl = w.R, len(D.layers)
+    full_us = per["store"] + per["quant"] + per["logits"] + per["topk"] + per["mla0"]
+    shared_us = float(np.mean([per[f"mla{l}"] for l in D.layers[1:]]))
+    ib = indexer_bytes(w.ctx, R)
+    mla_b = MLA_BYTES_PER_ROW * R
+    idx_gbps = ib / (per["logits"] * 1e-6) / 1e9
+    mla_gbps = mla_b / (per["mla0"] * 1e-6) / 1e9
+    mla_tflops = MLA_FLOPS_PER_ROW * R / (per["mla0"] * 1e-6) / 1e12
+    mla_total = sum(per[f"mla{l}"] for l in D.layers)
+    dominant = "mla" if mla_total > per["logits"] else "logits"
+    roof_idx = {"kernel": "k_logits_decode (dsa_indexer_logits)", "bound": "hbm", "achieved": round(idx_gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": ib, "avg_launch_us": round(per["logits"], 2)}
+    roof_mla = {"kernel": "k_sparse_mla (dsa_sparse_mla_decode)", "bound": "hbm", "achieved": round(mla_gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(mla_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": mla_b, "avg_launch_us": round(per["mla0"], 2),
+                "mfma_tflops": round(mla_tflops, 1), "mfma_frac_bf16": round(mla_tflops / BF16_PEAK_TFLOPS, 4)}
+    out = {
+        "metric": METRIC,
+        "value": R * nl / (ms_step * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 (index-K, indexer MFMA) / bf16 (MLA MFMA over fp8 latents)",
+        "data": "synthetic (seeded N(0,1) keys/latents/queries, U(0,1)/sqrt(32) head weights)",
+        "config": {"workload": "speculative verify: 64 requests x 6 rows, ctx 131072, page 64, "
+                               "4-layer group (1 full + 3 shared), top-2048",
+                   "value_def": "query tokens x DSA layers / s over the group"},
+        "roofline": roof_idx if dominant == "logits" else roof_mla,
+        "roofline_indexer": roof_idx,
+        "roofline_mla": roof_mla,
+        "indexer_cache_GBps": round(idx_gbps, 1),
+        "indexer_cache_frac_of_peak": round(idx_gbps / HBM_PEAK_GBPS, 4),
+        "full_layer_us": round(full_us, 2), "shared_layer_us": round(shared_us, 2),
+        "full_layer_query_tokens_per_s": R / (full_us * 1e-6),
+        "shared_layer_query_tokens_per_s": R / (shared_us * 1e-6),
+        "kernel_us": {k: round(v, 2) for k, v in per.items()},
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the oracle on host cores (bounded sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, nl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -78,7 +78,8 @@ def assert_logits_close(g, r, rows=None):
     assert np.all(g[~fin] == r[~fin])
     mean = np.array([np.abs(r[i][fin[i]]).mean() if fin[i].any() else 0.0 for i in range(r.shape[0])])
     tol = 1e-3 * np.abs(r) + 1e-5 * mean[:, None]
-    bad = fin & (np.abs(g - r) > tol)
+    with np.errstate(invalid="ignore"):
+        bad = fin & (np.abs(g - r) > tol)
     assert not bad.any(), f"{bad.sum()} logits out of tolerance; worst rel {np.max(np.abs(g - r)[fin] / (np.abs(r[fin]) + 1e-30)):.3g}"
 
 
