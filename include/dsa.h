@@ -183,6 +183,16 @@ size_t dsa_topk_workspace_size(int32_t R, int64_t stride, int32_t k);
 dsa_status dsa_topk(const float* logits, int64_t stride, const dsa_rows* rows, int32_t k,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
+/* Fused indexer + top-k: the same result as dsa_indexer_logits followed by dsa_topk
+ * (identical logits in `logits`, identical idx), with the logits kernel also producing the
+ * per-row logit range the top-k needs, which saves the top-k one pass over the logits.
+ * Arguments as for the two calls; ws sized by dsa_topk_workspace_size(R, stride, k).
+ * index_cache must not be NULL (a shared layer reuses the full layer's idx instead). */
+dsa_status dsa_indexer_topk(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                            const dsa_rows* rows, const dsa_pages* pt, const uint8_t* index_cache,
+                            float* logits, int64_t stride, int32_t k, int32_t* idx,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- sparse MLA */
 
 /* Workspace for dsa_sparse_mla_decode / _prefill, in bytes (may be 0). */

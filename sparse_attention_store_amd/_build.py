@@ -19,6 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["dsa_abi.hip", "k_store.hip", "k_indexer.hip", "k_topk.hip", "k_mla.hip"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form=1",     # MFMA results in VGPRs: no AGPR read-back
                "-I", os.path.join(ROOT, "include")]
 
 

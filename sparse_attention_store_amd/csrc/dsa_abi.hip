@@ -130,9 +130,36 @@ dsa_status dsa_indexer_logits(const uint8_t* q8, const float* qs, const float* w
   if (stride < dsa_logits_stride(rows->max_pos) || stride % 256)
     return fail(DSA_ERR_ARG, "dsa_indexer_logits: stride %lld < %lld or not a multiple of 256", (long long)stride,
                 (long long)dsa_logits_stride(rows->max_pos));
-  return hip_status(dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride,
+  return hip_status(dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride, nullptr,
                                                (hipStream_t)stream),
                     "dsa_indexer_logits");
+}
+
+dsa_status dsa_indexer_topk(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
+                            const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride, int32_t k,
+                            int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status st = check_rows(rows, "dsa_indexer_topk", true);
+  if (st) return st;
+  if (!cache) return fail(DSA_ERR_ARG, "dsa_indexer_topk: a shared layer has no indexer (reuse the full layer's idx)");
+  if (k < 1 || k > DSA_TOPK_MAX) return fail(DSA_ERR_ARG, "dsa_indexer_topk: k = %d not in [1, %d]", k, DSA_TOPK_MAX);
+  if (rows->n == 0) return DSA_OK;
+  if ((st = check_pages(pt, rows->max_pos, "dsa_indexer_topk"))) return st;
+  if (!q8 || !qs || !w || !logits || !idx) return fail(DSA_ERR_ARG, "dsa_indexer_topk: NULL pointer");
+  if (!aligned(q8, 16) || !aligned(cache, 16) || !aligned(logits, 16) || !aligned(qs, 4) || !aligned(w, 4) ||
+      !aligned(idx, 4))
+    return fail(DSA_ERR_ARG, "dsa_indexer_topk: misaligned pointer");
+  if (stride < dsa_logits_stride(rows->max_pos) || stride % 256)
+    return fail(DSA_ERR_ARG, "dsa_indexer_topk: stride %lld too small or not a multiple of 256", (long long)stride);
+  const size_t need = dsa_topk_workspace_size(rows->n, stride, k);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(DSA_ERR_WORKSPACE, "dsa_indexer_topk: workspace %zu B < %zu B (256-B aligned)", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dsa::launch_topk_init(rows->n, k, ws, s);
+  if (e == hipSuccess)
+    e = dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride,
+                                   dsa::topk_range_ptr(ws, rows->n, k), s);
+  if (e == hipSuccess) e = dsa::launch_topk_from_range(logits, stride, view(rows), k, idx, ws, s);
+  return hip_status(e, "dsa_indexer_topk");
 }
 
 size_t dsa_topk_workspace_size(int32_t R, int64_t stride, int32_t k) {

@@ -24,13 +24,20 @@ hipError_t launch_index_k_store(const uint16_t* k, RowsView tok, PagesView pg, u
                                 double eps, const double* inv_freq32, hipStream_t s);
 hipError_t launch_latent_store(const uint16_t* kv, RowsView tok, PagesView pg, uint8_t* cache, hipStream_t s);
 
+// range (nullable): per-row [min, max] order-preserving keys of the visible logits, merged
+// with atomicMin / atomicMax (the caller initialises it).
 hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float* w, RowsView rows,
                                  PagesView pg, const uint8_t* cache, float* logits, int64_t stride,
-                                 hipStream_t s);
+                                 uint32_t* range, hipStream_t s);
 
 size_t topk_workspace_bytes(int32_t R, int64_t stride, int32_t k);
 hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
                        void* ws, hipStream_t s);
+// Pieces of the top-k used by the fused indexer + top-k entry.
+hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s);
+uint32_t* topk_range_ptr(void* ws, int32_t R, int32_t k);
+hipError_t launch_topk_from_range(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
+                                  void* ws, hipStream_t s);
 
 size_t mla_workspace_bytes(int32_t R, int32_t k);
 hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, const uint8_t* cache,

@@ -15,12 +15,16 @@
 //  * Contraction on the FP8 MFMA v_mfma_f32_16x16x128_f8f6f4: A = 16 heads x 128 dims of
 //    q, B = 128 dims x 16 keys.  A key's 128 bytes feed the B operand directly from
 //    global memory (lane l holds bytes [16g,16g+16) and [64+16g,64+16g+16) of key l%16,
-//    g = l/16), so keys never pass through LDS; q is staged once per work-group in LDS.
+//    g = l/16), so keys never pass through LDS.
 //  * Epilogue per (row, 16-key tile): lane holds 4 heads x 1 key per head tile ->
-//    8 FMAs of w'*ReLU(c); a 3-shuffle butterfly reduce-scatter over the four lane
-//    groups leaves lane l with key l of the page, so each row's 64 logits are one
-//    coalesced 256-B store.
+//    8 FMAs of w'*ReLU(c) (ReLU as one v_med3); a reduce-scatter over the four 16-lane rows
+//    with gfx950's v_permlane32_swap / v_permlane16_swap (3 swaps + 3 adds, no LDS) leaves
+//    lane l with key l of the page, so each row's 64 logits are one coalesced 256-B store.
+//  * The q operands and head weights are staged in LDS and re-read per page, so a wave
+//    needs few registers and four waves share each SIMD to hide latency.
 //  * The next page's keys are loaded before the current page is computed.
+//  * Optionally (fused indexer + top-k) each work-group also folds the min / max of its rows'
+//    visible logits, as order-preserving 32-bit keys, into a per-row range for the top-k.
 #include "dsa_device.hpp"
 #include "dsa_internal.h"
 
@@ -28,12 +32,17 @@ namespace dsa {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kQRow = kIdxDim + 16;     // q row pitch in LDS (padding spreads LDS banks)
 
 __device__ inline i32x8 load_b_operand(const uint8_t* key_row, int g) {
   i32x4 lo = *reinterpret_cast<const i32x4*>(key_row + 16 * g);
   i32x4 hi = *reinterpret_cast<const i32x4*>(key_row + 64 + 16 * g);
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
+
+// max(x, 0) as one v_med3_f32 (fmaxf would add a NaN-quieting max per input in IEEE mode;
+// MFMA outputs here are finite).
+__device__ inline float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
 
 __device__ inline f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
   f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -57,9 +66,9 @@ __global__ void __launch_bounds__(256)
 k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
                 const int32_t* __restrict__ req, const int32_t* __restrict__ pos, DevPages pg,
                 const uint8_t* __restrict__ cache, float* __restrict__ logits, int64_t stride,
-                int chunk_pages) {
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[RG * kIdxHeads * kIdxDim];
-  __shared__ float w_lds[RG * kIdxHeads];
+                int chunk_pages, uint32_t* __restrict__ range) {
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[RG * kIdxHeads * kQRow];
+  __shared__ __attribute__((aligned(16))) float w_lds[RG * kIdxHeads];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, k16 = lane & 15;
@@ -76,63 +85,106 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
   const int64_t pend = min(min(pg0 + chunk_pages, (int64_t)(pmax >> 6) + 1), stride / 64);
 
   if (pg0 < pend) {
-    // stage q (RG x 4 KiB) and w*q_scale in LDS
-    for (int i = tid; i < RG * kIdxHeads * kIdxDim / 16; i += 256)
-      reinterpret_cast<i32x4*>(q_lds)[i] = reinterpret_cast<const i32x4*>(q8 + row0 * kIdxHeads * kIdxDim)[i];
+    // stage q (RG x 32 heads x 128 B, rows padded) and w*q_scale in LDS; the MFMA A operands
+    // and head weights are re-read from LDS for every page, which keeps the register file
+    // small enough for four waves per SIMD
+    for (int i = tid; i < RG * kIdxHeads * kIdxDim / 16; i += 256) {
+      const int row = i >> 3, c = i & 7;
+      *reinterpret_cast<i32x4*>(q_lds + row * kQRow + 16 * c) =
+          reinterpret_cast<const i32x4*>(q8 + row0 * kIdxHeads * kIdxDim)[i];
+    }
     for (int i = tid; i < RG * kIdxHeads; i += 256) w_lds[i] = w[row0 * kIdxHeads + i] * qs[row0 * kIdxHeads + i];
     __syncthreads();
 
-    i32x8 A[RG][2];
-    float wr[RG][2][4];
-#pragma unroll
-    for (int r = 0; r < RG; r++)
-#pragma unroll
-      for (int t = 0; t < 2; t++) {
-        const uint8_t* qrow = q_lds + (r * kIdxHeads + 16 * t + k16) * kIdxDim;
-        i32x4 lo = *reinterpret_cast<const i32x4*>(qrow + 16 * g);
-        i32x4 hi = *reinterpret_cast<const i32x4*>(qrow + 64 + 16 * g);
-        A[r][t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int i = 0; i < 4; i++) wr[r][t][i] = w_lds[r * kIdxHeads + 16 * t + 4 * g + i];
-      }
-
-    int64_t pi = pg0 + wave;
-    PageRegs cur, nxt;
-    int64_t cur_id = pi < pend ? page_of(pg, rq, pi * 64) : -1;
-    if (pi < pend && cur_id >= 0) load_page(cur, cache + cur_id * kIdxPageBytes, lane);
-    for (; pi < pend; pi += kWaves) {
-      const int64_t pn = pi + kWaves;
-      int64_t nxt_id = pn < pend ? page_of(pg, rq, pn * 64) : -1;
-      if (pn < pend && nxt_id >= 0) load_page(nxt, cache + nxt_id * kIdxPageBytes, lane);
+    // running min / max of the order-preserving key of this lane's visible logits over the
+    // group's rows (only kept when the fused top-k asked for row ranges; a range covering a
+    // row's keys is all the radix select needs, so the group's union serves each of its rows)
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    // score one page (held in registers) for all RG rows and store its 64 logits per row
+    auto process = [&](const PageRegs& P, int64_t pi, int64_t pid) {
+      // keep the per-page LDS reads of q / w inside the loop (hoisting them would pin all
+      // rows' operands in registers again)
+      __asm__ volatile("" ::: "memory");
       const int64_t s = pi * 64 + lane;
 #pragma unroll
       for (int r = 0; r < RG; r++) {
+        i32x8 A[2];
+        float4 wr[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          const uint8_t* qrow = q_lds + (r * kIdxHeads + 16 * t + k16) * kQRow;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(qrow + 16 * g);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(qrow + 64 + 16 * g);
+          A[t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          wr[t] = *reinterpret_cast<const float4*>(w_lds + r * kIdxHeads + 16 * t + 4 * g);
+        }
         float part[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-          f32x4 c0 = mfma_fp8(A[r][0], cur.b[t]);
-          f32x4 c1 = mfma_fp8(A[r][1], cur.b[t]);
-          float acc = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            acc = fmaf(wr[r][0][i], fmaxf(c0[i], 0.f), acc);
-            acc = fmaf(wr[r][1][i], fmaxf(c1[i], 0.f), acc);
-          }
+          const f32x4 c0 = mfma_fp8(A[0], P.b[t]);
+          const f32x4 c1 = mfma_fp8(A[1], P.b[t]);
+          float acc = wr[0].x * relu(c0[0]);
+          acc = fmaf(wr[0].y, relu(c0[1]), acc);
+          acc = fmaf(wr[0].z, relu(c0[2]), acc);
+          acc = fmaf(wr[0].w, relu(c0[3]), acc);
+          acc = fmaf(wr[1].x, relu(c1[0]), acc);
+          acc = fmaf(wr[1].y, relu(c1[1]), acc);
+          acc = fmaf(wr[1].z, relu(c1[2]), acc);
+          acc = fmaf(wr[1].w, relu(c1[3]), acc);
           part[t] = acc;
         }
-        // reduce-scatter over lane groups g: lane group g ends with tile g (key = lane)
-        const int h = g >> 1, o = g & 1;
-        float keep0 = h ? part[2] : part[0], keep1 = h ? part[3] : part[1];
-        float send0 = h ? part[0] : part[2], send1 = h ? part[1] : part[3];
-        keep0 += __shfl_xor(send0, 32, 64);
-        keep1 += __shfl_xor(send1, 32, 64);
-        float mine = o ? keep1 : keep0, other = o ? keep0 : keep1;
-        mine += __shfl_xor(other, 16, 64);
-        float v = (cur_id >= 0 && s <= prow[r]) ? mine * cur.ks : -INFINITY;
+        // reduce-scatter over the four 16-lane rows g with VALU lane swaps: lane row g ends
+        // with the head sum of tile g, i.e. key `lane` of the page
+        const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+        const float keep0 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);   // rows 0,1: tile 0; rows 2,3: tile 2
+        const float keep1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);   // rows 0,1: tile 1; rows 2,3: tile 3
+        const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(keep0), __float_as_uint(keep1), false, false);
+        const float mine = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+        const bool vis = pid >= 0 && s <= prow[r];
+        const float v = vis ? mine * P.ks : -INFINITY;
         logits[(row0 + r) * stride + s] = v;
+        if (range != nullptr && s <= prow[r]) {
+          const uint32_t u = __float_as_uint(v);
+          const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+          kmn = min(kmn, key);
+          kmx = max(kmx, key);
+        }
       }
-      cur = nxt;
-      cur_id = nxt_id;
+    };
+    // two register buffers in ping-pong: the next page loads while this one is scored
+    PageRegs pa, pb;
+    int64_t pi = pg0 + wave;
+    int64_t ida = pi < pend ? page_of(pg, rq, pi * 64) : -1;
+    if (pi < pend && ida >= 0) load_page(pa, cache + ida * kIdxPageBytes, lane);
+    for (; pi < pend; pi += 2 * kWaves) {
+      const int64_t pn = pi + kWaves;
+      const int64_t idb = pn < pend ? page_of(pg, rq, pn * 64) : -1;
+      if (pn < pend && idb >= 0) load_page(pb, cache + idb * kIdxPageBytes, lane);
+      process(pa, pi, ida);
+      if (pn >= pend) break;
+      const int64_t pn2 = pn + kWaves;
+      ida = pn2 < pend ? page_of(pg, rq, pn2 * 64) : -1;
+      if (pn2 < pend && ida >= 0) load_page(pa, cache + ida * kIdxPageBytes, lane);
+      process(pb, pn, idb);
+    }
+    if (range != nullptr) {
+      __shared__ uint32_t red[kWaves][2];
+      uint32_t mn = kmn, mx = kmx;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+      }
+      if (lane == 0) { red[wave][0] = mn; red[wave][1] = mx; }
+      __syncthreads();
+      if (tid < RG) {
+        for (int w2 = 0; w2 < kWaves; w2++) { mn = min(mn, red[w2][0]); mx = max(mx, red[w2][1]); }
+        if (mn <= mx) {
+          atomicMin(&range[2 * (row0 + tid)], mn);
+          atomicMax(&range[2 * (row0 + tid) + 1], mx);
+        }
+      }
     }
   }
   // columns of this chunk past the group's last visible page
@@ -144,7 +196,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
 
 template <int RG>
 hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsView rows, DevPages g,
-                     const uint8_t* cache, float* logits, int64_t stride, hipStream_t s) {
+                     const uint8_t* cache, float* logits, int64_t stride, uint32_t* range, hipStream_t s) {
   const int64_t n_groups = rows.n / RG;
   const int64_t total_pages = stride / 64;
   // enough work-groups to cover the chip (each page is one wave-iteration)
@@ -152,14 +204,15 @@ hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsVie
   while (chunk > 4 && n_groups * ((total_pages + chunk - 1) / chunk) < 2048) chunk >>= 1;
   const int64_t nchunks = (total_pages + chunk - 1) / chunk;
   hipLaunchKernelGGL(k_logits_decode<RG>, dim3((unsigned)nchunks, (unsigned)n_groups), dim3(256), 0, s, q8, qs, w,
-                     rows.req, rows.pos, g, cache, logits, stride, chunk);
+                     rows.req, rows.pos, g, cache, logits, stride, chunk, range);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float* w, RowsView rows, PagesView pg,
-                                 const uint8_t* cache, float* logits, int64_t stride, hipStream_t s) {
+                                 const uint8_t* cache, float* logits, int64_t stride, uint32_t* range,
+                                 hipStream_t s) {
   if (rows.n <= 0) return hipSuccess;
   DevPages g{pg.pt, pg.pt_stride, pg.num_reqs, pg.num_pages};
   // rows of a group are processed in sub-groups of the largest divisor of `group` <= 6
@@ -168,12 +221,12 @@ hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float
   for (int d = 6; d >= 1; d--)
     if (rows.group % d == 0) { rg = d; break; }
   switch (rg) {
-    case 6: return launch_rg<6>(q8, qs, w, rows, g, cache, logits, stride, s);
-    case 5: return launch_rg<5>(q8, qs, w, rows, g, cache, logits, stride, s);
-    case 4: return launch_rg<4>(q8, qs, w, rows, g, cache, logits, stride, s);
-    case 3: return launch_rg<3>(q8, qs, w, rows, g, cache, logits, stride, s);
-    case 2: return launch_rg<2>(q8, qs, w, rows, g, cache, logits, stride, s);
-    default: return launch_rg<1>(q8, qs, w, rows, g, cache, logits, stride, s);
+    case 6: return launch_rg<6>(q8, qs, w, rows, g, cache, logits, stride, range, s);
+    case 5: return launch_rg<5>(q8, qs, w, rows, g, cache, logits, stride, range, s);
+    case 4: return launch_rg<4>(q8, qs, w, rows, g, cache, logits, stride, range, s);
+    case 3: return launch_rg<3>(q8, qs, w, rows, g, cache, logits, stride, range, s);
+    case 2: return launch_rg<2>(q8, qs, w, rows, g, cache, logits, stride, range, s);
+    default: return launch_rg<1>(q8, qs, w, rows, g, cache, logits, stride, range, s);
   }
 }
 

@@ -6,17 +6,21 @@
 // by all heads and also serves as the value: "GLM-5.3 推理全链路(一)", section on the
 // decode MQA form and absorption).
 //
-// Work-group = (row, split of the row's selected keys); 4 waves; keys in tiles of 32.
+// Work-group = (row, split of the row's selected keys); 8 waves; keys in tiles of 32.
 //  * Record addresses of the split are resolved once into LDS (idx -> page table).
-//  * Each tile's 32 records (656 B each: fp8 latent, 4 scales, bf16 rope) are loaded to
-//    registers one tile ahead and written to LDS.
-//  * Phase 1 (QK, wave w owns heads 16w..16w+15): S^T[32 keys x 16 heads] on
-//    v_mfma_f32_16x16x32_bf16; the A operand is the key tile, converted fp8 -> bf16 with
-//    its block scale in one v_cvt_scalef32_pk_bf16_fp8 per pair; q stays in registers.
-//    Online softmax per head in registers (exp2 domain); P scaled by each key's block
-//    scale is written to LDS for the four value blocks.
-//  * Phase 2 (PV, wave w owns value dims 128w..128w+127 for all 64 heads): O += P_w V_w,
-//    V read transposed straight from the fp8 key tile with ds_read_b64_tr_b8.
+//  * Each tile's 32 records (656 B each: fp8 latent, 4 scales, bf16 rope) are copied from
+//    HBM straight into LDS with gfx950's global_load_lds_dwordx4, three tiles ahead of the
+//    compute (explicit vmcnt waits + raw s_barrier: a full __syncthreads() would drain the
+//    in-flight copies every tile).
+//  * Warp specialisation, one barrier per tile: waves 0-3 score tile t (S^T[32 keys x 16
+//    heads]; the 512 latent dims on the block-scaled FP8 MFMA v_mfma_scale_f32_16x16x128_
+//    f8f6f4 fed with the cached codes and their ue8m0 scales as E8M0 operands, against a
+//    two-term FP8 expansion of q that keeps bf16's precision; the 64 rope dims on the bf16
+//    MFMA), run the online softmax (exp2
+//    domain, lazy rescaling of the running max) and write P scaled by each key's block scale
+//    for the four value blocks; at the same time waves 4-7 accumulate O += P V for tile t-1
+//    (each owns 128 value dims of all 64 heads), V read transposed straight from the fp8 key
+//    tile with ds_read_b64_tr_b8.  Each SIMD so hosts one VALU-heavy and one MFMA-heavy wave.
 //  * A split's un-normalised O, running max and sum go to a workspace and a combine
 //    kernel merges the splits; with one split the kernel normalises and writes bf16.
 #include "dsa_device.hpp"
@@ -25,18 +29,17 @@
 namespace dsa {
 namespace {
 
-constexpr int kTile = 32;
-constexpr int kLatStride = 512 + 16;       // fp8 latent row in LDS (padded)
-constexpr int kRopeStride = 128 + 16;      // bf16 rope row in LDS, bytes (padded)
+constexpr int kThreads = 512;             // 4 QK waves + 4 PV waves
+constexpr int kTile = 32;                  // keys per tile
 constexpr int kChunks = kRecBytes / 16;    // 41 x 16 B per record
+constexpr int kTileChunks = kTile * kChunks;            // 1312 chunks of 16 B
+constexpr int kDmaPerWave = 3;                           // 8 waves x 3 x 64 lanes >= 1312
+constexpr int kTileBytes = 8 * kDmaPerWave * 64 * 16;    // 24 KiB (tail is padding)
+constexpr int kDepth = 2;                                // tiles in flight ahead of the QK tile
+constexpr int kBufs = kDepth + 2;                        // + the QK tile + the PV tile
 constexpr int kMaxSplitKeys = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
-
-struct TileLds {
-  uint8_t lat[kTile * kLatStride];
-  uint8_t rope[kTile * kRopeStride];
-  float sc[kTile * 4];
-};
+constexpr float kRescaleSlack = 8.0f;      // log2 units the running max may lag behind
 
 __device__ inline f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -51,233 +54,343 @@ __device__ inline bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float scale) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-struct Gather {     // one thread's share of a tile: up to 6 chunks of 16 B
-  uint4 v[6];
-};
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Work-group barrier that waits for this wave's LDS traffic only (not for outstanding
+// global->LDS copies, which the tile pipeline tracks with explicit vmcnt waits).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
-__device__ inline void gather_issue(Gather& G, const uint8_t* cache, const int* phys, int tile_base, int nkeys) {
+// Issues the global->LDS copies of one tile: LDS chunk c of the tile holds 16 B of key
+// c/41, chunk c%41 of its 656-B record (records land back to back).  Every wave issues
+// exactly kDmaPerWave copies so that per-tile vmcnt accounting is uniform; lanes past the
+// tile or of invalid keys copy from the first record of the pool into the buffer (the
+// records of invalid keys are zeroed before use).
+__device__ inline void issue_tile(const uint8_t* cache, const int* phys, int tile_base, int nkeys,
+                                  uint8_t* buf, int wave, int lane) {
 #pragma unroll
-  for (int u = 0; u < 6; u++) {
-    const int it = threadIdx.x + 256 * u;
-    G.v[u] = make_uint4(0, 0, 0, 0);
-    if (it < kTile * kChunks) {
-      const int key = it / kChunks, ch = it - key * kChunks;
+  for (int u = 0; u < kDmaPerWave; u++) {
+    const int slot = wave * kDmaPerWave + u;
+    const int c = slot * 64 + lane;
+    const uint8_t* src = cache;
+    if (c < kTileChunks) {
+      const int key = c / kChunks, ch = c - key * kChunks;
       const int j = tile_base + key;
       const int ph = j < nkeys ? phys[j] : -1;
-      if (ph >= 0) G.v[u] = *reinterpret_cast<const uint4*>(cache + (int64_t)ph * kRecBytes + 16 * ch);
+      if (ph >= 0) src = cache + (int64_t)ph * kRecBytes + 16 * ch;
     }
+    __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(buf + slot * 1024), 16, 0, 0);
   }
 }
 
-__device__ inline void gather_commit(const Gather& G, TileLds& T) {
-#pragma unroll
-  for (int u = 0; u < 6; u++) {
-    const int it = threadIdx.x + 256 * u;
-    if (it < kTile * kChunks) {
-      const int key = it / kChunks, ch = it - key * kChunks;
-      if (ch < 32) *reinterpret_cast<uint4*>(T.lat + key * kLatStride + 16 * ch) = G.v[u];
-      else if (ch == 32) *reinterpret_cast<uint4*>(T.sc + 4 * key) = G.v[u];
-      else *reinterpret_cast<uint4*>(T.rope + key * kRopeStride + 16 * (ch - 33)) = G.v[u];
-    }
-  }
-}
-
+// Warp-specialised pipeline: in iteration `it`, waves 0-3 (QK) score tile `it`, run the
+// online softmax and write P (scaled per value block) for it; waves 4-7 (PV) accumulate
+// tile it-1 with the P written one iteration earlier.  One barrier per iteration.
+//  * QK wave q owns heads 16q..16q+15 over the full 576 contraction dims (q in registers).
+//  * PV wave v owns value dims 128v..128v+127 (value block v) for all 64 heads.
 template <bool kSplit>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kThreads)
 k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, const int32_t* __restrict__ pos,
              DevPages pg, const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx, int32_t k,
              int keys_per_split, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
              float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  __shared__ TileLds tiles[2];
-  __shared__ __attribute__((aligned(16))) uint16_t pl[4][kHeads][kTile + 8];   // P scaled per value block
-  __shared__ float alpha_s[kHeads];
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[kBufs][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint16_t pl[2][4][kHeads][kTile + 8];   // P per value block
+  __shared__ float alpha_s[2][kHeads];
   __shared__ float m_s[kHeads], l_s[kHeads];
   __shared__ int phys[kMaxSplitKeys];
+  __shared__ int tile_bad[kMaxSplitKeys / kTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
+  const bool is_qk = wave < 4;
+  const int qw = wave & 3;                       // QK: head group; PV: value block
   const int r = blockIdx.y, split = blockIdx.x;
   const int j0 = split * keys_per_split;
   const int nkeys = max(0, min(keys_per_split, k - j0));
+  const int ntiles = (nkeys + kTile - 1) / kTile;
   const int p = pos[r];
   const int rq = req[r];
 
   // resolve record addresses (physical token index) of this split's keys
-  for (int j = tid; j < nkeys; j += 256) {
-    const int s = idx[(int64_t)r * k + j0 + j];
+  for (int t = tid; t < ntiles; t += kThreads) tile_bad[t] = 0;
+  __syncthreads();
+  for (int j = tid; j < ntiles * kTile; j += kThreads) {
     int ph = -1;
-    if (p >= 0 && s >= 0 && s <= p) {
-      const int64_t page = page_of(pg, rq, s);
-      if (page >= 0) ph = (int)(page * kPage + (s & 63));
+    if (j < nkeys) {
+      const int s = idx[(int64_t)r * k + j0 + j];
+      if (p >= 0 && s >= 0 && s <= p) {
+        const int64_t page = page_of(pg, rq, s);
+        if (page >= 0) ph = (int)(page * kPage + (s & 63));
+      }
     }
     phys[j] = ph;
+    if (ph < 0) tile_bad[j / kTile] = 1;
   }
-
-  // q of this wave's 16 heads as the B operand: lane holds head 16w+c16, dims 32ks+8g..+7
-  bf16x8 qb[18];
-  {
-    const uint16_t* qh = q + ((int64_t)r * kHeads + 16 * wave + c16) * kLat;
-#pragma unroll
-    for (int ks = 0; ks < 18; ks++) qb[ks] = *reinterpret_cast<const bf16x8*>(qh + 32 * ks + 8 * g);
-  }
-
-  f32x4 O[4][8];
-#pragma unroll
-  for (int a = 0; a < 4; a++)
-#pragma unroll
-    for (int b = 0; b < 8; b++) O[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;        // for head 16w + c16 (phase-1 role)
 
   __syncthreads();                              // phys ready
-  const int ntiles = (nkeys + kTile - 1) / kTile;
-  Gather G;
-  if (ntiles > 0) {
-    gather_issue(G, cache, phys, 0, nkeys);
-    gather_commit(G, tiles[0]);
-  }
-  __syncthreads();
+  for (int t = 0; t < kDepth && t < ntiles; t++) issue_tile(cache, phys, t * kTile, nkeys, tiles[t], wave, lane);
 
-  for (int t = 0; t < ntiles; t++) {
-    TileLds& T = tiles[t & 1];
-    const bool more = t + 1 < ntiles;
-    if (more) gather_issue(G, cache, phys, (t + 1) * kTile, nkeys);
-
-    // ---------------- phase 1: S^T (keys x heads) for this wave's heads
-    f32x4 s_acc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-      const int key = 16 * mt + c16;
-      const float4 ksc = *reinterpret_cast<const float4*>(T.sc + 4 * key);
-      const float kscale[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 16; ks++) {
-        const uint2 w8 = *reinterpret_cast<const uint2*>(T.lat + key * kLatStride + 32 * ks + 8 * g);
-        acc = mfma_bf16(fp8x8_to_bf16(w8.x, w8.y, kscale[ks >> 2]), qb[ks], acc);
-      }
-#pragma unroll
-      for (int ks = 16; ks < 18; ks++) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(T.rope + key * kRopeStride + 2 * (32 * (ks - 16) + 8 * g));
-        acc = mfma_bf16(a, qb[ks], acc);
-      }
-      s_acc[mt] = acc;
+  // Per-iteration prologue shared by both roles (same barriers in the same order):
+  // wait for tile `it`, barrier, issue tile it+kDepth into the buffer of tile it-2, zero the
+  // records of invalid keys of tile `it`.
+  auto prologue = [&](int it) {
+    if (it < ntiles) {
+      if (min(kDepth - 1, ntiles - 1 - it) >= 1) wait_vmcnt<kDmaPerWave>();
+      else wait_vmcnt<0>();
     }
-    // scores in log2 units; invalid keys -> -inf.  lane: keys 4g+i (+16 mt), head c16
-    float sv[2][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int j = t * kTile + 16 * mt + 4 * g + i;
-        const bool ok = j < nkeys && phys[j] >= 0;
-        sv[mt][i] = ok ? s_acc[mt][i] * sm_log2 : -INFINITY;
-        tmax = fmaxf(tmax, sv[mt][i]);
+    lds_barrier();             // tile `it` in LDS; QK(it-1) and PV(it-2) of every wave done
+    if (it + kDepth < ntiles)
+      issue_tile(cache, phys, (it + kDepth) * kTile, nkeys, tiles[(it + kDepth) % kBufs], wave, lane);
+    if (it < ntiles && tile_bad[it]) {
+      uint8_t* T = tiles[it % kBufs];
+      for (int i = tid; i < kTile * kChunks; i += kThreads) {
+        const int key = i / kChunks;
+        if (phys[it * kTile + key] < 0) *reinterpret_cast<uint4*>(T + 16 * i) = make_uint4(0, 0, 0, 0);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-    float psum = 0.f;
-    float pv[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        pv[mt][i] = (m_new == -INFINITY) ? 0.f : exp2f(sv[mt][i] - m_new);
-        psum += pv[mt][i];
-      }
-    l_part = l_part * alpha + psum;
-    m_run = m_new;
-    const int hh = 16 * wave + c16;
-    if (g == 0) alpha_s[hh] = alpha;
-    // P scaled by the value block scale of each key, bf16, for the four value blocks
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-      float4 kb[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) kb[i] = *reinterpret_cast<const float4*>(T.sc + 4 * (16 * mt + 4 * g + i));
+      lds_barrier();
+    }
+  };
+
+  if (is_qk) {
+    // ======================= QK waves: heads 16qw..16qw+15, full 576 contraction dims
+    // q of heads 16qw..16qw+15 as MFMA B operands.  The 512 latent dims are split into two
+    // FP8 terms per 128-dim block, q = hi * 2^e_hi + lo * 2^e_lo (lo quantises the residual
+    // of hi), which carries bf16's 8 significant bits; the 64 rope dims stay bf16.  Lane
+    // holds head 16qw + c16, dims 128b + [16g, 16g+16) and 128b + 64 + [16g, 16g+16).
+    i32x8 qhi[4], qlo[4];
+    int sbhi[4], sblo[4];
+    bf16x8 qr[2];
+    {
+      const uint16_t* qh = q + ((int64_t)r * kHeads + 16 * qw + c16) * kLat;
 #pragma unroll
       for (int b = 0; b < 4; b++) {
-        const float s0 = b == 0 ? kb[0].x : b == 1 ? kb[0].y : b == 2 ? kb[0].z : kb[0].w;
-        const float s1 = b == 0 ? kb[1].x : b == 1 ? kb[1].y : b == 2 ? kb[1].z : kb[1].w;
-        const float s2 = b == 0 ? kb[2].x : b == 1 ? kb[2].y : b == 2 ? kb[2].z : kb[2].w;
-        const float s3 = b == 0 ? kb[3].x : b == 1 ? kb[3].y : b == 2 ? kb[3].z : kb[3].w;
-        uint2 packed;
-        packed.x = (uint32_t)f32_to_bf16_bits(pv[mt][0] * s0) | ((uint32_t)f32_to_bf16_bits(pv[mt][1] * s1) << 16);
-        packed.y = (uint32_t)f32_to_bf16_bits(pv[mt][2] * s2) | ((uint32_t)f32_to_bf16_bits(pv[mt][3] * s3) << 16);
-        *reinterpret_cast<uint2*>(&pl[b][hh][16 * mt + 4 * g]) = packed;
+        float x[32];
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+          const uint16_t* src = qh + 128 * b + 64 * half + 16 * g;
+#pragma unroll
+          for (int c = 0; c < 2; c++) {
+            const uint4 u = *reinterpret_cast<const uint4*>(src + 8 * c);
+            const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              x[16 * half + 8 * c + 2 * i] = __uint_as_float(wds[i] << 16);
+              x[16 * half + 8 * c + 2 * i + 1] = __uint_as_float(wds[i] & 0xFFFF0000u);
+            }
+          }
+        }
+        // block amax over the 4 lanes holding this head's 128 dims (lanes c16, c16^16, ^32, ^48)
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; i++) am = fmaxf(am, fabsf(x[i]));
+        am = fmaxf(am, __shfl_xor(am, 16, 64));
+        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        const int eh = ue8m0_exponent(am);
+        const float ih = __builtin_ldexpf(1.0f, -eh), sh = __builtin_ldexpf(1.0f, eh);
+        uint32_t hw[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) hw[i] = pack4_fp8(x[4 * i] * ih, x[4 * i + 1] * ih, x[4 * i + 2] * ih, x[4 * i + 3] * ih);
+        // residual (exact in fp32: both terms carry few significant bits)
+        float am2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hw[i], false);
+          const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hw[i], true);
+          x[4 * i] -= d0[0] * sh; x[4 * i + 1] -= d0[1] * sh; x[4 * i + 2] -= d1[0] * sh; x[4 * i + 3] -= d1[1] * sh;
+#pragma unroll
+          for (int j = 0; j < 4; j++) am2 = fmaxf(am2, fabsf(x[4 * i + j]));
+        }
+        am2 = fmaxf(am2, __shfl_xor(am2, 16, 64));
+        am2 = fmaxf(am2, __shfl_xor(am2, 32, 64));
+        const int el = ue8m0_exponent(am2);
+        const float il = __builtin_ldexpf(1.0f, -el);
+        uint32_t lw[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) lw[i] = pack4_fp8(x[4 * i] * il, x[4 * i + 1] * il, x[4 * i + 2] * il, x[4 * i + 3] * il);
+        qhi[b] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
+        qlo[b] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
+        sbhi[b] = eh + 127;      // E8M0 scale operands
+        sblo[b] = el + 127;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) qr[ks] = *reinterpret_cast<const bf16x8*>(qh + kVal + 32 * ks + 8 * g);
+    }
+    float m_run = -INFINITY, l_part = 0.f;      // for head 16qw + c16
+    for (int it = 0; it <= ntiles; it++) {
+      prologue(it);
+      if (it == ntiles) break;
+      const uint8_t* T = tiles[it % kBufs];
+      const int par = it & 1;
+      // S^T (32 keys x 16 heads): lane holds keys 4g+i (+16 mt), head c16.  Latent part on the
+      // block-scaled FP8 MFMA straight from the cached codes (E8M0 scales = the records' ue8m0
+      // block scales), rope part on the bf16 MFMA.
+      f32x4 s_acc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        const uint8_t* rec = T + (16 * mt + c16) * kRecBytes;
+        const uint4 ksc = *reinterpret_cast<const uint4*>(rec + kRecScaleOff);
+        const uint32_t kbits[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const i32x4 lo4 = *reinterpret_cast<const i32x4*>(rec + 128 * b + 16 * g);
+          const i32x4 hi4 = *reinterpret_cast<const i32x4*>(rec + 128 * b + 64 + 16 * g);
+          const i32x8 a8 = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          const int sa = (int)((kbits[b] >> 23) & 0xFFu);
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, qhi[b], acc, 0, 0, 0, sa, 0, sbhi[b]);
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, qlo[b], acc, 0, 0, 0, sa, 0, sblo[b]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(rec + kRecRopeOff + 2 * (32 * ks + 8 * g));
+          acc = mfma_bf16(a, qr[ks], acc);
+        }
+        s_acc[mt] = acc;
+      }
+      float sv[2][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int j = it * kTile + 16 * mt + 4 * g + i;
+          sv[mt][i] = phys[j] >= 0 ? s_acc[mt][i] * sm_log2 : -INFINITY;
+          tmax = fmaxf(tmax, sv[mt][i]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      // lazy rescaling: the reference max only moves when the new max exceeds it by more
+      // than kRescaleSlack (exp2 of the lag stays below 2^8, harmless in fp32 / bf16)
+      float alpha = 1.f;
+      if (tmax > m_run + kRescaleSlack) {
+        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - tmax);
+        m_run = tmax;
+      }
+      const bool live = m_run != -INFINITY;
+      float psum = 0.f;
+      float pv[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          pv[mt][i] = live ? __builtin_amdgcn_exp2f(sv[mt][i] - m_run) : 0.f;
+          psum += pv[mt][i];
+        }
+      l_part = l_part * alpha + psum;
+      const int hh = 16 * qw + c16;
+      if (g == 0) alpha_s[par][hh] = alpha;
+      // P scaled by the value block scale of each key, bf16, for the four value blocks
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        float4 kb[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          kb[i] = *reinterpret_cast<const float4*>(T + (16 * mt + 4 * g + i) * kRecBytes + kRecScaleOff);
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const float s0 = b == 0 ? kb[0].x : b == 1 ? kb[0].y : b == 2 ? kb[0].z : kb[0].w;
+          const float s1 = b == 0 ? kb[1].x : b == 1 ? kb[1].y : b == 2 ? kb[1].z : kb[1].w;
+          const float s2 = b == 0 ? kb[2].x : b == 1 ? kb[2].y : b == 2 ? kb[2].z : kb[2].w;
+          const float s3 = b == 0 ? kb[3].x : b == 1 ? kb[3].y : b == 2 ? kb[3].z : kb[3].w;
+          uint2 packed;
+          packed.x = (uint32_t)f32_to_bf16_bits(pv[mt][0] * s0) | ((uint32_t)f32_to_bf16_bits(pv[mt][1] * s1) << 16);
+          packed.y = (uint32_t)f32_to_bf16_bits(pv[mt][2] * s2) | ((uint32_t)f32_to_bf16_bits(pv[mt][3] * s3) << 16);
+          *reinterpret_cast<uint2*>(&pl[par][b][hh][16 * mt + 4 * g]) = packed;
+        }
       }
     }
+    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (g == 0) { m_s[16 * qw + c16] = m_run; l_s[16 * qw + c16] = l_tot; }
     __syncthreads();
-
-    // ---------------- phase 2: O[64 heads x 128 dims of block w] += P_w V_w
-    float al[4][4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) al[ht][i] = alpha_s[16 * ht + 4 * g + i];
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++)
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) O[ht][dt][i] *= al[ht][i];
-    bf16x8 pa[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++) pa[ht] = *reinterpret_cast<const bf16x8*>(&pl[wave][16 * ht + c16][8 * g]);
-    // tr8: lane i of a 16-lane group points at key 8g + i/2, dims +8*(i%2); gets 8 keys of dim c16
-    DSA_LDS uint8_t* lat_lds = (DSA_LDS uint8_t*)T.lat;
-#pragma unroll
-    for (int dt = 0; dt < 8; dt++) {
-      const int dim0 = 128 * wave + 16 * dt;
-      DSA_LDS i32x2* src =
-          (DSA_LDS i32x2*)(lat_lds + (8 * g + (c16 >> 1)) * kLatStride + dim0 + 8 * (c16 & 1));
-      const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(src);
-      const bf16x8 vb = fp8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1], 1.0f);
-#pragma unroll
-      for (int ht = 0; ht < 4; ht++) O[ht][dt] = mfma_bf16(pa[ht], vb, O[ht][dt]);
-    }
-    if (more) gather_commit(G, tiles[(t + 1) & 1]);
-    __syncthreads();
-  }
-
-  // ---------------- finish: per-head max and sum
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (g == 0) { m_s[16 * wave + c16] = m_run; l_s[16 * wave + c16] = l_tot; }
-  __syncthreads();
-  if (!kSplit) {
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int h = 16 * ht + 4 * g + i;
-        const float l = l_s[h];
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* orow = out + ((int64_t)r * kHeads + h) * kVal + 128 * wave + c16;
-#pragma unroll
-        for (int dt = 0; dt < 8; dt++) orow[16 * dt] = f32_to_bf16_bits(O[ht][dt][i] * inv);
+    if (tid < kHeads) {
+      if (!kSplit) {
+        if (lse != nullptr) {
+          const float l = l_s[tid];
+          lse[(int64_t)r * kHeads + tid] = l > 0.f ? (m_s[tid] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+        }
+      } else {
+        const int nsplit = gridDim.x;
+        float* ml = ws_ml + (((int64_t)r * nsplit + split) * kHeads + tid) * 2;
+        ml[0] = m_s[tid];
+        ml[1] = l_s[tid];
       }
-    if (lse != nullptr && tid < kHeads) {
-      const float l = l_s[tid];
-      lse[(int64_t)r * kHeads + tid] = l > 0.f ? (m_s[tid] + log2f(l)) * 0.69314718055994531f : -INFINITY;
     }
   } else {
-    const int nsplit = gridDim.x;
-    float* wo = ws_o + (((int64_t)r * nsplit + split) * kHeads) * kVal;
+    // ======================= PV waves: value dims 128qw..128qw+127 of all 64 heads
+    f32x4 O[4][8];
 #pragma unroll
-    for (int ht = 0; ht < 4; ht++)
+    for (int a = 0; a < 4; a++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int h = 16 * ht + 4 * g + i;
+      for (int b = 0; b < 8; b++) O[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it <= ntiles; it++) {
+      prologue(it);
+      if (it == 0) continue;
+      const int par = (it - 1) & 1;
+      const uint8_t* T = tiles[(it - 1) % kBufs];
+      float al[4][4];
+      bool resc = false;
 #pragma unroll
-        for (int dt = 0; dt < 8; dt++) wo[(int64_t)h * kVal + 128 * wave + 16 * dt + c16] = O[ht][dt][i];
+      for (int ht = 0; ht < 4; ht++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          al[ht][i] = alpha_s[par][16 * ht + 4 * g + i];
+          resc |= al[ht][i] != 1.f;
+        }
+      if (__any(resc)) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ht++)
+#pragma unroll
+          for (int dt = 0; dt < 8; dt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) O[ht][dt][i] *= al[ht][i];
       }
-    if (tid < kHeads) {
-      float* ml = ws_ml + (((int64_t)r * nsplit + split) * kHeads + tid) * 2;
-      ml[0] = m_s[tid];
-      ml[1] = l_s[tid];
+      bf16x8 pa[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ht++) pa[ht] = *reinterpret_cast<const bf16x8*>(&pl[par][qw][16 * ht + c16][8 * g]);
+      // tr8: lane i of a 16-lane group points at key 8g + i/2, dims +8*(i%2); gets 8 keys of dim c16
+      DSA_LDS uint8_t* lat_lds = (DSA_LDS uint8_t*)T;
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) {
+        const int dim0 = 128 * qw + 16 * dt;
+        DSA_LDS i32x2* src = (DSA_LDS i32x2*)(lat_lds + (8 * g + (c16 >> 1)) * kRecBytes + dim0 + 8 * (c16 & 1));
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(src);
+        const bf16x8 vv = fp8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1], 1.0f);
+#pragma unroll
+        for (int ht = 0; ht < 4; ht++) O[ht][dt] = mfma_bf16(pa[ht], vv, O[ht][dt]);
+      }
+    }
+    __syncthreads();                            // m_s / l_s written by the QK waves
+    if (!kSplit) {
+#pragma unroll
+      for (int ht = 0; ht < 4; ht++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int h = 16 * ht + 4 * g + i;
+          const float l = l_s[h];
+          const float inv = l > 0.f ? 1.f / l : 0.f;
+          uint16_t* orow = out + ((int64_t)r * kHeads + h) * kVal + 128 * qw + c16;
+#pragma unroll
+          for (int dt = 0; dt < 8; dt++) orow[16 * dt] = f32_to_bf16_bits(O[ht][dt][i] * inv);
+        }
+    } else {
+      const int nsplit = gridDim.x;
+      float* wo = ws_o + (((int64_t)r * nsplit + split) * kHeads) * kVal;
+#pragma unroll
+      for (int ht = 0; ht < 4; ht++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int h = 16 * ht + 4 * g + i;
+#pragma unroll
+          for (int dt = 0; dt < 8; dt++) wo[(int64_t)h * kVal + 128 * qw + 16 * dt + c16] = O[ht][dt][i];
+        }
     }
   }
 }
@@ -332,14 +445,14 @@ hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, con
   const int kps = (k + nsplit - 1) / nsplit;
   const float sm_log2 = sm_scale * kLog2e;
   if (nsplit == 1) {
-    hipLaunchKernelGGL(k_sparse_mla<false>, dim3(1, R), dim3(256), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
+    hipLaunchKernelGGL(k_sparse_mla<false>, dim3(1, R), dim3(kThreads), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
                        kps, sm_log2, out, lse, nullptr, nullptr);
     return hipGetLastError();
   }
   if (ws == nullptr || ws_bytes < mla_workspace_bytes(R, k)) return hipErrorInvalidValue;
   float* wo = (float*)ws;
   float* wml = wo + (size_t)R * nsplit * kHeads * kVal;
-  hipLaunchKernelGGL(k_sparse_mla<true>, dim3(nsplit, R), dim3(256), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
+  hipLaunchKernelGGL(k_sparse_mla<true>, dim3(nsplit, R), dim3(kThreads), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
                      kps, sm_log2, out, lse, wo, wml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

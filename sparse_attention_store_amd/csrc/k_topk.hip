@@ -5,44 +5,58 @@
 // position is selected and the row is [0 .. pos[r], -1 ...] without reading logits
 // ("GLM-5.3 推理全链路(十一)", section on skipping the score for short contexts).
 //
-// Radix select on the order-preserving 32-bit image of each fp32 logit:
-//  1. k_hist:   grid (chunk, row) -> LDS histogram of the top 12 bits, merged into a
-//               per-row global histogram (one atomic per non-empty bin).
-//  2. k_select: grid (chunk, row) -> every work-group finds the same threshold bin T
-//               (the bin holding the k-th largest) from the histogram; elements above T
-//               are appended to the row's output list, elements in T to a candidate list
-//               (wave-aggregated atomics).
-//  3. k_final:  one work-group per row refines the low 20 bits over the candidates in
-//               LDS (two 10-bit rounds), keeps the lowest positions among exact ties at
-//               the threshold, sorts the k positions ascending and writes them.
-//               If more candidates than fit in LDS fell into T (e.g. massive ties), the
-//               same rounds run over the row in global memory instead.
+// Exact radix select on the order-preserving 32-bit image ("key") of each fp32 logit,
+// with a first digit fitted to the row's own key range so that the bin holding the k-th
+// largest value is narrow whatever the logits' scale:
+//  1. k_range:  grid (chunk, row): min / max key of the row (atomicMin / atomicMax).
+//               The fused indexer+top-k entry gets the range from the logits kernel instead.
+//  2. k_hist:   grid (chunk, row): LDS histogram of d = (key - kmin) >> shift, 4096 bins,
+//               shift chosen from the range; merged into a per-row global histogram.
+//  3. k_thresh: one work-group per row finds the threshold bin T (the bin holding the k-th
+//               largest key) from the merged histogram.
+//     k_select: grid (chunk, row): keys with d > T are selected, keys with d == T become
+//               candidates.  Appends are gathered per work-group in LDS and reserved with
+//               one global atomic per list.
+//  4. k_final:  one work-group per row resolves the low `shift` bits over the candidates in
+//               LDS (10-bit rounds), keeps the lowest positions among exact ties at the
+//               threshold, and writes the k positions in ascending order via an LDS bitmap of
+//               the row (or an LDS bitonic sort for rows too long for the bitmap).  If more
+//               candidates than fit in LDS share the threshold bin (massive exact ties), the
+//               rounds and the tie walk run over the row in global memory instead.
 #include "dsa_device.hpp"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kBins = 4096;      // 12-bit first digit
-constexpr int kCap = 4096;       // candidates kept per row
-constexpr int kChunk = 8192;     // logits per work-group in passes 1-2
+constexpr int kBins = 4096;          // first digit: 12 bits over the row's key range
+constexpr int kCap = 4096;           // candidates kept per row
+constexpr int kChunk = 8192;         // logits per work-group in passes 1-3
 constexpr int kFinalThreads = 1024;
+constexpr int kBitmapMaxN = 1 << 18; // rows up to 256K positions use the LDS bitmap (32 KiB)
 
 struct Ws {
-  int* hist;       // [R][kBins]
-  int* cnt;        // [R][4]: 0 = above count, 1 = candidate count
-  int* above;      // [R][k]
-  uint32_t* ckey;  // [R][kCap]
-  int* cpos;       // [R][kCap]
+  uint32_t* range;  // [R][2]: min key, max key
+  int* hist;        // [R][kBins]
+  int* cnt;         // [R][4]: 0 = selected-above count, 1 = candidate count, 2 = threshold bin T
+  int* above;       // [R][k]
+  uint32_t* ckey;   // [R][kCap]
+  int* cpos;        // [R][kCap]
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+__host__ __device__ inline size_t ws_bytes(int32_t R, int32_t k) {
+  return align256((size_t)R * 8) + align256((size_t)R * kBins * 4) + align256((size_t)R * 16) +
+         align256((size_t)R * k * 4) + 2 * align256((size_t)R * kCap * 4);
+}
+
 __host__ __device__ inline Ws carve(void* base, int32_t R, int32_t k) {
   uint8_t* p = (uint8_t*)base;
   Ws w;
+  w.range = (uint32_t*)p;  p += align256((size_t)R * 8);
   w.hist = (int*)p;        p += align256((size_t)R * kBins * 4);
-  w.cnt = (int*)p;         p += align256((size_t)R * 4 * 4);
+  w.cnt = (int*)p;         p += align256((size_t)R * 16);
   w.above = (int*)p;       p += align256((size_t)R * k * 4);
   w.ckey = (uint32_t*)p;   p += align256((size_t)R * kCap * 4);
   w.cpos = (int*)p;
@@ -54,40 +68,99 @@ __device__ inline uint32_t ord_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Appends for the lanes where pred holds; returns the slot (or -1).
-__device__ inline int wave_append(bool pred, int* counter) {
-  const int lane = threadIdx.x & 63;
-  uint64_t m = __ballot(pred);
-  if (m == 0) return -1;
-  int leader = __ffsll((unsigned long long)m) - 1;
-  int base = 0;
-  if (lane == leader) base = atomicAdd(counter, __popcll(m));
-  base = __shfl(base, leader, 64);
-  return pred ? base + __popcll(m & ((1ull << lane) - 1ull)) : -1;
+// shift so that (kmax - kmin) >> shift < kBins
+__device__ inline int range_shift(uint32_t kmin, uint32_t kmax) {
+  const uint32_t span = kmax - kmin;
+  const int bits = span ? 32 - __clz(span) : 0;
+  return bits > 12 ? bits - 12 : 0;
 }
 
-__global__ void k_zero(int* __restrict__ p, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+__device__ inline int64_t row_len(const int32_t* pos, int r, int64_t stride) {
+  return min((int64_t)pos[r] + 1, stride);
+}
+
+// Workspace initialisation: ranges to (max, 0), histograms and counters to 0.
+__global__ void k_init(Ws w, int32_t R) {
+  const int64_t n_hist = (int64_t)R * kBins;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_hist; i += (int64_t)gridDim.x * blockDim.x) {
+    w.hist[i] = 0;
+    if (i < (int64_t)R * 4) w.cnt[i] = 0;
+    if (i < R) { w.range[2 * i] = 0xFFFFFFFFu; w.range[2 * i + 1] = 0u; }
+  }
+}
+
+__device__ inline void block_minmax256(uint32_t& mn, uint32_t& mx, uint32_t* sh) {
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) { sh[2 * wave] = mn; sh[2 * wave + 1] = mx; }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int i = 1; i < 4; i++) { mn = min(mn, sh[2 * i]); mx = max(mx, sh[2 * i + 1]); }
+}
+
+__global__ void __launch_bounds__(256) k_range(const float* __restrict__ logits, int64_t stride,
+                                               const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+  __shared__ uint32_t sh[8];
+  const int r = blockIdx.y;
+  const int64_t n = row_len(pos, r, stride);
+  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+  if (n <= k || c0 >= n) return;
+  const int64_t c1 = min(c0 + kChunk, n);
+  const float* row = logits + (int64_t)r * stride;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int64_t i = c0 + 4 * threadIdx.x; i < c1; i += 4 * 256) {
+    const float4 v = *reinterpret_cast<const float4*>(row + i);   // c0, stride multiples of 4
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      if (i + j < c1) { const uint32_t key = ord_key(e[j]); mn = min(mn, key); mx = max(mx, key); }
+  }
+  block_minmax256(mn, mx, sh);
+  if (threadIdx.x == 0) {
+    atomicMin(&ws.range[2 * r], mn);
+    atomicMax(&ws.range[2 * r + 1], mx);
+  }
+}
+
+constexpr int kPerThread = kChunk / 256 / 4;   // float4 loads per thread per chunk (8)
+
+// Loads this thread's share of a chunk (all loads issued before any use).
+__device__ inline void load_chunk(const float* row, int64_t c0, int64_t c1, float4 (&v)[kPerThread]) {
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) {
+    const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
+    v[u] = i < c1 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 }
 
 __global__ void __launch_bounds__(256) k_hist(const float* __restrict__ logits, int64_t stride,
                                               const int32_t* __restrict__ pos, int32_t k, Ws ws) {
   __shared__ int h[kBins];
   const int r = blockIdx.y;
-  const int64_t n = min((int64_t)pos[r] + 1, stride);
+  const int64_t n = row_len(pos, r, stride);
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   if (n <= k || c0 >= n) return;
+  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
+  const int shift = range_shift(kmin, kmax);
+  const int64_t c1 = min(c0 + kChunk, n);
+  float4 v[kPerThread];
+  load_chunk(logits + (int64_t)r * stride, c0, c1, v);
   for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
   __syncthreads();
-  const int64_t c1 = min(c0 + kChunk, n);
-  const float* row = logits + (int64_t)r * stride;
-  for (int64_t i = c0 + 4 * threadIdx.x; i < c1; i += 4 * 256) {
-    float4 v = *reinterpret_cast<const float4*>(row + i);   // stride and c0 are multiples of 4
-    float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) {
+    const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
+    const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
     for (int j = 0; j < 4; j++)
-      if (i + j < c1) atomicAdd(&h[ord_key(e[j]) >> 20], 1);
+      if (i + j < c1) {
+        // keys outside [kmin, kmax] cannot occur when the range covers the row; clamp anyway
+        const uint32_t key = min(max(ord_key(e[j]), kmin), kmax);
+        atomicAdd(&h[(key - kmin) >> shift], 1);
+      }
   }
   __syncthreads();
   int* gh = ws.hist + (int64_t)r * kBins;
@@ -95,8 +168,8 @@ __global__ void __launch_bounds__(256) k_hist(const float* __restrict__ logits, 
     if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// Threshold bin of a histogram held in LDS: the bin b with count(bins > b) < k <=
-// count(bins >= b).  Returns b; *above_out = count(bins > b).  blockDim.x == NT.
+// Threshold bin of an LDS histogram: the bin b with count(bins > b) < k <= count(bins >= b).
+// result[0] = b, result[1] = count(bins > b).  blockDim.x == NT, NB % NT == 0.
 template <int NT, int NB>
 __device__ inline int find_threshold(const int* h, int k, int* scan, int* result) {
   constexpr int per = NB / NT;
@@ -105,16 +178,15 @@ __device__ inline int find_threshold(const int* h, int k, int* scan, int* result
   for (int i = 0; i < per; i++) local += h[t * per + i];
   scan[t] = local;
   __syncthreads();
-  // inclusive suffix sums over threads (Hillis-Steele)
-  for (int o = 1; o < NT; o <<= 1) {
-    int v = scan[t] + (t + o < NT ? scan[t + o] : 0);
+  for (int o = 1; o < NT; o <<= 1) {          // inclusive suffix sums (Hillis-Steele)
+    const int v = scan[t] + (t + o < NT ? scan[t + o] : 0);
     __syncthreads();
     scan[t] = v;
     __syncthreads();
   }
-  int running = scan[t] - local;    // count in bins of higher threads
+  int running = scan[t] - local;
   for (int i = per - 1; i >= 0; i--) {
-    int c = h[t * per + i];
+    const int c = h[t * per + i];
     if (running < k && running + c >= k) { result[0] = t * per + i; result[1] = running; }
     running += c;
   }
@@ -122,64 +194,105 @@ __device__ inline int find_threshold(const int* h, int k, int* scan, int* result
   return result[0];
 }
 
-__global__ void __launch_bounds__(256) k_select(const float* __restrict__ logits, int64_t stride,
-                                                const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+// Per row: the threshold bin T from the merged histogram (one work-group per row).
+__global__ void __launch_bounds__(256) k_thresh(const int32_t* __restrict__ pos, int64_t stride, int32_t k, Ws ws) {
   __shared__ int h[kBins];
   __shared__ int scan[256];
   __shared__ int res[2];
-  const int r = blockIdx.y;
-  const int64_t n = min((int64_t)pos[r] + 1, stride);
-  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-  if (n <= k || c0 >= n) return;
+  const int r = blockIdx.x;
+  if (row_len(pos, r, stride) <= k) return;
   for (int i = threadIdx.x; i < kBins; i += 256) h[i] = ws.hist[(int64_t)r * kBins + i];
   __syncthreads();
-  const uint32_t T = (uint32_t)find_threshold<256, kBins>(h, k, scan, res);
-  const int64_t c1 = min(c0 + kChunk, n);
-  const float* row = logits + (int64_t)r * stride;
-  int* cnt = ws.cnt + (int64_t)r * 4;
-  int* above = ws.above + (int64_t)r * k;
-  uint32_t* ckey = ws.ckey + (int64_t)r * kCap;
-  int* cpos = ws.cpos + (int64_t)r * kCap;
-  // uniform trip count across the block so that the wave-level ballots see every lane
-  for (int64_t b = c0; b < c1; b += 4 * 256) {
-    const int64_t i = b + 4 * threadIdx.x;
-    float e[4] = {0.f, 0.f, 0.f, 0.f};
-    if (i < c1) {
-      float4 v = *reinterpret_cast<const float4*>(row + i);
-      e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const bool valid = i + j < c1;
-      const uint32_t key = ord_key(e[j]);
-      const uint32_t bin = key >> 20;
-      int slot = wave_append(valid && bin > T, &cnt[0]);
-      if (slot >= 0 && slot < k) above[slot] = (int)(i + j);
-      slot = wave_append(valid && bin == T, &cnt[1]);
-      if (slot >= 0 && slot < kCap) { ckey[slot] = key; cpos[slot] = (int)(i + j); }
-    }
-  }
+  const int T = find_threshold<256, kBins>(h, k, scan, res);
+  if (threadIdx.x == 0) ws.cnt[(int64_t)r * 4 + 2] = T;
 }
 
-// Appends to the LDS selection list (never past its end).
+constexpr int kSelCap = 1024;    // candidates gathered per work-group before spilling to global appends
+
+__global__ void __launch_bounds__(256) k_select(const float* __restrict__ logits, int64_t stride,
+                                                const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+  __shared__ int l_above[kTopkMax];
+  __shared__ uint32_t l_ckey[kSelCap];
+  __shared__ int l_cpos[kSelCap];
+  __shared__ int n_above, n_cand, base_above, base_cand;
+  const int r = blockIdx.y;
+  const int64_t n = row_len(pos, r, stride);
+  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+  if (n <= k || c0 >= n) return;
+  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
+  const int shift = range_shift(kmin, kmax);
+  const uint32_t T = (uint32_t)ws.cnt[(int64_t)r * 4 + 2];
+  const int64_t c1 = min(c0 + kChunk, n);
+  float4 v[kPerThread];
+  load_chunk(logits + (int64_t)r * stride, c0, c1, v);
+  if (threadIdx.x == 0) { n_above = 0; n_cand = 0; }
+  __syncthreads();
+  uint32_t* ckey = ws.ckey + (int64_t)r * kCap;
+  int* cpos = ws.cpos + (int64_t)r * kCap;
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) {
+    const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
+    const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if (i + j >= c1) continue;
+      const uint32_t key = min(max(ord_key(e[j]), kmin), kmax);
+      const uint32_t d = (key - kmin) >> shift;
+      if (d > T) {
+        const int sl = atomicAdd(&n_above, 1);
+        if (sl < kTopkMax) l_above[sl] = (int)(i + j);
+      } else if (d == T) {
+        const int sl = atomicAdd(&n_cand, 1);
+        if (sl < kSelCap) {
+          l_ckey[sl] = key; l_cpos[sl] = (int)(i + j);
+        } else {                                  // rare: many ties in this chunk
+          const int gsl = atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], 1);
+          if (gsl < kCap) { ckey[gsl] = key; cpos[gsl] = (int)(i + j); }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // fewer than k keys of the whole row lie above T, so n_above < k here
+  const int nc_local = min(n_cand, kSelCap);
+  if (threadIdx.x == 0) {
+    base_above = n_above ? atomicAdd(&ws.cnt[(int64_t)r * 4], n_above) : 0;
+    base_cand = nc_local ? atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], nc_local) : 0;
+  }
+  __syncthreads();
+  int* above = ws.above + (int64_t)r * k;
+  for (int i = threadIdx.x; i < min(n_above, kTopkMax); i += 256)
+    if (base_above + i < k) above[base_above + i] = l_above[i];
+  for (int i = threadIdx.x; i < nc_local; i += 256)
+    if (base_cand + i < kCap) { ckey[base_cand + i] = l_ckey[i]; cpos[base_cand + i] = l_cpos[i]; }
+}
+
 __device__ inline void push(int* sel, int* n, int v) {
   const int s = atomicAdd(n, 1);
   if (s < kTopkMax) sel[s] = v;
 }
 
-// In-LDS bitonic sort of n (power of two) ints ascending; blockDim.x == kFinalThreads.
+// In-LDS bitonic sort of n (power of two) ints ascending.
 __device__ inline void bitonic_sort(int* a, int n) {
   for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+    for (int st = size >> 1; st > 0; st >>= 1) {
       for (int i = threadIdx.x; i < n / 2; i += kFinalThreads) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool up = ((lo & size) == 0);
-        int x = a[lo], y = a[hi];
+        const int lo = 2 * i - (i & (st - 1)), hi = lo + st;
+        const bool up = ((lo & size) == 0);
+        const int x = a[lo], y = a[hi];
         if ((x > y) == up) { a[lo] = y; a[hi] = x; }
       }
       __syncthreads();
     }
+  }
+}
+
+__device__ inline void block_scan_inclusive(int* scan, int tid) {
+  for (int o = 1; o < kFinalThreads; o <<= 1) {
+    const int v = scan[tid] + (tid >= o ? scan[tid - o] : 0);
+    __syncthreads();
+    scan[tid] = v;
+    __syncthreads();
   }
 }
 
@@ -189,89 +302,87 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
   __shared__ uint32_t skey[kCap];
   __shared__ int spos[kCap];
   __shared__ int sel[kTopkMax];
+  __shared__ uint32_t bitmap[kBitmapMaxN / 32];
   __shared__ int h[1024];
   __shared__ int scan[kFinalThreads];
   __shared__ int res[2];
   __shared__ int nsel, nties;
   const int r = blockIdx.x, tid = threadIdx.x;
-  const int64_t n = min((int64_t)pos[r] + 1, stride);
+  const int64_t n = row_len(pos, r, stride);
   int32_t* out = idx + (int64_t)r * k;
-  if (n <= k) {                       // short context (or padded row): all visible positions
+  if (n <= k) {                       // short context or padded row: every visible position
     for (int j = tid; j < k; j += kFinalThreads) out[j] = j < n ? j : -1;
     return;
   }
+  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
+  const int shift = range_shift(kmin, kmax);
   const int* cnt = ws.cnt + (int64_t)r * 4;
   const int na = min(cnt[0], k);
   const int nc = cnt[1];
-  const int need = k - na;            // >= 1 by construction of the threshold bin
+  const int need = k - na;            // >= 1: the threshold bin holds the k-th key
   const float* row = logits + (int64_t)r * stride;
   const bool in_lds = nc <= kCap;
-  if (in_lds) {
+  if (in_lds)
     for (int i = tid; i < nc; i += kFinalThreads) { skey[i] = ws.ckey[(int64_t)r * kCap + i]; spos[i] = ws.cpos[(int64_t)r * kCap + i]; }
-  }
-  for (int i = tid; i < kTopkMax; i += kFinalThreads) sel[i] = 0x7FFFFFFF;
   if (tid == 0) { nsel = 0; nties = 0; }
   __syncthreads();
-  // the first digit T is common to all candidates (nc >= 1 since need >= 1)
-  const uint32_t T = (in_lds ? skey[0] : ws.ckey[(int64_t)r * kCap]) >> 20;
+  // threshold bin, recovered from any candidate (all share it)
+  const uint32_t T = ((in_lds ? skey[0] : ws.ckey[(int64_t)r * kCap]) - kmin) >> shift;
 
-  // two 10-bit refinement rounds on bits 19..10 and 9..0
-  uint32_t prefix = T;      // known high bits
+  // resolve the low `shift` bits of (key - kmin) in rounds of at most 10 bits
+  uint32_t prefix = T;                // known high part of (key - kmin)
+  int low = shift;                    // bits still to resolve
   int need_r = need;
-  for (int round = 0; round < 2; round++) {
-    const int shift = round == 0 ? 10 : 0;
+  while (low > 0) {
+    const int take = low > 10 ? 10 : low;
+    const int sh = low - take;
     for (int i = tid; i < 1024; i += kFinalThreads) h[i] = 0;
     __syncthreads();
-    const int pshift = shift + 10;    // bits above the digit
     if (in_lds) {
-      for (int i = tid; i < nc; i += kFinalThreads)
-        if ((skey[i] >> pshift) == prefix) atomicAdd(&h[(skey[i] >> shift) & 1023], 1);
+      for (int i = tid; i < nc; i += kFinalThreads) {
+        const uint32_t v = skey[i] - kmin;
+        if ((v >> low) == prefix) atomicAdd(&h[(v >> sh) & ((1u << take) - 1)], 1);
+      }
     } else {
       for (int64_t i = tid; i < n; i += kFinalThreads) {
-        uint32_t key = ord_key(row[i]);
-        if ((key >> pshift) == prefix) atomicAdd(&h[(key >> shift) & 1023], 1);
+        const uint32_t v = min(max(ord_key(row[i]), kmin), kmax) - kmin;
+        if ((v >> low) == prefix) atomicAdd(&h[(v >> sh) & ((1u << take) - 1)], 1);
       }
     }
     __syncthreads();
     const int d = find_threshold<kFinalThreads, 1024>(h, need_r, scan, res);
     need_r -= res[1];
-    prefix = (prefix << 10) | (uint32_t)d;
+    prefix = (prefix << take) | (uint32_t)d;
+    low = sh;
     __syncthreads();
   }
-  const uint32_t thr = prefix;        // exact key of the k-th largest
-  const int need_ties = need_r;       // how many elements equal to thr to keep
-  // selected = above-bin list + candidates > thr + the lowest-position ties
+  const uint32_t thr = prefix + kmin;   // exact key of the k-th largest
+  const int need_ties = need_r;         // elements equal to thr to keep (lowest positions)
+
   for (int i = tid; i < na; i += kFinalThreads) sel[i] = ws.above[(int64_t)r * k + i];
   if (tid == 0) nsel = na;
   __syncthreads();
   if (in_lds) {
-    for (int i = tid; i < nc; i += kFinalThreads)
-      if (skey[i] > thr) push(sel, &nsel, spos[i]);
-    __syncthreads();
-    // ties: rank each tie by position among ties, keep rank < need_ties
     for (int i = tid; i < nc; i += kFinalThreads) {
-      if (skey[i] != thr) continue;
-      int rank = 0;
-      for (int j = 0; j < nc; j++) rank += (skey[j] == thr && spos[j] < spos[i]);
-      if (rank < need_ties) push(sel, &nsel, spos[i]);
+      if (skey[i] > thr) {
+        push(sel, &nsel, spos[i]);
+      } else if (skey[i] == thr) {
+        int rank = 0;                     // position rank among the exact ties
+        for (int j = 0; j < nc; j++) rank += (skey[j] == thr && spos[j] < spos[i]);
+        if (rank < need_ties) push(sel, &nsel, spos[i]);
+      }
     }
   } else {
-    // overflow: walk the row in position order; keys > thr inside bin T are taken,
-    // ties are taken in ascending position until need_ties are kept
+    // more candidates than LDS holds: walk the row in position order
     for (int64_t b = 0; b < n; b += kFinalThreads) {
       const int64_t i = b + tid;
-      uint32_t key = i < n ? ord_key(row[i]) : 0u;
-      const bool inT = i < n && (key >> 20) == T;
+      const uint32_t key = i < n ? min(max(ord_key(row[i]), kmin), kmax) : 0u;
+      const bool inT = i < n && ((key - kmin) >> shift) == T;
       if (inT && key > thr) push(sel, &nsel, (int)i);
       const int tie = (inT && key == thr) ? 1 : 0;
       scan[tid] = tie;
       __syncthreads();
-      for (int o = 1; o < kFinalThreads; o <<= 1) {        // inclusive prefix sum
-        int v = scan[tid] + (tid >= o ? scan[tid - o] : 0);
-        __syncthreads();
-        scan[tid] = v;
-        __syncthreads();
-      }
+      block_scan_inclusive(scan, tid);
       const int before = nties;
       if (tie && before + scan[tid] - 1 < need_ties) push(sel, &nsel, (int)i);
       __syncthreads();
@@ -280,35 +391,84 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
     }
   }
   __syncthreads();
-  int m = 1;
-  while (m < k) m <<= 1;
-  bitonic_sort(sel, m);
-  for (int j = tid; j < k; j += kFinalThreads) out[j] = sel[j];
+  const int ns = min(nsel, k);
+  if (n <= kBitmapMaxN) {
+    // ascending order through a bitmap of the row and a prefix count of set bits
+    const int nwords = (int)((n + 31) / 32);
+    for (int i = tid; i < nwords; i += kFinalThreads) bitmap[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < ns; i += kFinalThreads) atomicOr(&bitmap[sel[i] >> 5], 1u << (sel[i] & 31));
+    __syncthreads();
+    const int per = (nwords + kFinalThreads - 1) / kFinalThreads;      // words per thread
+    const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
+    int c = 0;
+    for (int wd = w0; wd < w1; wd++) c += __popc(bitmap[wd]);
+    scan[tid] = c;
+    __syncthreads();
+    block_scan_inclusive(scan, tid);
+    int o = scan[tid] - c;
+    for (int wd = w0; wd < w1; wd++) {
+      uint32_t m = bitmap[wd];
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1;
+        if (o < k) out[o] = wd * 32 + b;
+        o++;
+      }
+    }
+  } else {
+    for (int i = ns + tid; i < kTopkMax; i += kFinalThreads) sel[i] = 0x7FFFFFFF;
+    __syncthreads();
+    int m = 1;
+    while (m < k) m <<= 1;
+    bitonic_sort(sel, m);
+    for (int j = tid; j < k; j += kFinalThreads) out[j] = sel[j];
+  }
 }
 
 }  // namespace
 
-size_t topk_workspace_bytes(int32_t R, int64_t /*stride*/, int32_t k) {
-  return align256((size_t)R * kBins * 4) + align256((size_t)R * 16) + align256((size_t)R * k * 4) +
-         align256((size_t)R * kCap * 4) + align256((size_t)R * kCap * 4);
+size_t topk_workspace_bytes(int32_t R, int64_t /*stride*/, int32_t k) { return ws_bytes(R, k); }
+
+hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s) {
+  Ws w = carve(ws, R, k);
+  const int64_t n = (int64_t)R * kBins;
+  const int64_t grid = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(k_init, dim3((unsigned)grid), dim3(256), 0, s, w, R);
+  return hipGetLastError();
+}
+
+uint32_t* topk_range_ptr(void* ws, int32_t R, int32_t k) { return carve(ws, R, k).range; }
+
+// Passes 2-4 (the row ranges are already in the workspace).
+hipError_t launch_topk_from_range(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
+                                  void* ws, hipStream_t s) {
+  const int R = rows.n;
+  Ws w = carve(ws, R, k);
+  const int64_t visible = (int64_t)rows.max_pos + 1;
+  if (visible > k) {
+    const unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
+    hipLaunchKernelGGL(k_hist, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w);
+    hipLaunchKernelGGL(k_thresh, dim3(R), dim3(256), 0, s, rows.pos, stride, k, w);
+    hipLaunchKernelGGL(k_select, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w);
+  }
+  hipLaunchKernelGGL(k_final, dim3(R), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k, idx, w);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx, void* ws,
                        hipStream_t s) {
   const int R = rows.n;
   if (R <= 0) return hipSuccess;
-  Ws w = carve(ws, R, k);
-  const int64_t nz = (int64_t)(((uint8_t*)w.above) - ((uint8_t*)w.hist)) / 4;   // hist + counters
-  const int64_t zgrid = (nz + 255) / 256 < 4096 ? (nz + 255) / 256 : 4096;
-  hipLaunchKernelGGL(k_zero, dim3((unsigned)zgrid), dim3(256), 0, s, w.hist, nz);
+  hipError_t e = launch_topk_init(R, k, ws, s);
+  if (e != hipSuccess) return e;
   const int64_t visible = (int64_t)rows.max_pos + 1;
   if (visible > k) {
+    Ws w = carve(ws, R, k);
     const unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
-    hipLaunchKernelGGL(k_hist, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w);
-    hipLaunchKernelGGL(k_select, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w);
+    hipLaunchKernelGGL(k_range, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w);
   }
-  hipLaunchKernelGGL(k_final, dim3(R), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k, idx, w);
-  return hipGetLastError();
+  return launch_topk_from_range(logits, stride, rows, k, idx, ws, s);
 }
 
 DSA_DEFINE_ERROR_ACCESSOR(take_device_errors_topk)

@@ -67,6 +67,7 @@ def _load():
         "dsa_indexer_logits": ([p, p, p, R, P, p, p, i64, p], ctypes.c_int),
         "dsa_topk_workspace_size": ([i32, i64, i32], sz),
         "dsa_topk": ([p, i64, R, i32, p, p, sz, p], ctypes.c_int),
+        "dsa_indexer_topk": ([p, p, p, R, P, p, p, i64, i32, p, p, sz, p], ctypes.c_int),
         "dsa_sparse_mla_workspace_size": ([i32, i32], sz),
         "dsa_sparse_mla_decode": ([p, R, P, p, p, i32, f32, p, p, p, sz, p], ctypes.c_int),
         "dsa_sparse_mla_prefill": ([p, R, P, p, p, i32, f32, p, p, p, sz, p], ctypes.c_int),
@@ -82,7 +83,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("dsa_abi_version", "dsa_last_error", "dsa_layer_is_shared", "dsa_quant_fp8",
             "dsa_index_k_store", "dsa_latent_store", "dsa_logits_stride", "dsa_logits_rows_per_chunk",
-            "dsa_indexer_logits", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size",
+            "dsa_indexer_logits", "dsa_topk_workspace_size", "dsa_topk", "dsa_indexer_topk", "dsa_sparse_mla_workspace_size",
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_check_device_errors")
 
 
@@ -176,6 +177,13 @@ def dsa_topk(logits, rows: Rows, k: int, idx, ws, stream=None):
     r = rows.c()
     _check(_lib.dsa_topk(_ptr(logits), logits.shape[-1], ctypes.byref(r), k, _ptr(idx), _ptr(ws),
                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsa_indexer_topk(q8, q_scale, w, rows: Rows, pages: Pages, index_cache, logits, k: int, idx, ws, stream=None):
+    r, p = rows.c(), pages.c()
+    _check(_lib.dsa_indexer_topk(_ptr(q8), _ptr(q_scale), _ptr(w), ctypes.byref(r), ctypes.byref(p),
+                                 _ptr(index_cache), _ptr(logits), logits.shape[-1], k, _ptr(idx), _ptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dsa_sparse_mla_workspace_size(R: int, k: int) -> int:

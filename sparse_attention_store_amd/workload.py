@@ -120,10 +120,12 @@ class DeviceLayer:
         """Index-K store of the step's tokens, q quantisation, indexer logits, top-k, sparse MLA."""
         dsa.dsa_index_k_store(self.k_new, self.rows, self.pages, self.index_cache[layer], LN_EPS, ROPE_THETA)
         dsa.dsa_quant_fp8(self.q_idx, self.q8, self.qs)
-        dsa.dsa_indexer_logits(self.q8, self.qs, self.w_head, self.rows, self.pages, self.index_cache[layer],
-                               self.logits)
-        dsa.dsa_topk(self.logits, self.rows, TOPK, self.idx, self.ws_topk)
+        self.indexer_topk(layer)
         self.mla(layer)
+
+    def indexer_topk(self, layer: int = 0):
+        dsa.dsa_indexer_topk(self.q8, self.qs, self.w_head, self.rows, self.pages, self.index_cache[layer],
+                             self.logits, TOPK, self.idx, self.ws_topk)
 
     def mla(self, layer: int):
         fn = dsa.dsa_sparse_mla_prefill if self.w.rows_per_req > 64 else dsa.dsa_sparse_mla_decode

@@ -254,3 +254,19 @@ def test_bad_page_id_is_flagged_not_dereferenced():
         dsa.dsa_check_device_errors()
     assert e.value.status == 5
     dsa.dsa_check_device_errors()                          # the flag was cleared
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_fused_indexer_topk_equals_separate_calls(cid):
+    _announce(f"fused indexer+topk c{cid}")
+    w = gi.config(cid, "small")
+    L = DeviceLayer(w)
+    dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
+    L.indexer_topk(0)
+    torch.cuda.synchronize()
+    fused_logits, fused_idx = host(L.logits).copy(), host(L.idx).copy()
+    dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
+    dsa.dsa_topk(L.logits, L.rows, 2048, L.idx, L.ws_topk)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(L.logits), fused_logits)
+    assert np.array_equal(host(L.idx), fused_idx)
