@@ -36,7 +36,7 @@
  *    656 B/token/layer; the rope tail stays bf16 in this reading).
  *  - Page table: int32 [num_reqs][pt_stride]; logical position p of request b is
  *    page page_table[b][p / 64], slot p % 64.  One table serves both caches and all
- *    layers ([REQ] §prefix cache: both pools share page ids).
+ *    layers ([REQ] §第九阶段, 细节二: both pools share page ids).
  *  - FP8 is OCP E4M3 (e4m3fn), round-to-nearest-even, saturating at +-448; a ue8m0
  *    scale is the smallest power of two s with max|x| <= 448 s (1 for an all-zero
  *    block), stored as fp32.
@@ -183,9 +183,12 @@ size_t dsa_topk_workspace_size(int32_t R, int64_t stride, int32_t k);
 dsa_status dsa_topk(const float* logits, int64_t stride, const dsa_rows* rows, int32_t k,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
-/* Fused indexer + top-k: the same result as dsa_indexer_logits followed by dsa_topk
- * (identical logits in `logits`, identical idx), with the logits kernel also producing the
- * per-row logit range the top-k needs, which saves the top-k one pass over the logits.
+/* Fused indexer + top-k: the same idx as dsa_indexer_logits followed by dsa_topk, with the
+ * logits kernel also producing the per-row logit range the top-k needs, which saves the
+ * top-k one pass over the logits.  `logits` is scratch here: it holds the same values as
+ * dsa_indexer_logits would write, except that a row group (rows->group consecutive rows)
+ * whose rows all have pos + 1 <= k is not scored at all and its logits rows are left as
+ * they were ([IDXC] §优化二:短上下文直接跳过打分: such rows select every position).
  * Arguments as for the two calls; ws sized by dsa_topk_workspace_size(R, stride, k).
  * index_cache must not be NULL (a shared layer reuses the full layer's idx instead). */
 dsa_status dsa_indexer_topk(const uint8_t* q_fp8, const float* q_scale, const float* w,

@@ -130,7 +130,7 @@ dsa_status dsa_indexer_logits(const uint8_t* q8, const float* qs, const float* w
   if (stride < dsa_logits_stride(rows->max_pos) || stride % 256)
     return fail(DSA_ERR_ARG, "dsa_indexer_logits: stride %lld < %lld or not a multiple of 256", (long long)stride,
                 (long long)dsa_logits_stride(rows->max_pos));
-  return hip_status(dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride, nullptr,
+  return hip_status(dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride, nullptr, 0,
                                                (hipStream_t)stream),
                     "dsa_indexer_logits");
 }
@@ -157,7 +157,7 @@ dsa_status dsa_indexer_topk(const uint8_t* q8, const float* qs, const float* w, 
   hipError_t e = dsa::launch_topk_init(rows->n, k, ws, s);
   if (e == hipSuccess)
     e = dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride,
-                                   dsa::topk_range_ptr(ws, rows->n, k), s);
+                                   dsa::topk_range_ptr(ws, rows->n, k), k, s);
   if (e == hipSuccess) e = dsa::launch_topk_from_range(logits, stride, view(rows), k, idx, ws, s);
   return hip_status(e, "dsa_indexer_topk");
 }

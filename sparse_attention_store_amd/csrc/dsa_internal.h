@@ -25,10 +25,11 @@ hipError_t launch_index_k_store(const uint16_t* k, RowsView tok, PagesView pg, u
 hipError_t launch_latent_store(const uint16_t* kv, RowsView tok, PagesView pg, uint8_t* cache, hipStream_t s);
 
 // range (nullable): per-row [min, max] order-preserving keys of the visible logits, merged
-// with atomicMin / atomicMax (the caller initialises it).
+// with atomicMin / atomicMax (the caller initialises it).  skip_upto: row groups whose rows
+// all have pos + 1 <= skip_upto are not scored and their logits are not written (0: none).
 hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float* w, RowsView rows,
                                  PagesView pg, const uint8_t* cache, float* logits, int64_t stride,
-                                 uint32_t* range, hipStream_t s);
+                                 uint32_t* range, int32_t skip_upto, hipStream_t s);
 
 size_t topk_workspace_bytes(int32_t R, int64_t stride, int32_t k);
 hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,

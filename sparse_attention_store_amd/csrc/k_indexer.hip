@@ -24,7 +24,9 @@
 //    needs few registers and four waves share each SIMD to hide latency.
 //  * The next page's keys are loaded before the current page is computed.
 //  * Optionally (fused indexer + top-k) each work-group also folds the min / max of its rows'
-//    visible logits, as order-preserving 32-bit keys, into a per-row range for the top-k.
+//    visible logits, as order-preserving 32-bit keys, into a per-row range for the top-k, and
+//    skips row groups whose rows all see no more keys than the top-k keeps ("GLM-5.3
+//    推理全链路(十一)", section 优化二: short contexts skip the score).
 #include "dsa_device.hpp"
 #include "dsa_internal.h"
 
@@ -66,7 +68,7 @@ __global__ void __launch_bounds__(256)
 k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
                 const int32_t* __restrict__ req, const int32_t* __restrict__ pos, DevPages pg,
                 const uint8_t* __restrict__ cache, float* __restrict__ logits, int64_t stride,
-                int chunk_pages, uint32_t* __restrict__ range) {
+                int chunk_pages, uint32_t* __restrict__ range, int skip_upto) {
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[RG * kIdxHeads * kQRow];
   __shared__ __attribute__((aligned(16))) float w_lds[RG * kIdxHeads];
 
@@ -80,6 +82,9 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
   int pmax = -1;
 #pragma unroll
   for (int r = 0; r < RG; r++) { prow[r] = pos[row0 + r]; pmax = max(pmax, prow[r]); }
+  // every row of the group sees at most skip_upto keys: its top-k is all of them and needs
+  // no score (the fused indexer + top-k passes k here; nothing of the group is written)
+  if (pmax + 1 <= skip_upto) return;
   const int32_t rq = req[row0];
   // pages with a visible key (never past the logits row)
   const int64_t pend = min(min(pg0 + chunk_pages, (int64_t)(pmax >> 6) + 1), stride / 64);
@@ -196,7 +201,8 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
 
 template <int RG>
 hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsView rows, DevPages g,
-                     const uint8_t* cache, float* logits, int64_t stride, uint32_t* range, hipStream_t s) {
+                     const uint8_t* cache, float* logits, int64_t stride, uint32_t* range, int skip_upto,
+                     hipStream_t s) {
   const int64_t n_groups = rows.n / RG;
   const int64_t total_pages = stride / 64;
   // enough work-groups to cover the chip (each page is one wave-iteration)
@@ -204,7 +210,7 @@ hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsVie
   while (chunk > 4 && n_groups * ((total_pages + chunk - 1) / chunk) < 2048) chunk >>= 1;
   const int64_t nchunks = (total_pages + chunk - 1) / chunk;
   hipLaunchKernelGGL(k_logits_decode<RG>, dim3((unsigned)nchunks, (unsigned)n_groups), dim3(256), 0, s, q8, qs, w,
-                     rows.req, rows.pos, g, cache, logits, stride, chunk, range);
+                     rows.req, rows.pos, g, cache, logits, stride, chunk, range, skip_upto);
   return hipGetLastError();
 }
 
@@ -212,7 +218,7 @@ hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsVie
 
 hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float* w, RowsView rows, PagesView pg,
                                  const uint8_t* cache, float* logits, int64_t stride, uint32_t* range,
-                                 hipStream_t s) {
+                                 int32_t skip_upto, hipStream_t s) {
   if (rows.n <= 0) return hipSuccess;
   DevPages g{pg.pt, pg.pt_stride, pg.num_reqs, pg.num_pages};
   // rows of a group are processed in sub-groups of the largest divisor of `group` <= 6
@@ -221,12 +227,12 @@ hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float
   for (int d = 6; d >= 1; d--)
     if (rows.group % d == 0) { rg = d; break; }
   switch (rg) {
-    case 6: return launch_rg<6>(q8, qs, w, rows, g, cache, logits, stride, range, s);
-    case 5: return launch_rg<5>(q8, qs, w, rows, g, cache, logits, stride, range, s);
-    case 4: return launch_rg<4>(q8, qs, w, rows, g, cache, logits, stride, range, s);
-    case 3: return launch_rg<3>(q8, qs, w, rows, g, cache, logits, stride, range, s);
-    case 2: return launch_rg<2>(q8, qs, w, rows, g, cache, logits, stride, range, s);
-    default: return launch_rg<1>(q8, qs, w, rows, g, cache, logits, stride, range, s);
+    case 6: return launch_rg<6>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
+    case 5: return launch_rg<5>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
+    case 4: return launch_rg<4>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
+    case 3: return launch_rg<3>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
+    case 2: return launch_rg<2>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
+    default: return launch_rg<1>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
   }
 }
 

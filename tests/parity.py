@@ -115,3 +115,46 @@ def assert_attention_close(g_bits, r_bits, atol=2e-2, rtol=1e-2):
     tol = atol + rtol * np.abs(r)
     assert np.all(err <= tol), f"{(err > tol).sum()} outputs out of tolerance, max err {err.max():.3g}"
     return float(err.max())
+
+
+# ----------------------------------------------------------------------------- one request at a time
+# At full size the oracle works on sampled rows: it rebuilds only the sampled request's index-K
+# cache and only the selected latent records, in a compact page pool of that request alone
+# (page i of the request is pool page i; the result does not depend on page placement).
+def request_pool(w: gi.Workload, b: int):
+    npg = (int(w.ctx[b]) + 63) // 64
+    return np.arange(npg, dtype=np.int32)[None, :], npg
+
+
+def oracle_index_cache_of(w: gi.Workload, b: int, overrides=None):
+    L = int(w.ctx[b])
+    pt, npg = request_pool(w, b)
+    k = gi.normal_bf16(w.seed, gi.T_RAW_K, int(w.token_base[b]) * 128, L * 128).reshape(L, 128)
+    if b == 0:
+        for p, v in (overrides or {}).items():
+            k[p] = v
+    cache = np.zeros((npg, 8448), np.uint8)
+    orc.index_k_store(k, np.zeros(L, np.int32), np.arange(L, dtype=np.int32), pt, cache, LN_EPS, THETA)
+    return cache, pt
+
+
+def oracle_latent_cache_of(w: gi.Workload, b: int, layer: int, positions):
+    pt, npg = request_pool(w, b)
+    positions = np.asarray(positions).ravel()
+    sel = np.unique(positions[positions >= 0]).astype(np.int64)
+    cache = np.zeros((npg, 64 * 656), np.uint8)
+    if len(sel):
+        flat = ((int(w.token_base[b]) + sel)[:, None] * 576 + np.arange(576)[None, :]).ravel()
+        kv = gi.normal_bf16_at(w.seed, gi.T_LATENT0 + layer, flat).reshape(-1, 576)
+        orc.latent_store(kv, np.zeros(len(sel), np.int32), sel.astype(np.int32), pt, cache)
+    return cache, pt
+
+
+def row_queries(w: gi.Workload, rows, layers):
+    """Indexer q, head weights and MLA q of the given rows only (same values as queries())."""
+    rows = [int(r) for r in rows]
+    q = np.stack([gi.normal_bf16(w.seed, gi.T_IDX_Q, r * 32 * 128, 32 * 128) for r in rows]).reshape(-1, 32, 128)
+    wt = np.stack([gi.uniform_f32(w.seed, gi.T_W, r * 32, 32, gi.w_scale()) for r in rows])
+    qm = {l: np.stack([gi.normal_bf16(w.seed, gi.T_MLA_Q, (l * w.R + r) * 64 * 576, 64 * 576)
+                       for r in rows]).reshape(-1, 64, 576) for l in layers}
+    return q, wt, qm

@@ -1,0 +1,203 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark uses.
+
+The GPU runs the whole layer (group) over every request; the oracle recomputes sampled rows
+from the same seeds (only the sampled request's index-K cache and only the selected latent
+records are rebuilt on the host).  Also: the short-context path (no scoring when a row sees
+at most k positions) and a single-request context sweep from 1K to 128K.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as gi
+import oracle as orc
+from parity import (SM, assert_attention_close, assert_logits_close, needle_overrides, oracle_index_cache,
+                    oracle_index_cache_of, oracle_latent_cache, oracle_latent_cache_of, queries, row_queries,
+                    topk_sets_match)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from sparse_attention_store_amd import dsa  # noqa: E402
+from sparse_attention_store_amd.workload import DeviceLayer  # noqa: E402
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def take(t, rows):
+    """Rows of a device tensor, gathered on the device, as a host array."""
+    return host(t[torch.as_tensor(np.asarray(rows), dtype=torch.long, device=t.device)])
+
+
+def _announce(name):
+    print(f"\n[gpu] {name}", flush=True)
+
+
+def _release(L):
+    del L
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def check_sampled_rows(w, L, rows, overrides=None, min_same_frac=0.9):
+    """Every sampled row: q quantisation bit-exact, logits within tolerance, top-k set equal
+    (near-ties excepted), and each layer's attention output against the oracle."""
+    rows = np.asarray(sorted(set(int(r) for r in rows)))
+    n_same = 0
+    for b in np.unique(w.row_req[rows]):
+        rs = rows[w.row_req[rows] == b]
+        cache, pt = oracle_index_cache_of(w, int(b), overrides)
+        q, wt, qm = row_queries(w, rs, L.layers)
+        q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+        assert np.array_equal(take(L.q8, rs).reshape(-1, 128), q8)
+        assert np.array_equal(take(L.qs, rs).reshape(-1), qs)
+        pos = w.row_pos[rs]
+        req0 = np.zeros(len(rs), np.int32)
+        lg = orc.indexer_logits(q8.reshape(-1, 32, 128), qs.reshape(-1, 32), wt, req0, pos, pt, cache)
+        ridx, kth = orc.topk(lg, pos, 2048)
+        gidx = take(L.idx, rs)
+        long_rows = pos + 1 > 2048              # short rows are not scored by the fused call
+        if long_rows.any():
+            g_lg = take(L.logits, rs[long_rows])
+            ow = lg.shape[1]
+            assert_logits_close(g_lg[:, :ow], lg[long_rows])
+            assert np.all(np.isneginf(g_lg[:, ow:]))
+        topk_sets_match(gidx, ridx, lg, kth)
+        same = np.array([set(gidx[i]) == set(ridx[i]) for i in range(len(rs))])
+        n_same += int(same.sum())
+        for l in L.layers:
+            lat, _ = oracle_latent_cache_of(w, int(b), l, ridx)
+            ref, rlse = orc.sparse_mla(qm[l], req0, pos, pt, lat, ridx, SM)
+            assert_attention_close(take(L.out[l], rs)[same], ref[same])
+            assert np.allclose(take(L.lse[l], rs)[same], rlse[same], rtol=1e-4, atol=1e-4)
+    assert n_same >= min_same_frac * len(rows), f"only {n_same}/{len(rows)} rows have the oracle's exact set"
+    return n_same
+
+
+def test_full_c1_decode_batch_every_row():
+    _announce("full size c1: 32 requests, ctx 8K-32K, every row")
+    w = gi.config(1, "full")
+    L = DeviceLayer(w)
+    L.group_step()
+    torch.cuda.synchronize()
+    check_sampled_rows(w, L, range(w.R))
+    dsa.dsa_check_device_errors()
+    _release(L)
+
+
+def test_full_c2_verify_128k_sampled_requests():
+    _announce("full size c2: 64 x 6 rows at 128K, 4-layer group, 8 sampled requests")
+    w = gi.config(2, "full")
+    L = DeviceLayer(w)
+    L.group_step()
+    torch.cuda.synchronize()
+    reqs = [0, 1, 17, 31, 32, 47, 62, 63]
+    rows = [r for r in range(w.R) if int(w.row_req[r]) in reqs]
+    check_sampled_rows(w, L, rows)
+    dsa.dsa_check_device_errors()
+    _release(L)
+
+
+def test_full_c3_long_1m_needles():
+    _announce("full size c3: 1 request at 1M context, 2048 needles")
+    w = gi.config(3, "full")
+    ov = needle_overrides(w)
+    L = DeviceLayer(w, k_overrides=ov)
+    L.group_step()
+    torch.cuda.synchronize()
+    gidx = host(L.idx)[0]
+    assert np.array_equal(gidx, np.sort(w.needles)), "top-k must be exactly the needle set, ascending"
+    check_sampled_rows(w, L, [0], overrides=ov, min_same_frac=1.0)
+    dsa.dsa_check_device_errors()
+    _release(L)
+
+
+def test_full_c4_chunked_prefill_sampled_rows():
+    _announce("full size c4: 8192 prefill rows on a 65,536 prefix, 24 sampled rows")
+    w = gi.config(4, "full")
+    L = DeviceLayer(w)
+    L.group_step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    rows = [0, 1, 2, 63, 64, 4095, 8190, 8191] + list(rng.choice(w.R, 16, replace=False))
+    check_sampled_rows(w, L, rows)
+    dsa.dsa_check_device_errors()
+    _release(L)
+
+
+def test_short_context_rows_skip_scoring():
+    """Rows seeing at most k positions take every position and are not scored by the fused
+    call (their logits rows stay untouched); the separate logits call still scores them."""
+    _announce("short-context path (mixed batch)")
+    w = gi.make_decode("short_mix", gi.SEED_BASE + 40, [1000, 2048, 2049, 5000, 64, 1, 2047])
+    L = DeviceLayer(w)
+    L.logits.fill_(float("nan"))
+    dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
+    L.indexer_topk(0)
+    for l in L.layers:
+        L.mla(l)
+    torch.cuda.synchronize()
+    cache = oracle_index_cache(w)
+    q, wt, qm = queries(w, L.layers)
+    q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+    lg = orc.indexer_logits(q8.reshape(-1, 32, 128), qs.reshape(-1, 32), wt, w.row_req, w.row_pos,
+                            w.page_table, cache)
+    ridx, kth = orc.topk(lg, w.row_pos, 2048)
+    gidx, glg = host(L.idx), host(L.logits)
+    short = w.row_pos + 1 <= 2048
+    for r in range(w.R):
+        if short[r]:
+            p = int(w.row_pos[r])
+            assert np.array_equal(gidx[r, :p + 1], np.arange(p + 1)) and np.all(gidx[r, p + 1:] == -1)
+            assert np.all(np.isnan(glg[r])), f"row {r} (pos {p}) was scored"
+        else:
+            assert_logits_close(glg[r:r + 1], lg[r:r + 1])
+    topk_sets_match(gidx, ridx, lg, kth)                 # differences only at near-ties
+    same = np.array([set(gidx[r]) == set(ridx[r]) for r in range(w.R)])
+    assert same[short].all() and same.sum() >= w.R - 1
+    lat = oracle_latent_cache(w, 0)
+    ref, _ = orc.sparse_mla(qm[0], w.row_req, w.row_pos, w.page_table, lat, ridx, SM)
+    assert_attention_close(host(L.out[0])[same], ref[same])
+    # the plain logits call scores every row, short ones included
+    dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
+    torch.cuda.synchronize()
+    assert_logits_close(host(L.logits), lg)
+    dsa.dsa_check_device_errors()
+
+
+def test_short_group_of_six_rows():
+    """A request whose six draft rows all sit below k is skipped as a group; the next one is scored."""
+    _announce("short-context path (groups of 6)")
+    w = gi.make_decode("short_groups", gi.SEED_BASE + 41, [2000, 2051, 3000], rows_per_req=6)
+    L = DeviceLayer(w)
+    L.logits.fill_(float("nan"))
+    dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
+    L.indexer_topk(0)
+    torch.cuda.synchronize()
+    cache = oracle_index_cache(w)
+    q, wt, _ = queries(w, [])
+    q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+    lg = orc.indexer_logits(q8.reshape(-1, 32, 128), qs.reshape(-1, 32), wt, w.row_req, w.row_pos,
+                            w.page_table, cache)
+    ridx, kth = orc.topk(lg, w.row_pos, 2048)
+    gidx, glg = host(L.idx), host(L.logits)
+    assert np.all(np.isnan(glg[:6]))                       # request 0: every row short -> not scored
+    assert_logits_close(glg[6:], lg[6:])                   # request 1 mixes short and long rows
+    topk_sets_match(gidx, ridx, lg, kth)                   # differences only at near-ties
+    assert np.array_equal(gidx[:6], ridx[:6])
+
+
+@pytest.mark.parametrize("ctx", [1024, 2048, 2049, 4096, 16384, 131072])
+def test_context_sweep_single_request(ctx):
+    _announce(f"context sweep: 1 request, ctx {ctx}")
+    w = gi.make_decode(f"sweep_{ctx}", gi.SEED_BASE + 50, [ctx])
+    L = DeviceLayer(w)
+    L.group_step()
+    torch.cuda.synchronize()
+    check_sampled_rows(w, L, [0], min_same_frac=1.0)
+    dsa.dsa_check_device_errors()
+    _release(L)
