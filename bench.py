@@ -29,6 +29,7 @@ METRIC = "DSA layer query-tokens/s at 128K ctx; indexer-cache HBM GB/s (% of pea
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c2_verify128k_hbm_traffic.json")
 MLA_BYTES_PER_ROW = 2048 * 656 + 64 * 576 * 2 + 64 * 512 * 2 + 2048 * 4   # 1,490,944 B
 MLA_FLOPS_PER_ROW = 2 * 64 * 2048 * (576 + 512)                            # 285,212,672
 
@@ -41,52 +42,132 @@ def indexer_bytes(ctx, rows):
     return int((132 * L + 4 * ((L + 63) // 64)).sum() + rows * (32 * 128 + 32 * 4 + 32 * 4))
 
 
-def cpu_baseline(w, n_layers):
-    """The oracle (as it stands) on one request of the workload, full layer + shared layers."""
+def source_digest(files):
+    """sha256 over the kernel sources a counter measurement was taken with."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary:
+    FETCH_SIZE x fetch_factor + WRITE_SIZE x write_factor (KiB per dispatch, factors from a
+    plain copy of known size).  None when there is no summary or the kernel's sources have
+    changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k or source_digest(k["sources"]) != k["source_sha256"]:
+        return None
+    return int(round((k["fetch_kib"] * t["fetch_factor"] + k["write_kib"] * t["write_factor"]) * 1024))
+
+
+KERNEL_SOURCES = {
+    "k_logits_decode": ["sparse_attention_store_amd/csrc/k_indexer.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
+    "k_sparse_mla": ["sparse_attention_store_amd/csrc/k_mla.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
+    "k_mla_combine": ["sparse_attention_store_amd/csrc/k_mla.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
+    "k_hist": ["sparse_attention_store_amd/csrc/k_topk.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
+    "k_select": ["sparse_attention_store_amd/csrc/k_topk.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
+    "k_final": ["sparse_attention_store_amd/csrc/k_topk.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
+}
+
+
+def write_traffic(fetch_csv, write_csv, command):
+    """Summarises two rocprofv3 --pmc runs of this benchmark with --copy-probe (FETCH_SIZE, then
+    WRITE_SIZE) into TRAFFIC_FILE: per kernel the median KiB per dispatch, and the factors that
+    make a 1 GiB device copy read and write 1 GiB."""
+    import csv
+    import statistics
+
+    def per_kernel(path):
+        vals = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+
+    def pick(vals, key):
+        hits = [v for name, vs in vals.items() if key in name for v in vs]
+        return hits
+
+    gib_kib = float(1 << 20)
+    copy_f, copy_w = max(pick(fetch, "copyBuffer")), max(pick(write, "copyBuffer"))
+    out = {"about": "HBM traffic per dispatch of the c2 verify workload (64 x 6 rows at 128K), from rocprofv3 "
+                    "--pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches); factors make a "
+                    "1 GiB device copy read and write 1 GiB",
+           "command": command, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+           "fetch_factor": gib_kib / copy_f, "write_factor": gib_kib / copy_w, "kernels": {}}
+    for k, src in KERNEL_SOURCES.items():
+        f, wv = pick(fetch, k), pick(write, k)
+        if f and wv:
+            out["kernels"][k] = {"fetch_kib": statistics.median(f), "write_kib": statistics.median(wv),
+                                 "dispatches": len(f), "sources": src, "source_sha256": source_digest(src)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
+def cpu_baseline(w, n_layers, target_s=10.0):
+    """The oracle (as it stands) on whole requests of the workload, one after another, until
+    at least target_s seconds of oracle work are timed: per request, the full layer (store of
+    the step's tokens, q quantise, logits, top-k, sparse MLA) and the shared layers' MLA.
+    Each request's index-K cache and the selected latent records are built outside the timed
+    part (they are the caches' state before the step)."""
     import numpy as np
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import dsa_inputs as gi
     import oracle as orc
 
-    b = 0
-    rows = np.where(w.row_req == b)[0]
-    L = int(w.ctx[b])
-    npg = (L + 63) // 64
-    pt = np.arange(npg, dtype=np.int32)[None, :]       # compact pool for the one request
-    req = np.zeros(len(rows), np.int32)
-    pos = w.row_pos[rows]
-    # setup (not timed): this request's index-K cache from its raw keys
-    kraw = gi.normal_bf16(w.seed, gi.T_RAW_K, int(w.token_base[b]) * 128, L * 128).reshape(L, 128)
-    icache = np.zeros((npg, 8448), np.uint8)
-    orc.index_k_store(kraw, np.zeros(L, np.int32), np.arange(L, dtype=np.int32), pt, icache)
     R = w.R
-    q = gi.normal_bf16(w.seed, gi.T_IDX_Q, int(rows[0]) * 32 * 128, len(rows) * 32 * 128)
-    wt = gi.uniform_f32(w.seed, gi.T_W, int(rows[0]) * 32, len(rows) * 32, gi.w_scale()).reshape(-1, 32)
-    qm = [gi.normal_bf16(w.seed, gi.T_MLA_Q, (l * R + int(rows[0])) * 64 * 576, len(rows) * 64 * 576)
-          for l in range(n_layers)]
-    knew = gi.normal_bf16(w.seed, gi.T_RAW_K, (int(w.token_base[b]) + int(pos[0])) * 128, len(rows) * 128)
-    t0 = time.perf_counter()
-    orc.index_k_store(knew.reshape(-1, 128), req, pos, pt, icache)
-    q8, qs = orc.quant_fp8(q.reshape(-1, 128))
-    lg = orc.indexer_logits(q8.reshape(-1, 32, 128), qs.reshape(-1, 32), wt, req, pos, pt, icache)
-    idx, _ = orc.topk(lg, pos, 2048)
-    t_idx = time.perf_counter() - t0
-    # latent records of the selected positions only (setup, not timed)
-    sel = np.unique(idx[idx >= 0])
-    t_mla = 0.0
-    for l in range(n_layers):
-        kv = gi.normal_bf16_at(w.seed, gi.T_LATENT0 + l,
-                               ((int(w.token_base[b]) + sel)[:, None] * 576 + np.arange(576)[None, :]).ravel())
-        lcache = np.zeros((npg, 64 * 656), np.uint8)
-        orc.latent_store(kv.reshape(-1, 576), np.zeros(len(sel), np.int32), sel.astype(np.int32), pt, lcache)
-        t1 = time.perf_counter()
-        orc.sparse_mla(qm[l].reshape(-1, 64, 576), req, pos, pt, lcache, idx, 1.0 / 16.0)
-        t_mla += time.perf_counter() - t1
+    t_idx = t_mla = 0.0
+    n_rows = n_req = 0
+    for b in range(w.B):
+        rows = np.where(w.row_req == b)[0]
+        L = int(w.ctx[b])
+        npg = (L + 63) // 64
+        pt = np.arange(npg, dtype=np.int32)[None, :]       # compact pool for the one request
+        req = np.zeros(len(rows), np.int32)
+        pos = w.row_pos[rows]
+        kraw = gi.normal_bf16(w.seed, gi.T_RAW_K, int(w.token_base[b]) * 128, L * 128).reshape(L, 128)
+        icache = np.zeros((npg, 8448), np.uint8)
+        orc.index_k_store(kraw, np.zeros(L, np.int32), np.arange(L, dtype=np.int32), pt, icache)
+        q = gi.normal_bf16(w.seed, gi.T_IDX_Q, int(rows[0]) * 32 * 128, len(rows) * 32 * 128)
+        wt = gi.uniform_f32(w.seed, gi.T_W, int(rows[0]) * 32, len(rows) * 32, gi.w_scale()).reshape(-1, 32)
+        qm = [gi.normal_bf16(w.seed, gi.T_MLA_Q, (l * R + int(rows[0])) * 64 * 576, len(rows) * 64 * 576)
+              for l in range(n_layers)]
+        knew = kraw[pos]
+        t0 = time.perf_counter()
+        orc.index_k_store(knew, req, pos, pt, icache)
+        q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+        lg = orc.indexer_logits(q8.reshape(-1, 32, 128), qs.reshape(-1, 32), wt, req, pos, pt, icache)
+        idx, _ = orc.topk(lg, pos, 2048)
+        t_idx += time.perf_counter() - t0
+        sel = np.unique(idx[idx >= 0]).astype(np.int64)
+        for l in range(n_layers):
+            kv = gi.normal_bf16_at(w.seed, gi.T_LATENT0 + l,
+                                   ((int(w.token_base[b]) + sel)[:, None] * 576 + np.arange(576)[None, :]).ravel())
+            lcache = np.zeros((npg, 64 * 656), np.uint8)
+            orc.latent_store(kv.reshape(-1, 576), np.zeros(len(sel), np.int32), sel.astype(np.int32), pt, lcache)
+            t1 = time.perf_counter()
+            orc.sparse_mla(qm[l].reshape(-1, 64, 576), req, pos, pt, lcache, idx, 1.0 / 16.0)
+            t_mla += time.perf_counter() - t1
+        n_rows += len(rows)
+        n_req += 1
+        if t_idx + t_mla >= target_s:
+            break
     dt = t_idx + t_mla
     cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    return {"value": len(rows) * n_layers / dt, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"1 of {w.B} requests ({len(rows)} rows at {L} ctx): store + quant + logits + top-k + "
-                      f"{n_layers} sparse-MLA layers; {dt:.2f} s (indexer part {t_idx:.2f} s)"}
+    return {"value": n_rows * n_layers / dt, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_req} of {w.B} requests ({n_rows} rows at {int(w.ctx[0])} ctx): store + quant + logits + "
+                      f"top-k + {n_layers} sparse-MLA layers each; {dt:.1f} s timed (indexer part {t_idx:.1f} s)"}
 
 
 def main():
@@ -96,7 +177,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="summarise two rocprofv3 --pmc counter files into the committed traffic summary")
     a = ap.parse_args()
+    if a.write_traffic:
+        print(json.dumps(write_traffic(*a.write_traffic), indent=1))
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
@@ -175,10 +261,12 @@ def main():
     mla_total = sum(per[f"mla{l}"] for l in D.layers)
     dominant = "logits"      # the metric's named kernel: index-K cache streaming
     roof_idx = {"kernel": "k_logits_decode (dsa_indexer_logits)", "bound": "hbm", "achieved": round(idx_gbps, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("k_logits_decode"),
                 "algorithmic_bytes_per_launch": ib, "avg_launch_us": round(per["logits"], 2)}
     roof_mla = {"kernel": "k_sparse_mla (dsa_sparse_mla_decode)", "bound": "hbm", "achieved": round(mla_gbps, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(mla_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(mla_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic("k_sparse_mla") and
+                (measured_traffic("k_sparse_mla") + (measured_traffic("k_mla_combine") or 0)),
                 "algorithmic_bytes_per_launch": mla_b, "avg_launch_us": round(per["mla0"], 2),
                 "mfma_tflops": round(mla_tflops, 1), "mfma_frac_bf16": round(mla_tflops / BF16_PEAK_TFLOPS, 4)}
     out = {

@@ -111,6 +111,9 @@ def bf16_to_f64(h):
 def assert_attention_close(g_bits, r_bits, atol=2e-2, rtol=1e-2):
     g = bf16_to_f64(g_bits)
     r = bf16_to_f64(r_bits)
+    assert g.shape == r.shape
+    if g.size == 0:                      # no row left to compare (all differed at near-ties)
+        return 0.0
     err = np.abs(g - r)
     tol = atol + rtol * np.abs(r)
     assert np.all(err <= tol), f"{(err > tol).sum()} outputs out of tolerance, max err {err.max():.3g}"
