@@ -9,7 +9,7 @@
 // Work-group = (row, split of the row's selected keys); 8 waves; keys in tiles of 32.
 //  * Record addresses of the split are resolved once into LDS (idx -> page table).
 //  * Each tile's 32 records (656 B each: fp8 latent, 4 scales, bf16 rope) are copied from
-//    HBM straight into LDS with gfx950's global_load_lds_dwordx4, three tiles ahead of the
+//    HBM straight into LDS with gfx950's global_load_lds_dwordx4, two tiles ahead of the
 //    compute (explicit vmcnt waits + raw s_barrier: a full __syncthreads() would drain the
 //    in-flight copies every tile).
 //  * Warp specialisation, one barrier per tile: waves 0-3 score tile t (S^T[32 keys x 16
@@ -33,11 +33,13 @@ constexpr int kThreads = 512;             // 4 QK waves + 4 PV waves
 constexpr int kTile = 32;                  // keys per tile
 constexpr int kChunks = kRecBytes / 16;    // 41 x 16 B per record
 constexpr int kTileChunks = kTile * kChunks;            // 1312 chunks of 16 B
-constexpr int kDmaPerWave = 3;                           // 8 waves x 3 x 64 lanes >= 1312
-constexpr int kTileBytes = 8 * kDmaPerWave * 64 * 16;    // 24 KiB (tail is padding)
+constexpr int kDmaWaves = 4;                             // the QK waves issue every copy
+constexpr int kDmaPerWave = 6;                           // 4 waves x 6 x 64 lanes >= 1312
+constexpr int kTileBytes = kDmaWaves * kDmaPerWave * 64 * 16;   // 24 KiB (tail is padding)
 constexpr int kDepth = 2;                                // tiles in flight ahead of the QK tile
 constexpr int kBufs = kDepth + 2;                        // + the QK tile + the PV tile
 constexpr int kMaxSplitKeys = 2048;
+constexpr int kPRow = kTile + 8;                          // P row pitch (bf16) in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;      // log2 units the running max may lag behind
 
@@ -68,24 +70,163 @@ __device__ inline void lds_barrier() {
 }
 
 // Issues the global->LDS copies of one tile: LDS chunk c of the tile holds 16 B of key
-// c/41, chunk c%41 of its 656-B record (records land back to back).  Every wave issues
+// c/41, chunk c%41 of its 656-B record (records land back to back).  Each QK wave issues
 // exactly kDmaPerWave copies so that per-tile vmcnt accounting is uniform; lanes past the
 // tile or of invalid keys copy from the first record of the pool into the buffer (the
-// records of invalid keys are zeroed before use).
-__device__ inline void issue_tile(const uint8_t* cache, const int* phys, int tile_base, int nkeys,
-                                  uint8_t* buf, int wave, int lane) {
+// records of invalid keys are zeroed before use).  The record lookups are read
+// before any copy is issued, so the wave waits for LDS once.
+__device__ __forceinline__ void issue_tile(const uint8_t* cache, const DSA_LDS int* phys, int tile_base,
+                                           DSA_LDS uint8_t* buf, int wave, int lane) {
+  int ph[kDmaPerWave], chunk[kDmaPerWave];
+  bool in_tile[kDmaPerWave];
 #pragma unroll
   for (int u = 0; u < kDmaPerWave; u++) {
-    const int slot = wave * kDmaPerWave + u;
-    const int c = slot * 64 + lane;
-    const uint8_t* src = cache;
-    if (c < kTileChunks) {
-      const int key = c / kChunks, ch = c - key * kChunks;
-      const int j = tile_base + key;
-      const int ph = j < nkeys ? phys[j] : -1;
-      if (ph >= 0) src = cache + (int64_t)ph * kRecBytes + 16 * ch;
+    const int c = (wave * kDmaPerWave + u) * 64 + lane;
+    in_tile[u] = c < kTileChunks;
+    const int key = min(c / kChunks, kTile - 1);
+    chunk[u] = c - key * kChunks;
+    ph[u] = phys[tile_base + key];           // tile_base + key < ntiles * kTile <= kMaxSplitKeys
+  }
+#pragma unroll
+  for (int u = 0; u < kDmaPerWave; u++) {
+    const bool ok = in_tile[u] && ph[u] >= 0;
+    const uint8_t* src = ok ? cache + (int64_t)ph[u] * kRecBytes + 16 * chunk[u] : cache;
+    __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(buf + (wave * kDmaPerWave + u) * 1024), 16,
+                                     0, 0);
+  }
+}
+
+// Zeroes the records of the invalid keys of a tile (all threads of the work-group).
+__device__ __forceinline__ void zero_bad_records(DSA_LDS uint8_t* __restrict__ T, const DSA_LDS int* phys, int tile_base,
+                                                 int tid) {
+  for (int i = tid; i < kTile * kChunks; i += kThreads) {
+    const int key = i / kChunks;
+    if (phys[tile_base + key] < 0) *reinterpret_cast<DSA_LDS i32x4*>(T + 16 * i) = i32x4{0, 0, 0, 0};
+  }
+}
+
+// max over the four 16-lane rows (lanes l, l^16, l^32, l^48) with lane swaps, no LDS
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// q of one QK wave (heads 16qw..16qw+15) as MFMA B operands
+struct QkOps {
+  i32x8 qhi[4], qlo[4];
+  int sbhi[4], sblo[4];
+  bf16x8 qr[2];
+};
+
+// One pipeline step of a QK wave.  The tile pointers are restrict-qualified: the copy
+// destination (tile it + kDepth) and the tile read here (tile it) are different buffers,
+// which lets the compiler keep the copies in flight across the LDS reads; the arrival of
+// tile `it` itself is ordered by the caller's vmcnt wait and barrier.
+__device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int* __restrict__ phys, int it, int ntiles,
+                                        bool bad,
+                                        DSA_LDS uint8_t* __restrict__ dst, DSA_LDS uint8_t* __restrict__ T,
+                                        DSA_LDS uint16_t* __restrict__ plp, DSA_LDS float* __restrict__ alpha_p,
+                                        const QkOps& Q, float sm_log2, float& m_run, float& l_part, int qw, int wave,
+                                        int lane, int tid) {
+  const int g = lane >> 4, c16 = lane & 15;
+  if (it + kDepth < ntiles) issue_tile(cache, phys, (it + kDepth) * kTile, dst, wave, lane);
+  if (bad) {
+    zero_bad_records(T, phys, it * kTile, tid);
+    lds_barrier();
+  }
+  // S^T (32 keys x 16 heads): lane holds keys 4g+i (+16 mt), head c16.  All operands of
+  // the tile are read first; the two 16-key accumulator chains are interleaved.
+  i32x8 a[2][4];
+  bf16x8 ar[2][2];
+  int sa[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+    const DSA_LDS uint8_t* rec = T + (16 * mt + c16) * kRecBytes;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const i32x4 lo4 = *reinterpret_cast<const DSA_LDS i32x4*>(rec + 128 * b + 16 * g);
+      const i32x4 hi4 = *reinterpret_cast<const DSA_LDS i32x4*>(rec + 128 * b + 64 + 16 * g);
+      a[mt][b] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     }
-    __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(buf + slot * 1024), 16, 0, 0);
+    const i32x4 ksc = *reinterpret_cast<const DSA_LDS i32x4*>(rec + kRecScaleOff);
+#pragma unroll
+    for (int b = 0; b < 4; b++) sa[mt][b] = (ksc[b] >> 23) & 0xFF;   // E8M0 = the fp32 exponent of 2^e
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+      ar[mt][ks] = *reinterpret_cast<const DSA_LDS bf16x8*>(rec + kRecRopeOff + 2 * (32 * ks + 8 * g));
+  }
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int b = 0; b < 4; b++) {
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+      acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mt][b], Q.qhi[b], acc[mt], 0, 0, 0, sa[mt][b], 0,
+                                                                 Q.sbhi[b]);
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+      acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mt][b], Q.qlo[b], acc[mt], 0, 0, 0, sa[mt][b], 0,
+                                                                 Q.sblo[b]);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) acc[mt] = mfma_bf16(ar[mt][ks], Q.qr[ks], acc[mt]);
+
+  // validity of the lane's 8 keys (two runs of four consecutive entries of phys)
+  const i32x4 vk[2] = {*reinterpret_cast<const DSA_LDS i32x4*>(phys + it * kTile + 4 * g),
+                       *reinterpret_cast<const DSA_LDS i32x4*>(phys + it * kTile + 16 + 4 * g)};
+  float sv[2][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      sv[mt][i] = vk[mt][i] >= 0 ? acc[mt][i] * sm_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sv[mt][i]);
+    }
+  tmax = rows_max(tmax);
+  // lazy rescaling: the reference max only moves when the new max exceeds it by more
+  // than kRescaleSlack (exp2 of the lag stays below 2^8, harmless in fp32 / bf16)
+  float alpha = 1.f;
+  if (tmax > m_run + kRescaleSlack) {
+    alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - tmax);
+    m_run = tmax;
+  }
+  const bool live = m_run != -INFINITY;
+  float psum = 0.f;
+  float p[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      p[mt][i] = live ? __builtin_amdgcn_exp2f(sv[mt][i] - m_run) : 0.f;
+      psum += p[mt][i];
+    }
+  l_part = l_part * alpha + psum;
+  const int hh = 16 * qw + c16;
+  if (g == 0) alpha_p[hh] = alpha;
+  // P scaled by the value-block scale of each key, bf16, for the four value blocks
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+    f32x4 kb[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      kb[i] = *reinterpret_cast<const DSA_LDS f32x4*>(T + (16 * mt + 4 * g + i) * kRecBytes + kRecScaleOff);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      i32x2 packed;
+      packed[0] = (int)((uint32_t)f32_to_bf16_bits(p[mt][0] * kb[0][b]) | ((uint32_t)f32_to_bf16_bits(p[mt][1] * kb[1][b]) << 16));
+      packed[1] = (int)((uint32_t)f32_to_bf16_bits(p[mt][2] * kb[2][b]) | ((uint32_t)f32_to_bf16_bits(p[mt][3] * kb[3][b]) << 16));
+      *reinterpret_cast<DSA_LDS i32x2*>(plp + (b * kHeads + hh) * kPRow + 16 * mt + 4 * g) = packed;
+    }
   }
 }
 
@@ -101,10 +242,10 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
              int keys_per_split, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
              float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[kBufs][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t pl[2][4][kHeads][kTile + 8];   // P per value block
-  __shared__ float alpha_s[2][kHeads];
+  __shared__ __attribute__((aligned(16))) uint16_t pl[2][4 * kHeads * kPRow];   // P per value block
+  __shared__ __attribute__((aligned(16))) float alpha_s[2][kHeads];
   __shared__ float m_s[kHeads], l_s[kHeads];
-  __shared__ int phys[kMaxSplitKeys];
+  __shared__ __attribute__((aligned(16))) int phys[kMaxSplitKeys];
   __shared__ int tile_bad[kMaxSplitKeys / kTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -117,6 +258,23 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
   const int ntiles = (nkeys + kTile - 1) / kTile;
   const int p = pos[r];
   const int rq = req[r];
+  DSA_LDS uint8_t* tl = (DSA_LDS uint8_t*)&tiles[0][0];
+  const DSA_LDS int* phl = (const DSA_LDS int*)phys;
+
+  // QK waves fetch their q rows first: the loads then precede every tile copy, so the
+  // per-tile vmcnt waits cover them and nothing in the loop waits for all copies
+  i32x4 qraw[4][4];
+  bf16x8 qr_raw[2];
+  if (is_qk) {
+    const uint16_t* qh = q + ((int64_t)r * kHeads + 16 * qw + c16) * kLat;
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        qraw[b][u] = *reinterpret_cast<const i32x4*>(qh + 128 * b + 64 * (u >> 1) + 16 * g + 8 * (u & 1));
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) qr_raw[ks] = *reinterpret_cast<const bf16x8*>(qh + kVal + 32 * ks + 8 * g);
+  }
 
   // resolve record addresses (physical token index) of this split's keys
   for (int t = tid; t < ntiles; t += kThreads) tile_bad[t] = 0;
@@ -135,27 +293,18 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
   }
 
   __syncthreads();                              // phys ready
-  for (int t = 0; t < kDepth && t < ntiles; t++) issue_tile(cache, phys, t * kTile, nkeys, tiles[t], wave, lane);
+  if (is_qk)
+    for (int t = 0; t < kDepth && t < ntiles; t++) issue_tile(cache, phl, t * kTile, tl + t * kTileBytes, wave, lane);
 
-  // Per-iteration prologue shared by both roles (same barriers in the same order):
-  // wait for tile `it`, barrier, issue tile it+kDepth into the buffer of tile it-2, zero the
-  // records of invalid keys of tile `it`.
-  auto prologue = [&](int it) {
-    if (it < ntiles) {
+  // Start of every iteration (both roles, same barriers in the same order): wait for this
+  // wave's copies of tile `it`, then a barrier so that all of tile `it` is in LDS and every
+  // wave is done with QK(it-1) and PV(it-2) (whose buffers are refilled next).
+  auto wait_tile = [&](int it) {
+    if (is_qk && it < ntiles) {
       if (min(kDepth - 1, ntiles - 1 - it) >= 1) wait_vmcnt<kDmaPerWave>();
       else wait_vmcnt<0>();
     }
-    lds_barrier();             // tile `it` in LDS; QK(it-1) and PV(it-2) of every wave done
-    if (it + kDepth < ntiles)
-      issue_tile(cache, phys, (it + kDepth) * kTile, nkeys, tiles[(it + kDepth) % kBufs], wave, lane);
-    if (it < ntiles && tile_bad[it]) {
-      uint8_t* T = tiles[it % kBufs];
-      for (int i = tid; i < kTile * kChunks; i += kThreads) {
-        const int key = i / kChunks;
-        if (phys[it * kTile + key] < 0) *reinterpret_cast<uint4*>(T + 16 * i) = make_uint4(0, 0, 0, 0);
-      }
-      lds_barrier();
-    }
+    lds_barrier();
   };
 
   if (is_qk) {
@@ -164,34 +313,24 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
     // FP8 terms per 128-dim block, q = hi * 2^e_hi + lo * 2^e_lo (lo quantises the residual
     // of hi), which carries bf16's 8 significant bits; the 64 rope dims stay bf16.  Lane
     // holds head 16qw + c16, dims 128b + [16g, 16g+16) and 128b + 64 + [16g, 16g+16).
-    i32x8 qhi[4], qlo[4];
-    int sbhi[4], sblo[4];
-    bf16x8 qr[2];
+    QkOps Q;
     {
-      const uint16_t* qh = q + ((int64_t)r * kHeads + 16 * qw + c16) * kLat;
 #pragma unroll
       for (int b = 0; b < 4; b++) {
         float x[32];
 #pragma unroll
-        for (int half = 0; half < 2; half++) {
-          const uint16_t* src = qh + 128 * b + 64 * half + 16 * g;
+        for (int u = 0; u < 4; u++)          // u = 2 * half + c: dims 64 * half + 16g + 8c + [0, 8)
 #pragma unroll
-          for (int c = 0; c < 2; c++) {
-            const uint4 u = *reinterpret_cast<const uint4*>(src + 8 * c);
-            const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              x[16 * half + 8 * c + 2 * i] = __uint_as_float(wds[i] << 16);
-              x[16 * half + 8 * c + 2 * i + 1] = __uint_as_float(wds[i] & 0xFFFF0000u);
-            }
+          for (int i = 0; i < 4; i++) {
+            const uint32_t wd = (uint32_t)qraw[b][u][i];
+            x[8 * u + 2 * i] = __uint_as_float(wd << 16);
+            x[8 * u + 2 * i + 1] = __uint_as_float(wd & 0xFFFF0000u);
           }
-        }
         // block amax over the 4 lanes holding this head's 128 dims (lanes c16, c16^16, ^32, ^48)
         float am = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; i++) am = fmaxf(am, fabsf(x[i]));
-        am = fmaxf(am, __shfl_xor(am, 16, 64));
-        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        am = rows_max(am);
         const int eh = ue8m0_exponent(am);
         const float ih = __builtin_ldexpf(1.0f, -eh), sh = __builtin_ldexpf(1.0f, eh);
         uint32_t hw[8];
@@ -207,107 +346,30 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
 #pragma unroll
           for (int j = 0; j < 4; j++) am2 = fmaxf(am2, fabsf(x[4 * i + j]));
         }
-        am2 = fmaxf(am2, __shfl_xor(am2, 16, 64));
-        am2 = fmaxf(am2, __shfl_xor(am2, 32, 64));
+        am2 = rows_max(am2);
         const int el = ue8m0_exponent(am2);
         const float il = __builtin_ldexpf(1.0f, -el);
         uint32_t lw[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) lw[i] = pack4_fp8(x[4 * i] * il, x[4 * i + 1] * il, x[4 * i + 2] * il, x[4 * i + 3] * il);
-        qhi[b] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
-        qlo[b] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
-        sbhi[b] = eh + 127;      // E8M0 scale operands
-        sblo[b] = el + 127;
+        Q.qhi[b] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
+        Q.qlo[b] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
+        Q.sbhi[b] = eh + 127;      // E8M0 scale operands
+        Q.sblo[b] = el + 127;
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ks++) qr[ks] = *reinterpret_cast<const bf16x8*>(qh + kVal + 32 * ks + 8 * g);
+      for (int ks = 0; ks < 2; ks++) Q.qr[ks] = qr_raw[ks];
     }
     float m_run = -INFINITY, l_part = 0.f;      // for head 16qw + c16
-    for (int it = 0; it <= ntiles; it++) {
-      prologue(it);
-      if (it == ntiles) break;
-      const uint8_t* T = tiles[it % kBufs];
+    for (int it = 0; it < ntiles; it++) {
+      wait_tile(it);
       const int par = it & 1;
-      // S^T (32 keys x 16 heads): lane holds keys 4g+i (+16 mt), head c16.  Latent part on the
-      // block-scaled FP8 MFMA straight from the cached codes (E8M0 scales = the records' ue8m0
-      // block scales), rope part on the bf16 MFMA.
-      f32x4 s_acc[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++) {
-        const uint8_t* rec = T + (16 * mt + c16) * kRecBytes;
-        const uint4 ksc = *reinterpret_cast<const uint4*>(rec + kRecScaleOff);
-        const uint32_t kbits[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-          const i32x4 lo4 = *reinterpret_cast<const i32x4*>(rec + 128 * b + 16 * g);
-          const i32x4 hi4 = *reinterpret_cast<const i32x4*>(rec + 128 * b + 64 + 16 * g);
-          const i32x8 a8 = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          const int sa = (int)((kbits[b] >> 23) & 0xFFu);
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, qhi[b], acc, 0, 0, 0, sa, 0, sbhi[b]);
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, qlo[b], acc, 0, 0, 0, sa, 0, sblo[b]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(rec + kRecRopeOff + 2 * (32 * ks + 8 * g));
-          acc = mfma_bf16(a, qr[ks], acc);
-        }
-        s_acc[mt] = acc;
-      }
-      float sv[2][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int j = it * kTile + 16 * mt + 4 * g + i;
-          sv[mt][i] = phys[j] >= 0 ? s_acc[mt][i] * sm_log2 : -INFINITY;
-          tmax = fmaxf(tmax, sv[mt][i]);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      // lazy rescaling: the reference max only moves when the new max exceeds it by more
-      // than kRescaleSlack (exp2 of the lag stays below 2^8, harmless in fp32 / bf16)
-      float alpha = 1.f;
-      if (tmax > m_run + kRescaleSlack) {
-        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - tmax);
-        m_run = tmax;
-      }
-      const bool live = m_run != -INFINITY;
-      float psum = 0.f;
-      float pv[2][4];
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          pv[mt][i] = live ? __builtin_amdgcn_exp2f(sv[mt][i] - m_run) : 0.f;
-          psum += pv[mt][i];
-        }
-      l_part = l_part * alpha + psum;
-      const int hh = 16 * qw + c16;
-      if (g == 0) alpha_s[par][hh] = alpha;
-      // P scaled by the value block scale of each key, bf16, for the four value blocks
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++) {
-        float4 kb[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          kb[i] = *reinterpret_cast<const float4*>(T + (16 * mt + 4 * g + i) * kRecBytes + kRecScaleOff);
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-          const float s0 = b == 0 ? kb[0].x : b == 1 ? kb[0].y : b == 2 ? kb[0].z : kb[0].w;
-          const float s1 = b == 0 ? kb[1].x : b == 1 ? kb[1].y : b == 2 ? kb[1].z : kb[1].w;
-          const float s2 = b == 0 ? kb[2].x : b == 1 ? kb[2].y : b == 2 ? kb[2].z : kb[2].w;
-          const float s3 = b == 0 ? kb[3].x : b == 1 ? kb[3].y : b == 2 ? kb[3].z : kb[3].w;
-          uint2 packed;
-          packed.x = (uint32_t)f32_to_bf16_bits(pv[mt][0] * s0) | ((uint32_t)f32_to_bf16_bits(pv[mt][1] * s1) << 16);
-          packed.y = (uint32_t)f32_to_bf16_bits(pv[mt][2] * s2) | ((uint32_t)f32_to_bf16_bits(pv[mt][3] * s3) << 16);
-          *reinterpret_cast<uint2*>(&pl[par][b][hh][16 * mt + 4 * g]) = packed;
-        }
-      }
+      qk_step(cache, phl, it, ntiles, tile_bad[it] != 0, tl + ((it + kDepth) % kBufs) * kTileBytes,
+              tl + (it % kBufs) * kTileBytes, (DSA_LDS uint16_t*)pl[par], (DSA_LDS float*)alpha_s[par], Q, sm_log2,
+              m_run, l_part, qw, wave, lane, tid);
     }
-    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    wait_tile(ntiles);                          // the PV waves' last step
+    const float l_tot = rows_sum(l_part);
     if (g == 0) { m_s[16 * qw + c16] = m_run; l_s[16 * qw + c16] = l_tot; }
     __syncthreads();
     if (tid < kHeads) {
@@ -331,10 +393,16 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
 #pragma unroll
       for (int b = 0; b < 8; b++) O[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it <= ntiles; it++) {
-      prologue(it);
+      wait_tile(it);
+      if (it < ntiles && tile_bad[it]) {
+        zero_bad_records(tl + (it % kBufs) * kTileBytes, phl, it * kTile, tid);
+        lds_barrier();
+      }
       if (it == 0) continue;
+      // O += P V for tile it - 1.  PV waves issue no copies (the QK waves wait for them
+      // before the barrier that starts the iteration), so these LDS reads need no vmcnt wait.
       const int par = (it - 1) & 1;
-      const uint8_t* T = tiles[(it - 1) % kBufs];
+      DSA_LDS uint8_t* T = tl + ((it - 1) % kBufs) * kTileBytes;
       float al[4][4];
       bool resc = false;
 #pragma unroll
@@ -354,13 +422,13 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
       }
       bf16x8 pa[4];
 #pragma unroll
-      for (int ht = 0; ht < 4; ht++) pa[ht] = *reinterpret_cast<const bf16x8*>(&pl[par][qw][16 * ht + c16][8 * g]);
+      for (int ht = 0; ht < 4; ht++)
+        pa[ht] = *reinterpret_cast<const bf16x8*>(&pl[par][(qw * kHeads + 16 * ht + c16) * kPRow + 8 * g]);
       // tr8: lane i of a 16-lane group points at key 8g + i/2, dims +8*(i%2); gets 8 keys of dim c16
-      DSA_LDS uint8_t* lat_lds = (DSA_LDS uint8_t*)T;
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
         const int dim0 = 128 * qw + 16 * dt;
-        DSA_LDS i32x2* src = (DSA_LDS i32x2*)(lat_lds + (8 * g + (c16 >> 1)) * kRecBytes + dim0 + 8 * (c16 & 1));
+        DSA_LDS i32x2* src = (DSA_LDS i32x2*)(T + (8 * g + (c16 >> 1)) * kRecBytes + dim0 + 8 * (c16 & 1));
         const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(src);
         const bf16x8 vv = fp8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1], 1.0f);
 #pragma unroll
