@@ -35,9 +35,15 @@ constexpr int kChunks = kRecBytes / 16;    // 41 x 16 B per record
 constexpr int kTileChunks = kTile * kChunks;            // 1312 chunks of 16 B
 constexpr int kDmaWaves = 4;                             // the QK waves issue every copy
 constexpr int kDmaPerWave = 6;                           // 4 waves x 6 x 64 lanes >= 1312
-constexpr int kTileBytes = kDmaWaves * kDmaPerWave * 64 * 16;   // 24 KiB (tail is padding)
-constexpr int kDepth = 2;                                // tiles in flight ahead of the QK tile
+constexpr int kTileSlots = (kTileChunks + 63) / 64;     // 21 wave-wide 1-KiB copies hold a tile
+constexpr int kTileBytes = (kTileSlots + 1) * 1024;      // + one sink for the surplus copies
+#ifndef DSA_MLA_DEPTH
+#define DSA_MLA_DEPTH 2
+#endif
+constexpr int kDepth = DSA_MLA_DEPTH;                     // tiles in flight ahead of the QK tile
 constexpr int kBufs = kDepth + 2;                        // + the QK tile + the PV tile
+static_assert(kDepth >= 1 && kDepth <= 3, "the tile wait handles up to two tiles ahead");
+static_assert(kDmaWaves * kDmaPerWave >= kTileSlots, "copy slots must cover a tile");
 constexpr int kMaxSplitKeys = 2048;
 constexpr int kPRow = kTile + 8;                          // P row pitch (bf16) in LDS
 constexpr float kLog2e = 1.4426950408889634f;
@@ -91,8 +97,8 @@ __device__ __forceinline__ void issue_tile(const uint8_t* cache, const DSA_LDS i
   for (int u = 0; u < kDmaPerWave; u++) {
     const bool ok = in_tile[u] && ph[u] >= 0;
     const uint8_t* src = ok ? cache + (int64_t)ph[u] * kRecBytes + 16 * chunk[u] : cache;
-    __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(buf + (wave * kDmaPerWave + u) * 1024), 16,
-                                     0, 0);
+    const int slot = min(wave * kDmaPerWave + u, kTileSlots);   // surplus copies share the sink
+    __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(buf + slot * 1024), 16, 0, 0);
   }
 }
 
@@ -103,6 +109,11 @@ __device__ __forceinline__ void zero_bad_records(DSA_LDS uint8_t* __restrict__ T
     const int key = i / kChunks;
     if (phys[tile_base + key] < 0) *reinterpret_cast<DSA_LDS i32x4*>(T + 16 * i) = i32x4{0, 0, 0, 0};
   }
+}
+
+// two fp32 -> packed bf16 pair (low = a), round to nearest even, one v_cvt_pk_bf16_f32
+__device__ __forceinline__ int pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(int, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // max over the four 16-lane rows (lanes l, l^16, l^32, l^48) with lane swaps, no LDS
@@ -134,7 +145,7 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
                                         bool bad,
                                         DSA_LDS uint8_t* __restrict__ dst, DSA_LDS uint8_t* __restrict__ T,
                                         DSA_LDS uint16_t* __restrict__ plp, DSA_LDS float* __restrict__ alpha_p,
-                                        const QkOps& Q, float sm_log2, float& m_run, float& l_part, int qw, int wave,
+                                        DSA_LDS int* __restrict__ resc_p, const QkOps& Q, float sm_log2, float& m_run, float& l_part, int qw, int wave,
                                         int lane, int tid) {
   const int g = lane >> 4, c16 = lane & 15;
   if (it + kDepth < ntiles) issue_tile(cache, phys, (it + kDepth) * kTile, dst, wave, lane);
@@ -180,18 +191,24 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) acc[mt] = mfma_bf16(ar[mt][ks], Q.qr[ks], acc[mt]);
 
-  // validity of the lane's 8 keys (two runs of four consecutive entries of phys)
-  const i32x4 vk[2] = {*reinterpret_cast<const DSA_LDS i32x4*>(phys + it * kTile + 4 * g),
-                       *reinterpret_cast<const DSA_LDS i32x4*>(phys + it * kTile + 16 + 4 * g)};
   float sv[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) sv[mt][i] = acc[mt][i] * sm_log2;
+  if (bad) {     // invalid keys of the tile (two runs of four consecutive entries of phys) score -inf
+    const i32x4 vk[2] = {*reinterpret_cast<const DSA_LDS i32x4*>(phys + it * kTile + 4 * g),
+                         *reinterpret_cast<const DSA_LDS i32x4*>(phys + it * kTile + 16 + 4 * g)};
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) sv[mt][i] = vk[mt][i] >= 0 ? sv[mt][i] : -INFINITY;
+  }
   float tmax = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      sv[mt][i] = vk[mt][i] >= 0 ? acc[mt][i] * sm_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[mt][i]);
-    }
+    for (int i = 0; i < 4; i++) tmax = fmaxf(tmax, sv[mt][i]);
   tmax = rows_max(tmax);
   // lazy rescaling: the reference max only moves when the new max exceeds it by more
   // than kRescaleSlack (exp2 of the lag stays below 2^8, harmless in fp32 / bf16)
@@ -213,6 +230,8 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
   l_part = l_part * alpha + psum;
   const int hh = 16 * qw + c16;
   if (g == 0) alpha_p[hh] = alpha;
+  const bool any_resc = __any(alpha != 1.f);     // wave-uniform: tells the PV waves to rescale
+  if (lane == 0) resc_p[qw] = any_resc;
   // P scaled by the value-block scale of each key, bf16, for the four value blocks
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
@@ -222,9 +241,8 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
       kb[i] = *reinterpret_cast<const DSA_LDS f32x4*>(T + (16 * mt + 4 * g + i) * kRecBytes + kRecScaleOff);
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-      i32x2 packed;
-      packed[0] = (int)((uint32_t)f32_to_bf16_bits(p[mt][0] * kb[0][b]) | ((uint32_t)f32_to_bf16_bits(p[mt][1] * kb[1][b]) << 16));
-      packed[1] = (int)((uint32_t)f32_to_bf16_bits(p[mt][2] * kb[2][b]) | ((uint32_t)f32_to_bf16_bits(p[mt][3] * kb[3][b]) << 16));
+      const i32x2 packed = {pack2_bf16(p[mt][0] * kb[0][b], p[mt][1] * kb[1][b]),
+                            pack2_bf16(p[mt][2] * kb[2][b], p[mt][3] * kb[3][b])};
       *reinterpret_cast<DSA_LDS i32x2*>(plp + (b * kHeads + hh) * kPRow + 16 * mt + 4 * g) = packed;
     }
   }
@@ -244,6 +262,7 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[kBufs][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint16_t pl[2][4 * kHeads * kPRow];   // P per value block
   __shared__ __attribute__((aligned(16))) float alpha_s[2][kHeads];
+  __shared__ __attribute__((aligned(16))) int resc_s[2][4];     // per QK wave: some alpha != 1
   __shared__ float m_s[kHeads], l_s[kHeads];
   __shared__ __attribute__((aligned(16))) int phys[kMaxSplitKeys];
   __shared__ int tile_bad[kMaxSplitKeys / kTile];
@@ -301,7 +320,10 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
   // wave is done with QK(it-1) and PV(it-2) (whose buffers are refilled next).
   auto wait_tile = [&](int it) {
     if (is_qk && it < ntiles) {
-      if (min(kDepth - 1, ntiles - 1 - it) >= 1) wait_vmcnt<kDmaPerWave>();
+      // tiles it+1 .. it+kDepth-1 (those that exist) may stay in flight
+      const int ahead = min(kDepth - 1, ntiles - 1 - it);
+      if (ahead >= 2) wait_vmcnt<2 * kDmaPerWave>();
+      else if (ahead == 1) wait_vmcnt<kDmaPerWave>();
       else wait_vmcnt<0>();
     }
     lds_barrier();
@@ -365,7 +387,8 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
       wait_tile(it);
       const int par = it & 1;
       qk_step(cache, phl, it, ntiles, tile_bad[it] != 0, tl + ((it + kDepth) % kBufs) * kTileBytes,
-              tl + (it % kBufs) * kTileBytes, (DSA_LDS uint16_t*)pl[par], (DSA_LDS float*)alpha_s[par], Q, sm_log2,
+              tl + (it % kBufs) * kTileBytes, (DSA_LDS uint16_t*)pl[par], (DSA_LDS float*)alpha_s[par],
+              (DSA_LDS int*)resc_s[par], Q, sm_log2,
               m_run, l_part, qw, wave, lane, tid);
     }
     wait_tile(ntiles);                          // the PV waves' last step
@@ -403,16 +426,13 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
       // before the barrier that starts the iteration), so these LDS reads need no vmcnt wait.
       const int par = (it - 1) & 1;
       DSA_LDS uint8_t* T = tl + ((it - 1) % kBufs) * kTileBytes;
-      float al[4][4];
-      bool resc = false;
+      const i32x4 rf = *reinterpret_cast<const i32x4*>(resc_s[par]);
+      if (rf[0] | rf[1] | rf[2] | rf[3]) {      // rare after the first tile (lazy rescaling)
+        float al[4][4];
 #pragma unroll
-      for (int ht = 0; ht < 4; ht++)
+        for (int ht = 0; ht < 4; ht++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          al[ht][i] = alpha_s[par][16 * ht + 4 * g + i];
-          resc |= al[ht][i] != 1.f;
-        }
-      if (__any(resc)) {
+          for (int i = 0; i < 4; i++) al[ht][i] = alpha_s[par][16 * ht + 4 * g + i];
 #pragma unroll
         for (int ht = 0; ht < 4; ht++)
 #pragma unroll
