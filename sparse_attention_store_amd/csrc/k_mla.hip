@@ -45,7 +45,7 @@ constexpr int kBufs = kDepth + 2;                        // + the QK tile + the 
 static_assert(kDepth >= 1 && kDepth <= 3, "the tile wait handles up to two tiles ahead");
 static_assert(kDmaWaves * kDmaPerWave >= kTileSlots, "copy slots must cover a tile");
 constexpr int kMaxSplitKeys = 2048;
-constexpr int kPRow = kTile + 8;                          // P row pitch (bf16) in LDS
+constexpr int kPRow = kTile + 4;                          // P row pitch (fp32) in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;      // log2 units the running max may lag behind
 
@@ -144,7 +144,7 @@ struct QkOps {
 __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int* __restrict__ phys, int it, int ntiles,
                                         bool bad,
                                         DSA_LDS uint8_t* __restrict__ dst, DSA_LDS uint8_t* __restrict__ T,
-                                        DSA_LDS uint16_t* __restrict__ plp, DSA_LDS float* __restrict__ alpha_p,
+                                        DSA_LDS float* __restrict__ plp, DSA_LDS float* __restrict__ alpha_p,
                                         DSA_LDS int* __restrict__ resc_p, const QkOps& Q, float sm_log2, float& m_run, float& l_part, int qw, int wave,
                                         int lane, int tid) {
   const int g = lane >> 4, c16 = lane & 15;
@@ -232,20 +232,11 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
   if (g == 0) alpha_p[hh] = alpha;
   const bool any_resc = __any(alpha != 1.f);     // wave-uniform: tells the PV waves to rescale
   if (lane == 0) resc_p[qw] = any_resc;
-  // P scaled by the value-block scale of each key, bf16, for the four value blocks
+  // P (fp32, unscaled): the PV waves apply each key's value-block scale
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++) {
-    f32x4 kb[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-      kb[i] = *reinterpret_cast<const DSA_LDS f32x4*>(T + (16 * mt + 4 * g + i) * kRecBytes + kRecScaleOff);
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const i32x2 packed = {pack2_bf16(p[mt][0] * kb[0][b], p[mt][1] * kb[1][b]),
-                            pack2_bf16(p[mt][2] * kb[2][b], p[mt][3] * kb[3][b])};
-      *reinterpret_cast<DSA_LDS i32x2*>(plp + (b * kHeads + hh) * kPRow + 16 * mt + 4 * g) = packed;
-    }
-  }
+  for (int mt = 0; mt < 2; mt++)
+    *reinterpret_cast<DSA_LDS f32x4*>(plp + hh * kPRow + 16 * mt + 4 * g) =
+        f32x4{p[mt][0], p[mt][1], p[mt][2], p[mt][3]};
 }
 
 // Warp-specialised pipeline: in iteration `it`, waves 0-3 (QK) score tile `it`, run the
@@ -260,7 +251,7 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
              int keys_per_split, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
              float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[kBufs][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t pl[2][4 * kHeads * kPRow];   // P per value block
+  __shared__ __attribute__((aligned(16))) float pl[2][kHeads * kPRow];          // P of a tile, fp32
   __shared__ __attribute__((aligned(16))) float alpha_s[2][kHeads];
   __shared__ __attribute__((aligned(16))) int resc_s[2][4];     // per QK wave: some alpha != 1
   __shared__ float m_s[kHeads], l_s[kHeads];
@@ -387,7 +378,7 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
       wait_tile(it);
       const int par = it & 1;
       qk_step(cache, phl, it, ntiles, tile_bad[it] != 0, tl + ((it + kDepth) % kBufs) * kTileBytes,
-              tl + (it % kBufs) * kTileBytes, (DSA_LDS uint16_t*)pl[par], (DSA_LDS float*)alpha_s[par],
+              tl + (it % kBufs) * kTileBytes, (DSA_LDS float*)pl[par], (DSA_LDS float*)alpha_s[par],
               (DSA_LDS int*)resc_s[par], Q, sm_log2,
               m_run, l_part, qw, wave, lane, tid);
     }
@@ -440,10 +431,24 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
 #pragma unroll
             for (int i = 0; i < 4; i++) O[ht][dt][i] *= al[ht][i];
       }
+      // A operands: P of heads 16ht + c16 for keys 8g..8g+7, times those keys' scale of
+      // value block qw (a power of two: exact), rounded to bf16
+      f32x4 ks[2];
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) ks[h][i] = *reinterpret_cast<const DSA_LDS float*>(T + (8 * g + 4 * h + i) * kRecBytes +
+                                                                                kRecScaleOff + 4 * qw);
       bf16x8 pa[4];
 #pragma unroll
-      for (int ht = 0; ht < 4; ht++)
-        pa[ht] = *reinterpret_cast<const bf16x8*>(&pl[par][(qw * kHeads + 16 * ht + c16) * kPRow + 8 * g]);
+      for (int ht = 0; ht < 4; ht++) {
+        const float* prow = &pl[par][(16 * ht + c16) * kPRow + 8 * g];
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
+        const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
+        const int w0 = pack2_bf16(p0[0] * ks[0][0], p0[1] * ks[0][1]), w1 = pack2_bf16(p0[2] * ks[0][2], p0[3] * ks[0][3]);
+        const int w2 = pack2_bf16(p1[0] * ks[1][0], p1[1] * ks[1][1]), w3 = pack2_bf16(p1[2] * ks[1][2], p1[3] * ks[1][3]);
+        pa[ht] = __builtin_bit_cast(bf16x8, i32x4{w0, w1, w2, w3});
+      }
       // tr8: lane i of a 16-lane group points at key 8g + i/2, dims +8*(i%2); gets 8 keys of dim c16
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
