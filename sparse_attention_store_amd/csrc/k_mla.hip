@@ -30,6 +30,7 @@ namespace dsa {
 namespace {
 
 constexpr int kThreads = 512;             // 4 QK waves + 4 PV waves
+static_assert(kThreads == kVal, "the two-part merge maps one thread to each value dim");
 constexpr int kTile = 32;                  // keys per tile
 constexpr int kChunks = kRecBytes / 16;    // 41 x 16 B per record
 constexpr int kTileChunks = kTile * kChunks;            // 1312 chunks of 16 B
@@ -239,17 +240,31 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
         f32x4{p[mt][0], p[mt][1], p[mt][2], p[mt][3]};
 }
 
-// Warp-specialised pipeline: in iteration `it`, waves 0-3 (QK) score tile `it`, run the
-// online softmax and write P (scaled per value block) for it; waves 4-7 (PV) accumulate
-// tile it-1 with the P written one iteration earlier.  One barrier per iteration.
+// Partial results cross work-groups (and XCDs, each with its own L2): they are written and
+// read as relaxed agent-scope atomics, which the hardware keeps coherent across the L2s
+// without a device-wide cache write-back.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Attention of query row r over keys [j0, j0 + nkeys) of its selection (one segment), as a
+// warp-specialised pipeline: in iteration `it`, waves 0-3 (QK) score tile `it`, run the
+// online softmax and write P for it; waves 4-7 (PV) accumulate tile it-1 with the P written
+// one iteration earlier.  One barrier per iteration.
 //  * QK wave q owns heads 16q..16q+15 over the full 576 contraction dims (q in registers).
 //  * PV wave v owns value dims 128v..128v+127 (value block v) for all 64 heads.
-template <bool kSplit>
-__global__ void __launch_bounds__(kThreads)
-k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, const int32_t* __restrict__ pos,
-             DevPages pg, const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx, int32_t k,
-             int keys_per_split, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-             float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+// The result goes to the bf16 output (and lse) when part_o is null; otherwise it is written
+// as a partial: un-normalised O [64][512], and per head the running max m (log2 units) and
+// the sum l, to part_o / part_ml.  All threads of the work-group call it together.
+__device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q, const int32_t* __restrict__ req,
+                                            const int32_t* __restrict__ pos, const DevPages& pg,
+                                            const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx,
+                                            int32_t k, float sm_log2, int r, int j0, int nkeys,
+                                            uint16_t* __restrict__ out, float* __restrict__ lse,
+                                            float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[kBufs][kTileBytes];
   __shared__ __attribute__((aligned(16))) float pl[2][kHeads * kPRow];          // P of a tile, fp32
   __shared__ __attribute__((aligned(16))) float alpha_s[2][kHeads];
@@ -262,9 +277,6 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
   const int g = lane >> 4, c16 = lane & 15;
   const bool is_qk = wave < 4;
   const int qw = wave & 3;                       // QK: head group; PV: value block
-  const int r = blockIdx.y, split = blockIdx.x;
-  const int j0 = split * keys_per_split;
-  const int nkeys = max(0, min(keys_per_split, k - j0));
   const int ntiles = (nkeys + kTile - 1) / kTile;
   const int p = pos[r];
   const int rq = req[r];
@@ -387,16 +399,14 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
     if (g == 0) { m_s[16 * qw + c16] = m_run; l_s[16 * qw + c16] = l_tot; }
     __syncthreads();
     if (tid < kHeads) {
-      if (!kSplit) {
+      if (part_o == nullptr) {
         if (lse != nullptr) {
           const float l = l_s[tid];
           lse[(int64_t)r * kHeads + tid] = l > 0.f ? (m_s[tid] + log2f(l)) * 0.69314718055994531f : -INFINITY;
         }
       } else {
-        const int nsplit = gridDim.x;
-        float* ml = ws_ml + (((int64_t)r * nsplit + split) * kHeads + tid) * 2;
-        ml[0] = m_s[tid];
-        ml[1] = l_s[tid];
+        store_coherent(&part_ml[2 * tid], m_s[tid]);
+        store_coherent(&part_ml[2 * tid + 1], l_s[tid]);
       }
     }
   } else {
@@ -461,7 +471,7 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
       }
     }
     __syncthreads();                            // m_s / l_s written by the QK waves
-    if (!kSplit) {
+    if (part_o == nullptr) {
 #pragma unroll
       for (int ht = 0; ht < 4; ht++)
 #pragma unroll
@@ -474,18 +484,121 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
           for (int dt = 0; dt < 8; dt++) orow[16 * dt] = f32_to_bf16_bits(O[ht][dt][i] * inv);
         }
     } else {
-      const int nsplit = gridDim.x;
-      float* wo = ws_o + (((int64_t)r * nsplit + split) * kHeads) * kVal;
 #pragma unroll
       for (int ht = 0; ht < 4; ht++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int h = 16 * ht + 4 * g + i;
 #pragma unroll
-          for (int dt = 0; dt < 8; dt++) wo[(int64_t)h * kVal + 128 * qw + 16 * dt + c16] = O[ht][dt][i];
+          for (int dt = 0; dt < 8; dt++) store_coherent(&part_o[(int64_t)h * kVal + 128 * qw + 16 * dt + c16], O[ht][dt][i]);
         }
     }
   }
+}
+
+// One (row, split of its selection) per work-group; with one split the row is finished here,
+// otherwise its partial goes to the workspace for k_mla_combine.
+__global__ void __launch_bounds__(kThreads)
+k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, const int32_t* __restrict__ pos,
+             DevPages pg, const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx, int32_t k,
+             int keys_per_split, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+             float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  const int r = blockIdx.y, split = blockIdx.x, nsplit = gridDim.x;
+  const int j0 = split * keys_per_split;
+  const int nkeys = max(0, min(keys_per_split, k - j0));
+  float* po = nsplit > 1 ? ws_o + ((int64_t)r * nsplit + split) * kHeads * kVal : nullptr;
+  float* pml = nsplit > 1 ? ws_ml + ((int64_t)r * nsplit + split) * kHeads * 2 : nullptr;
+  mla_segment(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse, po, pml);
+}
+
+// Merges the two partials of one row (po: [2][64][512], pml: [2][64][2]) into the bf16
+// output and lse.  512 threads: thread t handles value dim t of every head, so each wave's
+// coherent loads read 256 contiguous bytes; the per-head weights are formed once in LDS.
+__device__ __forceinline__ void merge_two_parts(const float* po, const float* pml, int r, uint16_t* __restrict__ out,
+                                                float* __restrict__ lse) {
+  __shared__ float wgt[kHeads][3];             // per head: weight of part 0, of part 1, 1 / sum
+  const int t = threadIdx.x;
+  if (t < kHeads) {
+    const float m0 = load_coherent(&pml[2 * t]), l0 = load_coherent(&pml[2 * t + 1]);
+    const float m1 = load_coherent(&pml[2 * kHeads + 2 * t]), l1 = load_coherent(&pml[2 * kHeads + 2 * t + 1]);
+    const float M = fmaxf(m0, m1);
+    const float f0 = m0 == -INFINITY ? 0.f : exp2f(m0 - M), f1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
+    const float L = l0 * f0 + l1 * f1;
+    wgt[t][0] = f0;
+    wgt[t][1] = f1;
+    wgt[t][2] = L > 0.f ? 1.f / L : 0.f;
+    if (lse != nullptr) lse[(int64_t)r * kHeads + t] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  }
+  __syncthreads();                             // wgt ready
+  uint16_t* ocol = out + (int64_t)r * kHeads * kVal + t;
+  // in two halves of 32 heads: every coherent load of a half is issued before any result is
+  // used or stored, so they are in flight together (atomics keep their order with the stores)
+#pragma unroll
+  for (int h0 = 0; h0 < kHeads; h0 += kHeads / 2) {
+    float va[kHeads / 2], vb[kHeads / 2];
+#pragma unroll
+    for (int h = 0; h < kHeads / 2; h++) va[h] = load_coherent(po + (h0 + h) * kVal + t);
+#pragma unroll
+    for (int h = 0; h < kHeads / 2; h++) vb[h] = load_coherent(po + (kHeads + h0 + h) * kVal + t);
+#pragma unroll
+    for (int h = 0; h < kHeads / 2; h++)
+      ocol[(h0 + h) * kVal] =
+          f32_to_bf16_bits((va[h] * wgt[h0 + h][0] + vb[h] * wgt[h0 + h][1]) * wgt[h0 + h][2]);
+  }
+}
+
+// mla_segment as a call: the stream-K kernel runs several segments in a loop, and an
+// inlined body there would spill registers.
+__device__ __attribute__((noinline)) void mla_segment_call(const uint16_t* q, const int32_t* req, const int32_t* pos,
+                                                          const DevPages& pg, const uint8_t* cache, const int32_t* idx,
+                                                          int32_t k, float sm_log2, int r, int j0, int nkeys,
+                                                          uint16_t* out, float* lse, float* part_o, float* part_ml) {
+  mla_segment(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse, part_o, part_ml);
+}
+
+// Stream-K schedule for R >= gridDim.x: the R x T tiles (T = tiles per row) are cut into
+// gridDim.x equal consecutive ranges, one per work-group, each covering at least one full
+// row; a work-group runs its range as row segments.  A row cut between work-groups g-1 and
+// g (never more than two parts) leaves one partial from each in slot g; each writer waits
+// for its coherent partial stores to complete, then counts the slot, and the second writer
+// merges both parts (no work-group ever waits for another).  ctr[] must be zero at launch.
+__global__ void __launch_bounds__(kThreads)
+k_sparse_mla_stream(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, const int32_t* __restrict__ pos,
+                    DevPages pg, const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx, int32_t k,
+                    int32_t R, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+                    float* __restrict__ ws_o, float* __restrict__ ws_ml, int* __restrict__ ctr) {
+  __shared__ int s_old;
+  const int G = gridDim.x, gi = blockIdx.x;
+  const int T = (k + kTile - 1) / kTile;
+  const int64_t U = (int64_t)R * T;
+  const int64_t u0 = U * gi / G, u1 = U * (gi + 1) / G;
+  for (int64_t u = u0; u < u1;) {
+    const int r = (int)(u / T), t0 = (int)(u % T);
+    const int t1 = (int)(t0 + (u1 - u) < T ? t0 + (u1 - u) : T);
+    const int j0 = t0 * kTile, nkeys = min(t1 * kTile, k) - j0;
+    if (t0 == 0 && t1 == T) {
+      mla_segment_call(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse, nullptr, nullptr);
+    } else {
+      const int slot = t0 == 0 ? gi + 1 : gi, part = t0 == 0 ? 0 : 1;
+      float* po = ws_o + (int64_t)slot * 2 * kHeads * kVal;
+      float* pml = ws_ml + (int64_t)slot * 2 * kHeads * 2;
+      mla_segment_call(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse,
+                       po + (int64_t)part * kHeads * kVal, pml + part * kHeads * 2);
+      wait_vmcnt<0>();                          // this thread's part of the partial is stored ...
+      __syncthreads();
+      if (threadIdx.x == 0)                     // ... before the part is counted
+        s_old = __hip_atomic_fetch_add(&ctr[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (s_old == 1) merge_two_parts(po, pml, r, out, lse);   // both parts are in: merge them
+      __syncthreads();
+    }
+    u += t1 - t0;
+  }
+}
+
+__global__ void k_zero_counters(int* __restrict__ ctr, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    __hip_atomic_store(&ctr[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Merges the splits of one row: block = (row, head), 128 threads x 4 dims.
@@ -520,9 +633,13 @@ int choose_splits(int32_t R, int32_t k) {
   return s;
 }
 
+constexpr int kStreamGroups = 256;              // one persistent work-group per CU (LDS-bound)
+
 }  // namespace
 
 size_t mla_workspace_bytes(int32_t R, int32_t k) {
+  if (R >= kStreamGroups)      // stream-K: two partials and a counter per slot
+    return (size_t)(kStreamGroups + 1) * (2 * kHeads * (kVal + 2) * sizeof(float) + sizeof(int));
   const int s = choose_splits(R, k);
   if (s == 1) return 0;
   return (size_t)R * s * kHeads * (kVal + 2) * sizeof(float);
@@ -534,18 +651,29 @@ hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, con
   const int R = rows.n;
   if (R <= 0) return hipSuccess;
   DevPages g{pg.pt, pg.pt_stride, pg.num_reqs, pg.num_pages};
+  const float sm_log2 = sm_scale * kLog2e;
+  if (R >= kStreamGroups) {
+    if (ws == nullptr || ws_bytes < mla_workspace_bytes(R, k)) return hipErrorInvalidValue;
+    const int slots = kStreamGroups + 1;
+    float* wo = (float*)ws;
+    float* wml = wo + (size_t)slots * 2 * kHeads * kVal;
+    int* ctr = (int*)(wml + (size_t)slots * 2 * kHeads * 2);
+    hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(256), 0, s, ctr, slots);
+    hipLaunchKernelGGL(k_sparse_mla_stream, dim3(kStreamGroups), dim3(kThreads), 0, s, q, rows.req, rows.pos, g,
+                       cache, idx, k, R, sm_log2, out, lse, wo, wml, ctr);
+    return hipGetLastError();
+  }
   const int nsplit = choose_splits(R, k);
   const int kps = (k + nsplit - 1) / nsplit;
-  const float sm_log2 = sm_scale * kLog2e;
   if (nsplit == 1) {
-    hipLaunchKernelGGL(k_sparse_mla<false>, dim3(1, R), dim3(kThreads), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
+    hipLaunchKernelGGL(k_sparse_mla, dim3(1, R), dim3(kThreads), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
                        kps, sm_log2, out, lse, nullptr, nullptr);
     return hipGetLastError();
   }
   if (ws == nullptr || ws_bytes < mla_workspace_bytes(R, k)) return hipErrorInvalidValue;
   float* wo = (float*)ws;
   float* wml = wo + (size_t)R * nsplit * kHeads * kVal;
-  hipLaunchKernelGGL(k_sparse_mla<true>, dim3(nsplit, R), dim3(kThreads), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
+  hipLaunchKernelGGL(k_sparse_mla, dim3(nsplit, R), dim3(kThreads), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
                      kps, sm_log2, out, lse, wo, wml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

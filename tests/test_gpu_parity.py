@@ -146,6 +146,38 @@ def test_mla_stage(cid):
     print(f"  max abs err {err:.3g}")
 
 
+@pytest.mark.parametrize("k", [512, 500])
+def test_mla_stream_schedule_many_rows(k):
+    """R >= 256 rows take the stream-K schedule (rows cut across work-groups and merged by the
+    second writer); every row is checked, with a ragged last tile when k % 32 != 0."""
+    _announce(f"mla stream schedule R=258 k={k}")
+    w = gi.make_decode("mla_stream", gi.SEED_BASE + 60, [3000 + 7 * b for b in range(43)], rows_per_req=6)
+    assert w.R == 258
+    cache = oracle_latent_cache(w, 0)
+    _, _, qm = queries(w, [0])
+    rng = np.random.default_rng(k)
+    idx = np.full((w.R, k), -1, np.int32)
+    for r in range(w.R):
+        p = int(w.row_pos[r])
+        sel = rng.choice(p + 1, size=min(k, p + 1), replace=False)
+        idx[r, :len(sel)] = sel
+    idx[3, 100:] = -1                                   # a row with few valid keys
+    idx[7, :] = -1                                      # a row with none
+    ref, rlse = orc.sparse_mla(qm[0], w.row_req, w.row_pos, w.page_table, cache, idx, SM)
+    out = torch.empty((w.R, 64, 512), dtype=torch.int16, device=DEV)
+    lse = torch.empty((w.R, 64), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(dsa.dsa_sparse_mla_workspace_size(w.R, k), 256), dtype=torch.uint8, device=DEV)
+    for _ in range(2):                                  # the slot counters are reset on every call
+        out.fill_(0x7FC0)
+        dsa.dsa_sparse_mla_decode(dev(qm[0].view(np.int16)), rows_of(w), pages_of(w), dev(cache), dev(idx), out, lse, ws)
+        torch.cuda.synchronize()
+        assert_attention_close(host(out), ref)
+        g = host(lse)
+        fin = np.isfinite(rlse)
+        assert np.array_equal(np.isfinite(g), fin) and np.allclose(g[fin], rlse[fin], rtol=1e-4, atol=1e-4)
+    dsa.dsa_check_device_errors()
+
+
 def test_mla_special_cases():
     _announce("mla special cases")
     w = gi.config(0, "small")
