@@ -130,7 +130,7 @@ dsa_status dsa_indexer_logits(const uint8_t* q8, const float* qs, const float* w
   if (stride < dsa_logits_stride(rows->max_pos) || stride % 256)
     return fail(DSA_ERR_ARG, "dsa_indexer_logits: stride %lld < %lld or not a multiple of 256", (long long)stride,
                 (long long)dsa_logits_stride(rows->max_pos));
-  return hip_status(dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride, nullptr, 0,
+  return hip_status(dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride, dsa::LogitsMode{},
                                                (hipStream_t)stream),
                     "dsa_indexer_logits");
 }
@@ -153,12 +153,25 @@ dsa_status dsa_indexer_topk(const uint8_t* q8, const float* qs, const float* w, 
   const size_t need = dsa_topk_workspace_size(rows->n, stride, k);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(DSA_ERR_WORKSPACE, "dsa_indexer_topk: workspace %zu B < %zu B (256-B aligned)", ws_bytes, need);
+  // threshold-filtered: scores of one page in sixteen set a per-row threshold; the full pass
+  // keeps only the scores at or above it (the logits are not written); the exact top-k runs
+  // over those candidates; rows whose candidates turn out short (fewer than k) or overflow
+  // get full scores and the exact radix top-k instead, so the result never depends on the
+  // sample
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dsa::launch_topk_init(rows->n, k, ws, s);
+  const dsa::RowsView rv = view(rows);
+  const dsa::PagesView pv = view(pt);
+  const int R = rows->n;
+  hipError_t e = dsa::launch_topk_init(R, k, ws, s);
   if (e == hipSuccess)
-    e = dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride,
-                                   dsa::topk_range_ptr(ws, rows->n, k), k, s);
-  if (e == hipSuccess) e = dsa::launch_topk_from_range(logits, stride, view(rows), k, idx, ws, s);
+    e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_sample_mode(ws, R, k, k), s);
+  if (e == hipSuccess) e = dsa::launch_topk_threshold(logits, stride, rv, k, ws, s);
+  if (e == hipSuccess)
+    e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_filter_mode(ws, R, k, k), s);
+  if (e == hipSuccess) e = dsa::launch_topk_filtered_final(rv, stride, k, idx, ws, s);
+  if (e == hipSuccess)
+    e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_fallback_mode(ws, R, k), s);
+  if (e == hipSuccess) e = dsa::launch_topk_fallback(logits, stride, rv, k, idx, ws, s);
   return hip_status(e, "dsa_indexer_topk");
 }
 

@@ -24,21 +24,51 @@ hipError_t launch_index_k_store(const uint16_t* k, RowsView tok, PagesView pg, u
                                 double eps, const double* inv_freq32, hipStream_t s);
 hipError_t launch_latent_store(const uint16_t* kv, RowsView tok, PagesView pg, uint8_t* cache, hipStream_t s);
 
-// range (nullable): per-row [min, max] order-preserving keys of the visible logits, merged
-// with atomicMin / atomicMax (the caller initialises it).  skip_upto: row groups whose rows
-// all have pos + 1 <= skip_upto are not scored and their logits are not written (0: none).
+// What a launch of the indexer-logits kernel does with the scores.
+enum { kLogitsPlain = 0, kLogitsSample = 1, kLogitsFilter = 2, kLogitsFallback = 3 };
+struct LogitsMode {
+  int kind = kLogitsPlain;
+  // plain / sample: per-row [min, max] order-preserving keys of the visible scores, merged
+  // with atomicMin / atomicMax (nullable; the caller initialises it)
+  uint32_t* range = nullptr;
+  // row groups whose rows all have pos + 1 <= skip_upto are not scored, nothing written
+  int skip_upto = 0;
+  // sample: only every page_step-th page of each request is scored (and written)
+  int page_step = 1;
+  // filter: no logits are written; scores with key >= thr[row] are appended (key, position)
+  // to the row's list fkey / fpos [R][fcap], counted in fcnt[row] (a count above fcap means
+  // the list overflowed)
+  const uint32_t* thr = nullptr;
+  int* fcnt = nullptr;
+  uint32_t* fkey = nullptr;
+  int* fpos = nullptr;
+  int fcap = 0;
+  // fallback: plain scores for the row groups with a flagged row only
+  const int* flag = nullptr;
+};
 hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float* w, RowsView rows,
                                  PagesView pg, const uint8_t* cache, float* logits, int64_t stride,
-                                 uint32_t* range, int32_t skip_upto, hipStream_t s);
+                                 const LogitsMode& md, hipStream_t s);
 
 size_t topk_workspace_bytes(int32_t R, int64_t stride, int32_t k);
 hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
                        void* ws, hipStream_t s);
-// Pieces of the top-k used by the fused indexer + top-k entry.
+// Pieces of the top-k used by the fused indexer + top-k entry (threshold-filtered):
+//  init; sample scores (logits kernel, sample mode, with the row ranges); per-row threshold;
+//  filtered scores (logits kernel, filter mode); exact top-k over each row's candidates,
+//  flagging rows whose candidate list is short or overflowed; for the flagged rows only,
+//  full scores (logits kernel, fallback mode) and the radix top-k passes.
+constexpr int kTopkSampleStep = 16;        // one page in sixteen is sampled
 hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s);
-uint32_t* topk_range_ptr(void* ws, int32_t R, int32_t k);
-hipError_t launch_topk_from_range(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
-                                  void* ws, hipStream_t s);
+LogitsMode topk_sample_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto);
+hipError_t launch_topk_threshold(const float* logits, int64_t stride, RowsView rows, int32_t k, void* ws,
+                                 hipStream_t s);
+LogitsMode topk_filter_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto);
+hipError_t launch_topk_filtered_final(RowsView rows, int64_t stride, int32_t k, int32_t* idx, void* ws,
+                                      hipStream_t s);
+LogitsMode topk_fallback_mode(void* ws, int32_t R, int32_t k);
+hipError_t launch_topk_fallback(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
+                                void* ws, hipStream_t s);
 
 size_t mla_workspace_bytes(int32_t R, int32_t k);
 hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, const uint8_t* cache,

@@ -34,6 +34,7 @@ namespace dsa {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kStageAll = 768;          // filter mode: candidates held per work-group (all rows)
 constexpr int kQRow = kIdxDim + 16;     // q row pitch in LDS (padding spreads LDS banks)
 
 __device__ inline i32x8 load_b_operand(const uint8_t* key_row, int g) {
@@ -63,31 +64,51 @@ __device__ inline void load_page(PageRegs& P, const uint8_t* page, int lane) {
   P.ks = *reinterpret_cast<const float*>(page + kIdxScaleOff + 4 * lane);
 }
 
-template <int RG>
-__global__ void __launch_bounds__(256)
+template <int RG, int KIND>
+__global__ void __launch_bounds__(256, 4)
 k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
                 const int32_t* __restrict__ req, const int32_t* __restrict__ pos, DevPages pg,
                 const uint8_t* __restrict__ cache, float* __restrict__ logits, int64_t stride,
-                int chunk_pages, uint32_t* __restrict__ range, int skip_upto) {
+                int chunk_pages, LogitsMode md) {
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[RG * kIdxHeads * kQRow];
   __shared__ __attribute__((aligned(16))) float w_lds[RG * kIdxHeads];
+  // filter mode: candidates of this work-group, per row, before one append per row
+  constexpr int kStage = kStageAll / RG;     // per row
+  __shared__ uint32_t st_key[KIND == kLogitsFilter ? RG : 1][KIND == kLogitsFilter ? kStage : 1];
+  __shared__ int st_pos[KIND == kLogitsFilter ? RG : 1][KIND == kLogitsFilter ? kStage : 1];
+  __shared__ int st_n[RG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, k16 = lane & 15;
   const int64_t row0 = (int64_t)blockIdx.y * RG;
-  const int64_t pg0 = (int64_t)blockIdx.x * chunk_pages;
+  // pages are numbered in steps of page_step (the sample mode scores every page_step-th page)
+  const int step = KIND == kLogitsSample ? md.page_step : 1;
+  const int64_t pg0 = (int64_t)blockIdx.x * chunk_pages;          // in units of `step` pages
   const int64_t col_end = min((pg0 + chunk_pages) * 64, stride);
 
   int prow[RG];
   int pmax = -1;
+  bool flagged = false;
 #pragma unroll
-  for (int r = 0; r < RG; r++) { prow[r] = pos[row0 + r]; pmax = max(pmax, prow[r]); }
+  for (int r = 0; r < RG; r++) {
+    prow[r] = pos[row0 + r];
+    pmax = max(pmax, prow[r]);
+    if (KIND == kLogitsFallback) flagged |= md.flag[row0 + r] != 0;
+  }
   // every row of the group sees at most skip_upto keys: its top-k is all of them and needs
   // no score (the fused indexer + top-k passes k here; nothing of the group is written)
-  if (pmax + 1 <= skip_upto) return;
+  if (pmax + 1 <= md.skip_upto) return;
+  if (KIND == kLogitsFallback && !flagged) return;     // no row of the group needs the full scores
+  uint32_t thr[RG];
+  if (KIND == kLogitsFilter) {
+#pragma unroll
+    for (int r = 0; r < RG; r++) thr[r] = md.thr[row0 + r];
+    if (tid < RG) st_n[tid] = 0;
+  }
   const int32_t rq = req[row0];
-  // pages with a visible key (never past the logits row)
-  const int64_t pend = min(min(pg0 + chunk_pages, (int64_t)(pmax >> 6) + 1), stride / 64);
+  // pages with a visible key (never past the logits row), in units of `step`
+  const int64_t vis_pages = min((int64_t)(pmax >> 6) + 1, stride / 64);
+  const int64_t pend = min(pg0 + chunk_pages, (vis_pages + step - 1) / step);
 
   if (pg0 < pend) {
     // stage q (RG x 32 heads x 128 B, rows padded) and w*q_scale in LDS; the MFMA A operands
@@ -105,12 +126,12 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     // group's rows (only kept when the fused top-k asked for row ranges; a range covering a
     // row's keys is all the radix select needs, so the group's union serves each of its rows)
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-    // score one page (held in registers) for all RG rows and store its 64 logits per row
-    auto process = [&](const PageRegs& P, int64_t pi, int64_t pid) {
+    // score one page (held in registers) for all RG rows
+    auto process = [&](const PageRegs& P, int64_t vi, int64_t pid) {
       // keep the per-page LDS reads of q / w inside the loop (hoisting them would pin all
       // rows' operands in registers again)
       __asm__ volatile("" ::: "memory");
-      const int64_t s = pi * 64 + lane;
+      const int64_t s = vi * step * 64 + lane;
 #pragma unroll
       for (int r = 0; r < RG; r++) {
         i32x8 A[2];
@@ -148,32 +169,40 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         const float mine = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
         const bool vis = pid >= 0 && s <= prow[r];
         const float v = vis ? mine * P.ks : -INFINITY;
-        logits[(row0 + r) * stride + s] = v;
-        if (range != nullptr && s <= prow[r]) {
-          const uint32_t u = __float_as_uint(v);
-          const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-          kmn = min(kmn, key);
-          kmx = max(kmx, key);
+        const uint32_t u = __float_as_uint(v);
+        const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        if (KIND == kLogitsFilter) {
+          // keep the scores at or above the row's threshold (rare: a few per cent)
+          if (vis && key >= thr[r]) {
+            const int sl = atomicAdd(&st_n[r], 1);
+            if (sl < kStage) { st_key[r][sl] = key; st_pos[r][sl] = (int)s; }
+          }
+        } else {
+          logits[(row0 + r) * stride + s] = v;
+          if (md.range != nullptr && s <= prow[r]) {
+            kmn = min(kmn, key);
+            kmx = max(kmx, key);
+          }
         }
       }
     };
     // two register buffers in ping-pong: the next page loads while this one is scored
     PageRegs pa, pb;
     int64_t pi = pg0 + wave;
-    int64_t ida = pi < pend ? page_of(pg, rq, pi * 64) : -1;
+    int64_t ida = pi < pend ? page_of(pg, rq, pi * step * 64) : -1;
     if (pi < pend && ida >= 0) load_page(pa, cache + ida * kIdxPageBytes, lane);
     for (; pi < pend; pi += 2 * kWaves) {
       const int64_t pn = pi + kWaves;
-      const int64_t idb = pn < pend ? page_of(pg, rq, pn * 64) : -1;
+      const int64_t idb = pn < pend ? page_of(pg, rq, pn * step * 64) : -1;
       if (pn < pend && idb >= 0) load_page(pb, cache + idb * kIdxPageBytes, lane);
       process(pa, pi, ida);
       if (pn >= pend) break;
       const int64_t pn2 = pn + kWaves;
-      ida = pn2 < pend ? page_of(pg, rq, pn2 * 64) : -1;
+      ida = pn2 < pend ? page_of(pg, rq, pn2 * step * 64) : -1;
       if (pn2 < pend && ida >= 0) load_page(pa, cache + ida * kIdxPageBytes, lane);
       process(pb, pn, idb);
     }
-    if (range != nullptr) {
+    if (KIND != kLogitsFilter && md.range != nullptr) {
       __shared__ uint32_t red[kWaves][2];
       uint32_t mn = kmn, mx = kmx;
 #pragma unroll
@@ -186,39 +215,75 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       if (tid < RG) {
         for (int w2 = 0; w2 < kWaves; w2++) { mn = min(mn, red[w2][0]); mx = max(mx, red[w2][1]); }
         if (mn <= mx) {
-          atomicMin(&range[2 * (row0 + tid)], mn);
-          atomicMax(&range[2 * (row0 + tid) + 1], mx);
+          atomicMin(&md.range[2 * (row0 + tid)], mn);
+          atomicMax(&md.range[2 * (row0 + tid) + 1], mx);
         }
       }
     }
-  }
-  // columns of this chunk past the group's last visible page
-  const int64_t fill0 = max(pend, pg0) * 64;
-  for (int64_t c = fill0 + tid; c < col_end; c += 256)
+    if (KIND == kLogitsFilter) {
+      // one append per row: reserve room in the row's candidate list, then copy
+      __shared__ int st_base[RG];
+      __syncthreads();
+      if (tid < RG) {
+        const int n = st_n[tid];
+        // a stage overflow makes the row's count exceed the list, which sends the row to the
+        // exact fallback
+        st_base[tid] = n == 0 ? 0 : atomicAdd(&md.fcnt[row0 + tid], n <= kStage ? n : md.fcap + 1);
+      }
+      __syncthreads();
 #pragma unroll
-    for (int r = 0; r < RG; r++) logits[(row0 + r) * stride + c] = -INFINITY;
+      for (int r = 0; r < RG; r++) {
+        const int n = min(st_n[r], kStage), base = st_base[r];
+        for (int i = tid; i < n; i += 256)
+          if (base + i < md.fcap) {
+            md.fkey[(row0 + r) * md.fcap + base + i] = st_key[r][i];
+            md.fpos[(row0 + r) * md.fcap + base + i] = st_pos[r][i];
+          }
+      }
+    }
+  }
+  if (KIND == kLogitsPlain || KIND == kLogitsFallback) {
+    // columns of this chunk past the group's last visible page
+    const int64_t fill0 = max(pend, pg0) * 64;
+    for (int64_t c = fill0 + tid; c < col_end; c += 256)
+#pragma unroll
+      for (int r = 0; r < RG; r++) logits[(row0 + r) * stride + c] = -INFINITY;
+  }
+}
+
+template <int RG, int KIND>
+hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsView rows, DevPages g,
+                     const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md, hipStream_t s) {
+  const int64_t n_groups = rows.n / RG;
+  const int step = KIND == kLogitsSample ? md.page_step : 1;
+  const int64_t total_pages = (stride / 64 + step - 1) / step;      // in units of `step` pages
+  // enough work-groups to cover the chip (each page is one wave-iteration); the sampling pass
+  // reads few pages, so it stops at one round of resident work-groups to amortise the q staging
+  const int64_t want = KIND == kLogitsSample ? 1024 : 2048;
+  int chunk = 32;
+  while (chunk > 4 && n_groups * ((total_pages + chunk - 1) / chunk) < want) chunk >>= 1;
+  const int64_t nchunks = (total_pages + chunk - 1) / chunk;
+  hipLaunchKernelGGL((k_logits_decode<RG, KIND>), dim3((unsigned)nchunks, (unsigned)n_groups), dim3(256), 0, s, q8, qs,
+                     w, rows.req, rows.pos, g, cache, logits, stride, chunk, md);
+  return hipGetLastError();
 }
 
 template <int RG>
-hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsView rows, DevPages g,
-                     const uint8_t* cache, float* logits, int64_t stride, uint32_t* range, int skip_upto,
-                     hipStream_t s) {
-  const int64_t n_groups = rows.n / RG;
-  const int64_t total_pages = stride / 64;
-  // enough work-groups to cover the chip (each page is one wave-iteration)
-  int chunk = 32;
-  while (chunk > 4 && n_groups * ((total_pages + chunk - 1) / chunk) < 2048) chunk >>= 1;
-  const int64_t nchunks = (total_pages + chunk - 1) / chunk;
-  hipLaunchKernelGGL(k_logits_decode<RG>, dim3((unsigned)nchunks, (unsigned)n_groups), dim3(256), 0, s, q8, qs, w,
-                     rows.req, rows.pos, g, cache, logits, stride, chunk, range, skip_upto);
-  return hipGetLastError();
+hipError_t launch_kind(const uint8_t* q8, const float* qs, const float* w, RowsView rows, DevPages g,
+                       const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md, hipStream_t s) {
+  switch (md.kind) {
+    case kLogitsSample: return launch_rg<RG, kLogitsSample>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case kLogitsFilter: return launch_rg<RG, kLogitsFilter>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case kLogitsFallback: return launch_rg<RG, kLogitsFallback>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    default: return launch_rg<RG, kLogitsPlain>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float* w, RowsView rows, PagesView pg,
-                                 const uint8_t* cache, float* logits, int64_t stride, uint32_t* range,
-                                 int32_t skip_upto, hipStream_t s) {
+                                 const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md,
+                                 hipStream_t s) {
   if (rows.n <= 0) return hipSuccess;
   DevPages g{pg.pt, pg.pt_stride, pg.num_reqs, pg.num_pages};
   // rows of a group are processed in sub-groups of the largest divisor of `group` <= 6
@@ -227,12 +292,12 @@ hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float
   for (int d = 6; d >= 1; d--)
     if (rows.group % d == 0) { rg = d; break; }
   switch (rg) {
-    case 6: return launch_rg<6>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
-    case 5: return launch_rg<5>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
-    case 4: return launch_rg<4>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
-    case 3: return launch_rg<3>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
-    case 2: return launch_rg<2>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
-    default: return launch_rg<1>(q8, qs, w, rows, g, cache, logits, stride, range, skip_upto, s);
+    case 6: return launch_kind<6>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case 5: return launch_kind<5>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case 4: return launch_kind<4>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case 3: return launch_kind<3>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case 2: return launch_kind<2>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    default: return launch_kind<1>(q8, qs, w, rows, g, cache, logits, stride, md, s);
   }
 }
 

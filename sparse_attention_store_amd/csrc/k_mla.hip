@@ -17,12 +17,15 @@
 //    f8f6f4 fed with the cached codes and their ue8m0 scales as E8M0 operands, against a
 //    two-term FP8 expansion of q that keeps bf16's precision; the 64 rope dims on the bf16
 //    MFMA), run the online softmax (exp2
-//    domain, lazy rescaling of the running max) and write P scaled by each key's block scale
-//    for the four value blocks; at the same time waves 4-7 accumulate O += P V for tile t-1
-//    (each owns 128 value dims of all 64 heads), V read transposed straight from the fp8 key
-//    tile with ds_read_b64_tr_b8.  Each SIMD so hosts one VALU-heavy and one MFMA-heavy wave.
-//  * A split's un-normalised O, running max and sum go to a workspace and a combine
-//    kernel merges the splits; with one split the kernel normalises and writes bf16.
+//    domain, lazy rescaling of the running max) and write P (fp32) to LDS; at the same time
+//    waves 4-7 accumulate O += P V for tile t-1 (each owns 128 value dims = one value block
+//    of all 64 heads): they scale P by each key's scale of their block, pack it to bf16 and
+//    read V transposed straight from the fp8 key tile with ds_read_b64_tr_b8.  Each SIMD so
+//    hosts one VALU-heavy and one MFMA-heavy wave.
+//  * Few rows (R < 256): a split's un-normalised O, running max and sum go to a workspace
+//    and a combine kernel merges the splits; with one split the kernel normalises and writes
+//    bf16.  Many rows: a stream-K schedule, one persistent work-group per CU over equal
+//    ranges of all rows' tiles; a row cut between two work-groups is merged by the second.
 #include "dsa_device.hpp"
 #include "dsa_internal.h"
 

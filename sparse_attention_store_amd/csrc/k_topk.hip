@@ -33,22 +33,35 @@ constexpr int kBins = 4096;          // first digit: 12 bits over the row's key 
 constexpr int kCap = 4096;           // candidates kept per row
 constexpr int kChunk = 8192;         // logits per work-group in passes 1-3
 constexpr int kFinalThreads = 1024;
+// Two 1024-thread work-groups per CU need 8 waves per SIMD, and measured on the device a SIMD
+// holds 8 waves only when each uses at most about 60 scalar registers (a kernel of 76 runs one
+// work-group per CU, whatever its LDS and vector registers), so such kernels cap them.
+#define DSA_TWO_GROUPS_PER_CU __attribute__((amdgpu_num_sgpr(56)))
+constexpr int kBufferWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit raw reads
+constexpr int kThrSamples = 16384;  // sampled keys a threshold work-group holds in registers
+static_assert(kThrSamples % kFinalThreads == 0 && kCap % kFinalThreads == 0, "whole loads per thread");
 constexpr int kBitmapMaxN = 1 << 18; // rows up to 256K positions use the LDS bitmap (32 KiB)
+// fused path: the filter keeps about kMarginNum / kMarginDen times k candidates per row
+constexpr int kMarginNum = 3, kMarginDen = 2;
 
 struct Ws {
   uint32_t* range;  // [R][2]: min key, max key
   int* hist;        // [R][kBins]
-  int* cnt;         // [R][4]: 0 = selected-above count, 1 = candidate count, 2 = threshold bin T
+  int* cnt;         // [R][4]: 0 = selected-above count, 1 = candidate count, 2 = threshold bin T,
+                    //         3 = filtered candidate count (fused path)
   int* above;       // [R][k]
-  uint32_t* ckey;   // [R][kCap]
+  uint32_t* ckey;   // [R][kCap]   radix candidates, or the fused path's filtered candidates
   int* cpos;        // [R][kCap]
+  uint32_t* thr;    // [R]  fused path: key threshold of the filter
+  int* fcnt;        // [R]  fused path: filtered candidates of the row (may exceed kCap)
+  int* flag;        // [R]  fused path: the row needs the exact fallback
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 __host__ __device__ inline size_t ws_bytes(int32_t R, int32_t k) {
   return align256((size_t)R * 8) + align256((size_t)R * kBins * 4) + align256((size_t)R * 16) +
-         align256((size_t)R * k * 4) + 2 * align256((size_t)R * kCap * 4);
+         align256((size_t)R * k * 4) + 2 * align256((size_t)R * kCap * 4) + 3 * align256((size_t)R * 4);
 }
 
 __host__ __device__ inline Ws carve(void* base, int32_t R, int32_t k) {
@@ -59,7 +72,10 @@ __host__ __device__ inline Ws carve(void* base, int32_t R, int32_t k) {
   w.cnt = (int*)p;         p += align256((size_t)R * 16);
   w.above = (int*)p;       p += align256((size_t)R * k * 4);
   w.ckey = (uint32_t*)p;   p += align256((size_t)R * kCap * 4);
-  w.cpos = (int*)p;
+  w.cpos = (int*)p;        p += align256((size_t)R * kCap * 4);
+  w.thr = (uint32_t*)p;    p += align256((size_t)R * 4);
+  w.fcnt = (int*)p;        p += align256((size_t)R * 4);
+  w.flag = (int*)p;
   return w;
 }
 
@@ -85,7 +101,7 @@ __global__ void k_init(Ws w, int32_t R) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_hist; i += (int64_t)gridDim.x * blockDim.x) {
     w.hist[i] = 0;
     if (i < (int64_t)R * 4) w.cnt[i] = 0;
-    if (i < R) { w.range[2 * i] = 0xFFFFFFFFu; w.range[2 * i + 1] = 0u; }
+    if (i < R) { w.range[2 * i] = 0xFFFFFFFFu; w.range[2 * i + 1] = 0u; w.flag[i] = 0; w.fcnt[i] = 0; }
   }
 }
 
@@ -101,10 +117,13 @@ __device__ inline void block_minmax256(uint32_t& mn, uint32_t& mx, uint32_t* sh)
     for (int i = 1; i < 4; i++) { mn = min(mn, sh[2 * i]); mx = max(mx, sh[2 * i + 1]); }
 }
 
+// `gate` (nullable): only rows with gate[r] != 0 are processed (the fused path's fallback).
 __global__ void __launch_bounds__(256) k_range(const float* __restrict__ logits, int64_t stride,
-                                               const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+                                               const int32_t* __restrict__ pos, int32_t k, Ws ws,
+                                               const int* __restrict__ gate) {
   __shared__ uint32_t sh[8];
   const int r = blockIdx.y;
+  if (gate != nullptr && !gate[r]) return;
   const int64_t n = row_len(pos, r, stride);
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   if (n <= k || c0 >= n) return;
@@ -137,9 +156,11 @@ __device__ inline void load_chunk(const float* row, int64_t c0, int64_t c1, floa
 }
 
 __global__ void __launch_bounds__(256) k_hist(const float* __restrict__ logits, int64_t stride,
-                                              const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+                                              const int32_t* __restrict__ pos, int32_t k, Ws ws,
+                                              const int* __restrict__ gate) {
   __shared__ int h[kBins];
   const int r = blockIdx.y;
+  if (gate != nullptr && !gate[r]) return;
   const int64_t n = row_len(pos, r, stride);
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   if (n <= k || c0 >= n) return;
@@ -168,26 +189,45 @@ __global__ void __launch_bounds__(256) k_hist(const float* __restrict__ logits, 
     if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
+// Inclusive prefix sum of v over the NT threads of the work-group in thread order (a wave
+// scan by lane shuffles, then the wave totals); *total receives the sum over all threads.
+// wsum holds NT / 64 ints of LDS.  Every thread calls it; it synchronises the work-group.
+template <int NT>
+__device__ inline int block_prefix(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; i++) {
+    const int x = wsum[i];
+    before += i < w ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return v + before;
+}
+
 // Threshold bin of an LDS histogram: the bin b with count(bins > b) < k <= count(bins >= b).
-// result[0] = b, result[1] = count(bins > b).  blockDim.x == NT, NB % NT == 0.
+// result[0] = b, result[1] = count(bins > b).  blockDim.x == NT, NB % NT == 0.  Thread t
+// holds the t-th block of bins from the top, so a prefix over threads is a suffix over bins.
 template <int NT, int NB>
 __device__ inline int find_threshold(const int* h, int k, int* scan, int* result) {
   constexpr int per = NB / NT;
-  const int t = threadIdx.x;
+  const int b = NT - 1 - (int)threadIdx.x;
   int local = 0;
-  for (int i = 0; i < per; i++) local += h[t * per + i];
-  scan[t] = local;
-  __syncthreads();
-  for (int o = 1; o < NT; o <<= 1) {          // inclusive suffix sums (Hillis-Steele)
-    const int v = scan[t] + (t + o < NT ? scan[t + o] : 0);
-    __syncthreads();
-    scan[t] = v;
-    __syncthreads();
-  }
-  int running = scan[t] - local;
+  for (int i = 0; i < per; i++) local += h[b * per + i];
+  int all;
+  int running = block_prefix<NT>(local, scan, &all) - local;   // keys in the bins above this block
   for (int i = per - 1; i >= 0; i--) {
-    const int c = h[t * per + i];
-    if (running < k && running + c >= k) { result[0] = t * per + i; result[1] = running; }
+    const int c = h[b * per + i];
+    if (running < k && running + c >= k) { result[0] = b * per + i; result[1] = running; }
     running += c;
   }
   __syncthreads();
@@ -195,11 +235,13 @@ __device__ inline int find_threshold(const int* h, int k, int* scan, int* result
 }
 
 // Per row: the threshold bin T from the merged histogram (one work-group per row).
-__global__ void __launch_bounds__(256) k_thresh(const int32_t* __restrict__ pos, int64_t stride, int32_t k, Ws ws) {
+__global__ void __launch_bounds__(256) k_thresh(const int32_t* __restrict__ pos, int64_t stride, int32_t k, Ws ws,
+                                                const int* __restrict__ gate) {
   __shared__ int h[kBins];
-  __shared__ int scan[256];
+  __shared__ int scan[256 / 64];
   __shared__ int res[2];
   const int r = blockIdx.x;
+  if (gate != nullptr && !gate[r]) return;
   if (row_len(pos, r, stride) <= k) return;
   for (int i = threadIdx.x; i < kBins; i += 256) h[i] = ws.hist[(int64_t)r * kBins + i];
   __syncthreads();
@@ -210,12 +252,14 @@ __global__ void __launch_bounds__(256) k_thresh(const int32_t* __restrict__ pos,
 constexpr int kSelCap = 1024;    // candidates gathered per work-group before spilling to global appends
 
 __global__ void __launch_bounds__(256) k_select(const float* __restrict__ logits, int64_t stride,
-                                                const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+                                                const int32_t* __restrict__ pos, int32_t k, Ws ws,
+                                                const int* __restrict__ gate) {
   __shared__ int l_above[kTopkMax];
   __shared__ uint32_t l_ckey[kSelCap];
   __shared__ int l_cpos[kSelCap];
   __shared__ int n_above, n_cand, base_above, base_cand;
   const int r = blockIdx.y;
+  if (gate != nullptr && !gate[r]) return;
   const int64_t n = row_len(pos, r, stride);
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   if (n <= k || c0 >= n) return;
@@ -287,27 +331,58 @@ __device__ inline void bitonic_sort(int* a, int n) {
   }
 }
 
-__device__ inline void block_scan_inclusive(int* scan, int tid) {
-  for (int o = 1; o < kFinalThreads; o <<= 1) {
-    const int v = scan[tid] + (tid >= o ? scan[tid - o] : 0);
+// Writes the ns <= k selected positions sel[] of a row of n positions to out[0..k) in
+// ascending order, -1 after them: an LDS bitmap of the row and a prefix count of set bits
+// (rows up to kBitmapMaxN), else an LDS bitonic sort.  All kFinalThreads threads call it.
+__device__ inline void write_ascending(int* sel, int ns, int64_t n, int k, int32_t* out, uint32_t* bitmap,
+                                       int* scan) {
+  const int tid = threadIdx.x;
+  if (n <= kBitmapMaxN) {
+    const int nwords = (int)((n + 31) / 32);
+    for (int i = tid; i < nwords; i += kFinalThreads) bitmap[i] = 0u;
     __syncthreads();
-    scan[tid] = v;
+    for (int i = tid; i < ns; i += kFinalThreads) atomicOr(&bitmap[sel[i] >> 5], 1u << (sel[i] & 31));
     __syncthreads();
+    const int per = (nwords + kFinalThreads - 1) / kFinalThreads;      // words per thread
+    const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
+    int c = 0;
+    for (int wd = w0; wd < w1; wd++) c += __popc(bitmap[wd]);
+    int all;
+    int o = block_prefix<kFinalThreads>(c, scan, &all) - c;
+    for (int wd = w0; wd < w1; wd++) {
+      uint32_t m = bitmap[wd];
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1;
+        if (o < k) out[o] = wd * 32 + b;
+        o++;
+      }
+    }
+    for (int j = ns + tid; j < k; j += kFinalThreads) out[j] = -1;
+  } else {
+    for (int i = ns + tid; i < kTopkMax; i += kFinalThreads) sel[i] = 0x7FFFFFFF;
+    __syncthreads();
+    int m = 1;
+    while (m < k) m <<= 1;
+    bitonic_sort(sel, m);
+    for (int j = tid; j < k; j += kFinalThreads) out[j] = j < ns ? sel[j] : -1;
   }
 }
 
 __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict__ logits, int64_t stride,
                                                          const int32_t* __restrict__ pos, int32_t k,
-                                                         int32_t* __restrict__ idx, Ws ws) {
+                                                         int32_t* __restrict__ idx, Ws ws,
+                                                         const int* __restrict__ gate) {
   __shared__ uint32_t skey[kCap];
   __shared__ int spos[kCap];
   __shared__ int sel[kTopkMax];
   __shared__ uint32_t bitmap[kBitmapMaxN / 32];
   __shared__ int h[1024];
-  __shared__ int scan[kFinalThreads];
+  __shared__ int scan[kFinalThreads / 64];
   __shared__ int res[2];
-  __shared__ int nsel, nties;
+  __shared__ int nsel;
   const int r = blockIdx.x, tid = threadIdx.x;
+  if (gate != nullptr && !gate[r]) return;
   const int64_t n = row_len(pos, r, stride);
   int32_t* out = idx + (int64_t)r * k;
   if (n <= k) {                       // short context or padded row: every visible position
@@ -324,7 +399,7 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
   const bool in_lds = nc <= kCap;
   if (in_lds)
     for (int i = tid; i < nc; i += kFinalThreads) { skey[i] = ws.ckey[(int64_t)r * kCap + i]; spos[i] = ws.cpos[(int64_t)r * kCap + i]; }
-  if (tid == 0) { nsel = 0; nties = 0; }
+  if (tid == 0) nsel = 0;
   __syncthreads();
   // threshold bin, recovered from any candidate (all share it)
   const uint32_t T = ((in_lds ? skey[0] : ws.ckey[(int64_t)r * kCap]) - kmin) >> shift;
@@ -374,56 +449,211 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
     }
   } else {
     // more candidates than LDS holds: walk the row in position order
+    int nties_seen = 0;
     for (int64_t b = 0; b < n; b += kFinalThreads) {
       const int64_t i = b + tid;
       const uint32_t key = i < n ? min(max(ord_key(row[i]), kmin), kmax) : 0u;
       const bool inT = i < n && ((key - kmin) >> shift) == T;
       if (inT && key > thr) push(sel, &nsel, (int)i);
       const int tie = (inT && key == thr) ? 1 : 0;
-      scan[tid] = tie;
-      __syncthreads();
-      block_scan_inclusive(scan, tid);
-      const int before = nties;
-      if (tie && before + scan[tid] - 1 < need_ties) push(sel, &nsel, (int)i);
-      __syncthreads();
-      if (tid == 0) nties = before + scan[kFinalThreads - 1];
-      __syncthreads();
+      int all;
+      const int incl = block_prefix<kFinalThreads>(tie, scan, &all);
+      if (tie && nties_seen + incl - 1 < need_ties) push(sel, &nsel, (int)i);
+      nties_seen += all;
     }
   }
   __syncthreads();
-  const int ns = min(nsel, k);
-  if (n <= kBitmapMaxN) {
-    // ascending order through a bitmap of the row and a prefix count of set bits
-    const int nwords = (int)((n + 31) / 32);
-    for (int i = tid; i < nwords; i += kFinalThreads) bitmap[i] = 0u;
+  write_ascending(sel, min(nsel, k), n, k, out, bitmap, scan);
+}
+
+// ----------------------------------------------------------------------------- fused path
+// Per row: the filter threshold from the sampled scores (pages 0, S, 2S, ... of the row,
+// positions <= pos).  With n_s sampled positions of the row's n, m = ceil(margin * k * n_s / n)
+// samples should pass; the threshold is the lower edge of the histogram bin holding the
+// m-th largest sample, so at least m samples, and about margin * k of the row's scores,
+// lie at or above it.  Short rows (n <= k) get a threshold nothing reaches; rows with too
+// few samples get 0 (every score passes).
+__global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt_thresh(const float* __restrict__ logits, int64_t stride,
+                                                                  const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+  constexpr int step = kTopkSampleStep;
+  __shared__ int h[kBins];
+  __shared__ int scan[kFinalThreads / 64];
+  __shared__ int res[2];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t n = row_len(pos, r, stride);
+  if (n <= k) {
+    if (tid == 0) ws.thr[r] = 0xFFFFFFFFu;
+    return;
+  }
+  const int64_t nsp = ((n + 63) / 64 + step - 1) / step;            // sampled pages
+  const int64_t last = (nsp - 1) * step * 64;                        // first position of the last one
+  const int64_t ns = (nsp - 1) * 64 + min((int64_t)64, n - last);    // sampled positions
+  const int64_t m = (kMarginNum * (int64_t)k * ns + kMarginDen * n - 1) / (kMarginDen * n);
+  if (m > ns) {
+    if (tid == 0) ws.thr[r] = 0u;
+    return;
+  }
+  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
+  const float* row = logits + (int64_t)r * stride;
+  // rows with few enough samples keep theirs in registers for both rounds, all requested
+  // before any is used (the pass is latency-bound, not bandwidth-bound)
+  constexpr int kPer = kThrSamples / kFinalThreads;
+  const bool held = ns <= kThrSamples;
+  uint32_t v[kPer];
+  if (held) {
+    // sample i = tid + j * kFinalThreads sits at position (i / 64) * step * 64 + i % 64: one
+    // lane offset plus a per-j constant, read through a buffer descriptor of the row's n scores
+    // (reads past it return 0 and are not counted below)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, (int)(n * 4), kBufferWord3);
+    const int o0 = ((tid >> 6) * (step * 64) + (tid & 63)) * 4;
+    constexpr int kJump = (kFinalThreads / 64) * step * 64 * 4;
+    float x[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o0, j * kJump, 0));
+#pragma unroll
+    for (int j = 0; j < kPer; j++) v[j] = min(max(ord_key(x[j]), kmin), kmax) - kmin;
+  }
+  // this thread's samples are v[0 .. jn): sample tid + j * kFinalThreads exists for j < jn
+  const int jn = held ? (int)min((int64_t)kPer, (ns - tid + kFinalThreads - 1) / kFinalThreads) : 0;
+  // two 12-bit rounds over (key - kmin): keys are close to logarithmic in the score, so one
+  // round's bin near the top of the range is far too wide a step for the threshold
+  const int shift = range_shift(kmin, kmax);
+  uint32_t prefix = 0;                 // high bits of (threshold - kmin) found so far
+  int low = shift + 12, need = (int)m;
+  for (int round = 0; round < 2 && low > 0; round++) {
+    const int take = low > 12 ? 12 : low;
+    const int sh = low - take;
+    for (int i = tid; i < kBins; i += kFinalThreads) h[i] = 0;
     __syncthreads();
-    for (int i = tid; i < ns; i += kFinalThreads) atomicOr(&bitmap[sel[i] >> 5], 1u << (sel[i] & 31));
-    __syncthreads();
-    const int per = (nwords + kFinalThreads - 1) / kFinalThreads;      // words per thread
-    const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
-    int c = 0;
-    for (int wd = w0; wd < w1; wd++) c += __popc(bitmap[wd]);
-    scan[tid] = c;
-    __syncthreads();
-    block_scan_inclusive(scan, tid);
-    int o = scan[tid] - c;
-    for (int wd = w0; wd < w1; wd++) {
-      uint32_t m = bitmap[wd];
-      while (m) {
-        const int b = __ffs(m) - 1;
-        m &= m - 1;
-        if (o < k) out[o] = wd * 32 + b;
-        o++;
+    if (held) {
+#pragma unroll
+      for (int j = 0; j < kPer; j++)
+        if (j < jn && (low >= 32 || (v[j] >> low) == prefix)) atomicAdd(&h[(v[j] >> sh) & (kBins - 1)], 1);
+    } else {
+      for (int64_t i = tid; i < ns; i += kFinalThreads) {
+        const int64_t s = (i >> 6) * step * 64 + (i & 63);
+        const uint32_t u = min(max(ord_key(row[s]), kmin), kmax) - kmin;
+        if (low >= 32 || (u >> low) == prefix) atomicAdd(&h[(u >> sh) & (kBins - 1)], 1);
       }
     }
-  } else {
-    for (int i = ns + tid; i < kTopkMax; i += kFinalThreads) sel[i] = 0x7FFFFFFF;
     __syncthreads();
-    int m = 1;
-    while (m < k) m <<= 1;
-    bitonic_sort(sel, m);
-    for (int j = tid; j < k; j += kFinalThreads) out[j] = sel[j];
+    const int d = find_threshold<kFinalThreads, kBins>(h, need, scan, res);
+    need -= res[1];
+    prefix = (prefix << take) | (uint32_t)d;
+    low = sh;
+    __syncthreads();
   }
+  if (tid == 0) ws.thr[r] = kmin + (prefix << low);   // lower edge of the final bin
+}
+
+// The need-th largest (1 <= need <= cnt) of keys[0..cnt) in LDS, all in [base, base + 2^width),
+// in radix rounds of at most 11 bits over (key - base) from bit `width` down.  need_eq receives
+// how many keys equal to it belong to the need largest.  All kFinalThreads threads call it;
+// h holds kFinalBins ints.
+constexpr int kFinalBits = 11;
+constexpr int kFinalBins = 1 << kFinalBits;
+__device__ inline uint32_t kth_largest(const uint32_t* keys, int cnt, int need, uint32_t base, int width, int* h,
+                                       int* scan, int* res, int& need_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0;
+  int low = width;
+  while (low > 0) {
+    const int take = low > kFinalBits ? kFinalBits : low;
+    const int sh = low - take;
+    for (int i = tid; i < kFinalBins; i += kFinalThreads) h[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < cnt; i += kFinalThreads) {
+      const uint32_t v = keys[i] - base;
+      if (low >= 32 || (v >> low) == prefix) atomicAdd(&h[(v >> sh) & ((1u << take) - 1)], 1);
+    }
+    __syncthreads();
+    const int d = find_threshold<kFinalThreads, kFinalBins>(h, need, scan, res);
+    need -= res[1];
+    prefix = (prefix << take) | (uint32_t)d;
+    low = sh;
+    __syncthreads();
+  }
+  need_eq = need;
+  return base + prefix;
+}
+
+// Per row: the exact top-k among its filtered candidates (all scores >= the threshold), in
+// LDS; rows with fewer than k candidates or an overflowed list are flagged for the exact
+// fallback instead.  Among exactly equal scores at the k-th the lower positions are kept:
+// the tied positions go to their own list, and when it holds more than are needed a second
+// selection over the complemented positions picks the lowest.
+__global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ pos, int64_t stride,
+                                                              int32_t k, int32_t* __restrict__ idx, Ws ws) {
+  // Under 64 KiB of LDS, so two work-groups share a CU.  The candidates (keys, then positions)
+  // and, once they are selected, the output bitmap share one buffer; the radix histogram lives
+  // in whichever of the tie list and the candidate buffer is idle at the time.
+  __shared__ uint32_t cand[2 * kCap];
+  __shared__ uint32_t ties[kCap];
+  __shared__ int sel[kTopkMax];
+  __shared__ int scan[kFinalThreads / 64];
+  static_assert(kCap >= kFinalBins, "the histogram fits the tie list");
+  __shared__ int res[2];
+  __shared__ int nsel, nties;
+  __shared__ uint32_t cmax;
+  static_assert(2 * kCap == kBitmapMaxN / 32, "the output bitmap reuses the candidate buffer");
+  uint32_t* skey = cand;
+  int* spos = (int*)(cand + kCap);
+  uint32_t* bitmap = cand;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t n = row_len(pos, r, stride);
+  int32_t* out = idx + (int64_t)r * k;
+  if (n <= k) {                       // short context or padded row: every visible position
+    for (int j = tid; j < k; j += kFinalThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  const int c = ws.fcnt[r];
+  if (c < k || c > kCap) {            // the filter kept too few (or too many): exact fallback
+    if (tid == 0) ws.flag[r] = 1;
+    return;
+  }
+  if (tid == 0) { nsel = 0; nties = 0; cmax = 0u; }
+  __syncthreads();
+  uint32_t mx = 0u;
+  {
+    constexpr int kPer = kCap / kFinalThreads;   // every load in flight before the first use
+    uint32_t key[kPer];
+    int p[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      const int i = tid + j * kFinalThreads;
+      key[j] = i < c ? ws.ckey[(int64_t)r * kCap + i] : 0u;
+      p[j] = i < c ? ws.cpos[(int64_t)r * kCap + i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      const int i = tid + j * kFinalThreads;
+      if (i < c) { skey[i] = key[j]; spos[i] = p[j]; mx = max(mx, key[j]); }
+    }
+  }
+  atomicMax(&cmax, mx);
+  __syncthreads();
+  // every candidate lies in [filter threshold, cmax]: the rounds start at that span's width
+  const uint32_t base = ws.thr[r];
+  const uint32_t span = cmax - base;
+  const int width = span == 0u ? 0 : 32 - __clz(span);
+  int need = 0;
+  const uint32_t thr = kth_largest(skey, c, k, base, width, (int*)ties, scan, res, need);   // exact key of the k-th largest
+  for (int i = tid; i < c; i += kFinalThreads) {
+    if (skey[i] > thr) push(sel, &nsel, spos[i]);
+    else if (skey[i] == thr) ties[atomicAdd(&nties, 1)] = ~(uint32_t)spos[i];   // larger = lower position
+  }
+  __syncthreads();
+  const int nt = nties;               // >= need >= 1
+  uint32_t tcut = 0;                  // every tie at or above it is kept
+  if (nt > need) {
+    int one = 0;
+    tcut = kth_largest(ties, nt, need, 0u, 32, (int*)cand, scan, res, one);   // positions are unique: exactly need
+  }
+  for (int i = tid; i < nt; i += kFinalThreads)
+    if (ties[i] >= tcut) push(sel, &nsel, (int)~ties[i]);
+  __syncthreads();
+  write_ascending(sel, min(nsel, k), n, k, out, bitmap, scan);
 }
 
 }  // namespace
@@ -438,21 +668,18 @@ hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s) {
   return hipGetLastError();
 }
 
-uint32_t* topk_range_ptr(void* ws, int32_t R, int32_t k) { return carve(ws, R, k).range; }
-
-// Passes 2-4 (the row ranges are already in the workspace).
-hipError_t launch_topk_from_range(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
-                                  void* ws, hipStream_t s) {
+// Passes 2-4 (the row ranges are already in the workspace); gate: only flagged rows.
+static hipError_t launch_radix_passes(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
+                                      Ws w, const int* gate, hipStream_t s) {
   const int R = rows.n;
-  Ws w = carve(ws, R, k);
   const int64_t visible = (int64_t)rows.max_pos + 1;
   if (visible > k) {
     const unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
-    hipLaunchKernelGGL(k_hist, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w);
-    hipLaunchKernelGGL(k_thresh, dim3(R), dim3(256), 0, s, rows.pos, stride, k, w);
-    hipLaunchKernelGGL(k_select, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w);
+    hipLaunchKernelGGL(k_hist, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
+    hipLaunchKernelGGL(k_thresh, dim3(R), dim3(256), 0, s, rows.pos, stride, k, w, gate);
+    hipLaunchKernelGGL(k_select, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
   }
-  hipLaunchKernelGGL(k_final, dim3(R), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k, idx, w);
+  hipLaunchKernelGGL(k_final, dim3(R), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k, idx, w, gate);
   return hipGetLastError();
 }
 
@@ -462,13 +689,64 @@ hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32
   if (R <= 0) return hipSuccess;
   hipError_t e = launch_topk_init(R, k, ws, s);
   if (e != hipSuccess) return e;
+  Ws w = carve(ws, R, k);
   const int64_t visible = (int64_t)rows.max_pos + 1;
   if (visible > k) {
-    Ws w = carve(ws, R, k);
     const unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
-    hipLaunchKernelGGL(k_range, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w);
+    hipLaunchKernelGGL(k_range, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, nullptr);
   }
-  return launch_topk_from_range(logits, stride, rows, k, idx, ws, s);
+  return launch_radix_passes(logits, stride, rows, k, idx, w, nullptr, s);
+}
+
+LogitsMode topk_sample_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto) {
+  LogitsMode m;
+  m.kind = kLogitsSample;
+  m.range = carve(ws, R, k).range;
+  m.skip_upto = skip_upto;
+  m.page_step = kTopkSampleStep;
+  return m;
+}
+
+hipError_t launch_topk_threshold(const float* logits, int64_t stride, RowsView rows, int32_t k, void* ws,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(k_filt_thresh, dim3(rows.n), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k,
+                     carve(ws, rows.n, k));
+  return hipGetLastError();
+}
+
+LogitsMode topk_filter_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto) {
+  const Ws w = carve(ws, R, k);
+  LogitsMode m;
+  m.kind = kLogitsFilter;
+  m.skip_upto = skip_upto;
+  m.thr = w.thr;
+  m.fcnt = w.fcnt;
+  m.fkey = w.ckey;
+  m.fpos = w.cpos;
+  m.fcap = kCap;
+  return m;
+}
+
+hipError_t launch_topk_filtered_final(RowsView rows, int64_t stride, int32_t k, int32_t* idx, void* ws,
+                                      hipStream_t s) {
+  hipLaunchKernelGGL(k_filt_final, dim3(rows.n), dim3(kFinalThreads), 0, s, rows.pos, stride, k, idx,
+                     carve(ws, rows.n, k));
+  return hipGetLastError();
+}
+
+LogitsMode topk_fallback_mode(void* ws, int32_t R, int32_t k) {
+  const Ws w = carve(ws, R, k);
+  LogitsMode m;
+  m.kind = kLogitsFallback;
+  m.flag = w.flag;
+  m.range = w.range;      // the full scores widen the sample's range to the row's
+  return m;
+}
+
+hipError_t launch_topk_fallback(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
+                                void* ws, hipStream_t s) {
+  const Ws w = carve(ws, rows.n, k);
+  return launch_radix_passes(logits, stride, rows, k, idx, w, w.flag, s);
 }
 
 DSA_DEFINE_ERROR_ACCESSOR(take_device_errors_topk)

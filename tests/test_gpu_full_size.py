@@ -47,6 +47,9 @@ def check_sampled_rows(w, L, rows, overrides=None, min_same_frac=0.9):
     """Every sampled row: q quantisation bit-exact, logits within tolerance, top-k set equal
     (near-ties excepted), and each layer's attention output against the oracle."""
     rows = np.asarray(sorted(set(int(r) for r in rows)))
+    # the fused indexer + top-k keeps the logits buffer as scratch: score separately to check
+    dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
+    torch.cuda.synchronize()
     n_same = 0
     for b in np.unique(w.row_req[rows]):
         rs = rows[w.row_req[rows] == b]
@@ -154,8 +157,6 @@ def test_short_context_rows_skip_scoring():
             p = int(w.row_pos[r])
             assert np.array_equal(gidx[r, :p + 1], np.arange(p + 1)) and np.all(gidx[r, p + 1:] == -1)
             assert np.all(np.isnan(glg[r])), f"row {r} (pos {p}) was scored"
-        else:
-            assert_logits_close(glg[r:r + 1], lg[r:r + 1])
     topk_sets_match(gidx, ridx, lg, kth)                 # differences only at near-ties
     same = np.array([set(gidx[r]) == set(ridx[r]) for r in range(w.R)])
     assert same[short].all() and same.sum() >= w.R - 1
@@ -186,8 +187,10 @@ def test_short_group_of_six_rows():
     ridx, kth = orc.topk(lg, w.row_pos, 2048)
     gidx, glg = host(L.idx), host(L.logits)
     assert np.all(np.isnan(glg[:6]))                       # request 0: every row short -> not scored
-    assert_logits_close(glg[6:], lg[6:])                   # request 1 mixes short and long rows
     topk_sets_match(gidx, ridx, lg, kth)                   # differences only at near-ties
+    dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
+    torch.cuda.synchronize()
+    assert_logits_close(host(L.logits), lg)               # the plain call scores every row
     assert np.array_equal(gidx[:6], ridx[:6])
 
 
@@ -201,3 +204,68 @@ def test_context_sweep_single_request(ctx):
     check_sampled_rows(w, L, [0], min_same_frac=1.0)
     dsa.dsa_check_device_errors()
     _release(L)
+
+
+SAMPLE_STEP = 16    # the fused path scores one page in SAMPLE_STEP to set its filter threshold
+
+
+def _fused_topk_case(w, overrides, expect_fallback):
+    L = DeviceLayer(w, k_overrides=overrides)
+    L.logits.fill_(float("nan"))
+    dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
+    L.indexer_topk(0)
+    torch.cuda.synchronize()
+    gidx, glg = host(L.idx), host(L.logits)
+    # which path the row took: the exact fallback scores every page, the filtered path
+    # only the sampled pages and writes no other score
+    n = int(w.row_pos[0]) + 1
+    unsampled = np.array([s for s in range(n) if (s // 64) % SAMPLE_STEP != 0])
+    assert np.isfinite(glg[0, unsampled]).all() == expect_fallback
+    cache = oracle_index_cache(w, overrides)
+    q, wt, _ = queries(w, [])
+    q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+    lg = orc.indexer_logits(q8.reshape(-1, 32, 128), qs.reshape(-1, 32), wt, w.row_req, w.row_pos, w.page_table, cache)
+    ridx, kth = orc.topk(lg, w.row_pos, 2048)
+    topk_sets_match(gidx, ridx, lg, kth)
+    # the unfused path (plain scores + radix top-k) selects the same positions
+    dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
+    dsa.dsa_topk(L.logits, L.rows, 2048, L.idx, L.ws_topk)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(L.idx), gidx)
+    return gidx, ridx
+
+
+def _equal_score_key():
+    """A raw key whose LayerNorm output is zero on the rotated dims 0..63, so every position
+    gets the same stored key and every score of a row is the same number."""
+    d = np.arange(1, 33) / 128.0                                  # 1 +- d exact in bf16
+    v = np.concatenate([np.ones(64), 1.0 + d, 1.0 - d])          # mean exactly 1
+    return orc.bf16_from_double(v)
+
+
+def test_fused_topk_fallback_when_filter_keeps_too_few():
+    _announce("fused top-k: filter keeps fewer than k -> exact fallback")
+    n = 30000
+    w = gi.make_decode("fb_few", gi.SEED_BASE + 70, [n])
+    rng = np.random.default_rng(70)
+    sampled = np.array([s for s in range(n - 1) if (s // 64) % SAMPLE_STEP == 0])
+    others = np.array([s for s in range(n - 1) if (s // 64) % SAMPLE_STEP != 0])
+    w.needles = np.sort(np.concatenate([rng.choice(sampled, 600, replace=False), rng.choice(others, 400, replace=False)]))
+    gidx, ridx = _fused_topk_case(w, needle_overrides(w), expect_fallback=True)
+    assert set(w.needles.tolist()) <= set(gidx[0].tolist())
+
+
+def test_fused_topk_fallback_when_candidates_overflow():
+    _announce("fused top-k: all scores equal, 9000 candidates -> exact fallback")
+    w = gi.make_decode("fb_overflow", gi.SEED_BASE + 71, [9000])
+    key = _equal_score_key()
+    gidx, ridx = _fused_topk_case(w, {p: key for p in range(9000)}, expect_fallback=True)
+    assert np.array_equal(gidx[0], np.arange(2048))       # exact ties keep the lowest positions
+
+
+def test_fused_topk_ties_inside_candidate_list():
+    _announce("fused top-k: all scores equal, 3000 candidates -> exact within the list")
+    w = gi.make_decode("fb_ties", gi.SEED_BASE + 72, [3000])
+    key = _equal_score_key()
+    gidx, ridx = _fused_topk_case(w, {p: key for p in range(3000)}, expect_fallback=False)
+    assert np.array_equal(gidx[0], np.arange(2048))

@@ -215,6 +215,9 @@ def test_layer_end_to_end(cid):
     assert np.array_equal(host(L.q8).reshape(-1, 128), q8) and np.array_equal(host(L.qs).reshape(-1), qs)
     q8, qs = q8.reshape(w.R, 32, 128), qs.reshape(w.R, 32)
     lg = orc.indexer_logits(q8, qs, wt, w.row_req, w.row_pos, w.page_table, cache)
+    # the fused indexer + top-k keeps its logits buffer as scratch: score separately to check them
+    dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
+    torch.cuda.synchronize()
     assert_logits_close(host(L.logits), lg)
     ridx, kth = orc.topk(lg, w.row_pos, 2048)
     gidx = host(L.idx)
@@ -257,10 +260,10 @@ def test_determinism_and_page_permutation():
     w = gi.config(1, "small")
     A = DeviceLayer(w)
     A.group_step()
-    first = (host(A.logits).copy(), host(A.idx).copy(), host(A.out[0]).copy())
+    first = (host(A.idx).copy(), host(A.out[0]).copy())
     A.group_step()
-    assert np.array_equal(host(A.logits), first[0]) and np.array_equal(host(A.idx), first[1])
-    assert np.array_equal(host(A.out[0]), first[2])
+    assert np.array_equal(host(A.idx), first[0])
+    assert np.array_equal(host(A.out[0]), first[1])
     # same logical content under a different page permutation
     w2 = gi.config(1, "small")
     perm = np.random.default_rng(1).permutation(w2.num_pages).astype(np.int32)
@@ -268,8 +271,8 @@ def test_determinism_and_page_permutation():
     B = DeviceLayer(w2)
     B.group_step()
     torch.cuda.synchronize()
-    assert np.array_equal(host(B.logits), first[0]) and np.array_equal(host(B.idx), first[1])
-    assert np.array_equal(host(B.out[0]), first[2])
+    assert np.array_equal(host(B.idx), first[0])
+    assert np.array_equal(host(B.out[0]), first[1])
 
 
 def test_bad_page_id_is_flagged_not_dereferenced():
@@ -296,9 +299,8 @@ def test_fused_indexer_topk_equals_separate_calls(cid):
     dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
     L.indexer_topk(0)
     torch.cuda.synchronize()
-    fused_logits, fused_idx = host(L.logits).copy(), host(L.idx).copy()
+    fused_idx = host(L.idx).copy()
     dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
     dsa.dsa_topk(L.logits, L.rows, 2048, L.idx, L.ws_topk)
     torch.cuda.synchronize()
-    assert np.array_equal(host(L.logits), fused_logits)
-    assert np.array_equal(host(L.idx), fused_idx)
+    assert np.array_equal(host(L.idx), fused_idx)      # same scores, same exact selection
