@@ -68,13 +68,19 @@ def measured_traffic(kernel):
     return int(round((k["fetch_kib"] * t["fetch_factor"] + k["write_kib"] * t["write_factor"]) * 1024))
 
 
+_IDX_SRC = ["sparse_attention_store_amd/csrc/k_indexer.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp",
+            "sparse_attention_store_amd/csrc/dsa_internal.h"]
+_MLA_SRC = ["sparse_attention_store_amd/csrc/k_mla.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"]
+_TOPK_SRC = ["sparse_attention_store_amd/csrc/k_topk.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp",
+             "sparse_attention_store_amd/csrc/dsa_internal.h"]
+# kernel name as rocprofv3 prints it, up to the opening parenthesis -> the sources it is built from
 KERNEL_SOURCES = {
-    "k_logits_decode": ["sparse_attention_store_amd/csrc/k_indexer.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
-    "k_sparse_mla": ["sparse_attention_store_amd/csrc/k_mla.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
-    "k_mla_combine": ["sparse_attention_store_amd/csrc/k_mla.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
-    "k_hist": ["sparse_attention_store_amd/csrc/k_topk.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
-    "k_select": ["sparse_attention_store_amd/csrc/k_topk.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
-    "k_final": ["sparse_attention_store_amd/csrc/k_topk.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"],
+    "k_logits_decode<6, 0>": _IDX_SRC,    # dsa_indexer_logits: every score written
+    "k_logits_decode<6, 1>": _IDX_SRC,    # dsa_indexer_topk: sampled pages
+    "k_logits_decode<6, 2>": _IDX_SRC,    # dsa_indexer_topk: filter pass (candidates only)
+    "k_sparse_mla_stream": _MLA_SRC,      # sparse MLA, 256+ rows
+    "k_filt_thresh": _TOPK_SRC,
+    "k_filt_final": _TOPK_SRC,
 }
 
 
@@ -95,11 +101,12 @@ def write_traffic(fetch_csv, write_csv, command):
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
 
     def pick(vals, key):
-        hits = [v for name, vs in vals.items() if key in name for v in vs]
+        hits = [v for name, vs in vals.items() if key + "(" in name for v in vs]
         return hits
 
     gib_kib = float(1 << 20)
-    copy_f, copy_w = max(pick(fetch, "copyBuffer")), max(pick(write, "copyBuffer"))
+    copy_f = max(v for name, vs in fetch.items() if "copyBuffer" in name for v in vs)
+    copy_w = max(v for name, vs in write.items() if "copyBuffer" in name for v in vs)
     out = {"about": "HBM traffic per dispatch of the c2 verify workload (64 x 6 rows at 128K), from rocprofv3 "
                     "--pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches); factors make a "
                     "1 GiB device copy read and write 1 GiB",
@@ -261,12 +268,11 @@ def main():
     mla_total = sum(per[f"mla{l}"] for l in D.layers)
     dominant = "logits"      # the metric's named kernel: index-K cache streaming
     roof_idx = {"kernel": "k_logits_decode (dsa_indexer_logits)", "bound": "hbm", "achieved": round(idx_gbps, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("k_logits_decode"),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("k_logits_decode<6, 0>"),
                 "algorithmic_bytes_per_launch": ib, "avg_launch_us": round(per["logits"], 2)}
-    roof_mla = {"kernel": "k_sparse_mla (dsa_sparse_mla_decode)", "bound": "hbm", "achieved": round(mla_gbps, 1),
+    roof_mla = {"kernel": "k_sparse_mla_stream (dsa_sparse_mla_decode)", "bound": "hbm", "achieved": round(mla_gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(mla_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic("k_sparse_mla") and
-                (measured_traffic("k_sparse_mla") + (measured_traffic("k_mla_combine") or 0)),
+                "traffic": measured_traffic("k_sparse_mla_stream"),
                 "algorithmic_bytes_per_launch": mla_b, "avg_launch_us": round(per["mla0"], 2),
                 "mfma_tflops": round(mla_tflops, 1), "mfma_frac_bf16": round(mla_tflops / BF16_PEAK_TFLOPS, 4)}
     out = {

@@ -31,6 +31,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define DSA_LDS __attribute__((address_space(3)))
+#define DSA_GLOBAL __attribute__((address_space(1)))
 
 // Device error flag raised by in-kernel range checks (page ids, indices); one per
 // translation unit, read and cleared by that unit's take_device_errors_*().

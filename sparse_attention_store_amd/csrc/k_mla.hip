@@ -49,7 +49,9 @@ constexpr int kBufs = kDepth + 2;                        // + the QK tile + the 
 static_assert(kDepth >= 1 && kDepth <= 3, "the tile wait handles up to two tiles ahead");
 static_assert(kDmaWaves * kDmaPerWave >= kTileSlots, "copy slots must cover a tile");
 constexpr int kMaxSplitKeys = 2048;
-constexpr int kPRow = kTile + 4;                          // P row pitch (fp32) in LDS
+static_assert(kDepth * kTile <= kMaxSplitKeys, "the first tiles' lookups stay inside phys");
+static_assert(kMaxSplitKeys % kThreads == 0, "whole index loads per thread");
+constexpr int kPRowB = kTile + 8;   // P row pitch in bf16 (80 B): 16-B reads of 8 head rows hit distinct banks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;      // log2 units the running max may lag behind
 
@@ -79,33 +81,32 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Issues the global->LDS copies of one tile: LDS chunk c of the tile holds 16 B of key
-// c/41, chunk c%41 of its 656-B record (records land back to back).  Each QK wave issues
-// exactly kDmaPerWave copies so that per-tile vmcnt accounting is uniform; lanes past the
-// tile or of invalid keys copy from the first record of the pool into the buffer (the
-// records of invalid keys are zeroed before use).  The record lookups are read
-// before any copy is issued, so the wave waits for LDS once.
-__device__ __forceinline__ void issue_tile(const uint8_t* cache, const DSA_LDS int* phys, int tile_base,
-                                           DSA_LDS uint8_t* buf, int wave, int lane) {
-  int ph[kDmaPerWave], chunk[kDmaPerWave];
-  bool in_tile[kDmaPerWave];
+// Global->LDS copies of one tile: LDS chunk c of the tile holds 16 B of key c/41, chunk
+// c%41 of its 656-B record (records land back to back).  Each QK wave issues exactly
+// kDmaPerWave copies so that per-tile vmcnt accounting is uniform; lanes past the tile or of
+// invalid keys copy from the first record of the pool into the buffer (the records of
+// invalid keys are zeroed before use).  The record lookups (read_tile_phys) are done a tile
+// ahead of the copies (issue_tile_ph), so the copies never wait for LDS.
+__device__ __forceinline__ void read_tile_phys(const DSA_LDS int* __restrict__ phys, int tile_base, int wave, int lane,
+                                               int (&ph)[kDmaPerWave]) {
 #pragma unroll
   for (int u = 0; u < kDmaPerWave; u++) {
     const int c = (wave * kDmaPerWave + u) * 64 + lane;
-    in_tile[u] = c < kTileChunks;
-    const int key = min(c / kChunks, kTile - 1);
-    chunk[u] = c - key * kChunks;
-    ph[u] = phys[tile_base + key];           // tile_base + key < ntiles * kTile <= kMaxSplitKeys
+    ph[u] = phys[tile_base + min(c / kChunks, kTile - 1)];   // < ntiles * kTile <= kMaxSplitKeys
   }
+}
+__device__ __forceinline__ void issue_tile_ph(const uint8_t* cache, const int (&ph)[kDmaPerWave], DSA_LDS uint8_t* buf,
+                                              int wave, int lane) {
 #pragma unroll
   for (int u = 0; u < kDmaPerWave; u++) {
-    const bool ok = in_tile[u] && ph[u] >= 0;
-    const uint8_t* src = ok ? cache + (int64_t)ph[u] * kRecBytes + 16 * chunk[u] : cache;
+    const int c = (wave * kDmaPerWave + u) * 64 + lane;
+    const int key = min(c / kChunks, kTile - 1);
+    const bool ok = c < kTileChunks && ph[u] >= 0;
+    const uint8_t* src = ok ? cache + (int64_t)ph[u] * kRecBytes + 16 * (c - key * kChunks) : cache;
     const int slot = min(wave * kDmaPerWave + u, kTileSlots);   // surplus copies share the sink
     __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(buf + slot * 1024), 16, 0, 0);
   }
 }
-
 // Zeroes the records of the invalid keys of a tile (all threads of the work-group).
 __device__ __forceinline__ void zero_bad_records(DSA_LDS uint8_t* __restrict__ T, const DSA_LDS int* phys, int tile_base,
                                                  int tid) {
@@ -148,11 +149,14 @@ struct QkOps {
 __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int* __restrict__ phys, int it, int ntiles,
                                         bool bad,
                                         DSA_LDS uint8_t* __restrict__ dst, DSA_LDS uint8_t* __restrict__ T,
-                                        DSA_LDS float* __restrict__ plp, DSA_LDS float* __restrict__ alpha_p,
+                                        DSA_LDS uint16_t* __restrict__ plp, DSA_LDS float* __restrict__ alpha_p,
                                         DSA_LDS int* __restrict__ resc_p, const QkOps& Q, float sm_log2, float& m_run, float& l_part, int qw, int wave,
-                                        int lane, int tid) {
+                                        int lane, int tid, int (&phn)[kDmaPerWave]) {
   const int g = lane >> 4, c16 = lane & 15;
-  if (it + kDepth < ntiles) issue_tile(cache, phys, (it + kDepth) * kTile, dst, wave, lane);
+  if (it + kDepth < ntiles) {
+    issue_tile_ph(cache, phn, dst, wave, lane);                  // record ids read a tile ago
+    if (it + kDepth + 1 < ntiles) read_tile_phys(phys, (it + kDepth + 1) * kTile, wave, lane, phn);
+  }
   if (bad) {
     zero_bad_records(T, phys, it * kTile, tid);
     lds_barrier();
@@ -236,17 +240,21 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
   if (g == 0) alpha_p[hh] = alpha;
   const bool any_resc = __any(alpha != 1.f);     // wave-uniform: tells the PV waves to rescale
   if (lane == 0) resc_p[qw] = any_resc;
-  // P (fp32, unscaled): the PV waves apply each key's value-block scale
+  // P as bf16, unscaled: the PV waves multiply in each key's value-block scale (a power of
+  // two, so the product is the bf16 rounding of P times the scale)
 #pragma unroll
   for (int mt = 0; mt < 2; mt++)
-    *reinterpret_cast<DSA_LDS f32x4*>(plp + hh * kPRow + 16 * mt + 4 * g) =
-        f32x4{p[mt][0], p[mt][1], p[mt][2], p[mt][3]};
+    *reinterpret_cast<DSA_LDS i32x2*>(plp + hh * kPRowB + 16 * mt + 4 * g) =
+        i32x2{pack2_bf16(p[mt][0], p[mt][1]), pack2_bf16(p[mt][2], p[mt][3])};
 }
 
 // Partial results cross work-groups (and XCDs, each with its own L2): they are written and
 // read as relaxed agent-scope atomics, which the hardware keeps coherent across the L2s
 // without a device-wide cache write-back.
 __device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(DSA_GLOBAL float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float load_coherent(const float* p) {
@@ -262,14 +270,29 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 // The result goes to the bf16 output (and lse) when part_o is null; otherwise it is written
 // as a partial: un-normalised O [64][512], and per head the running max m (log2 units) and
 // the sum l, to part_o / part_ml.  All threads of the work-group call it together.
-__device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q, const int32_t* __restrict__ req,
-                                            const int32_t* __restrict__ pos, const DevPages& pg,
-                                            const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx,
+__device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, const int32_t* __restrict__ req_in,
+                                            const int32_t* __restrict__ pos_in, const DevPages& pg,
+                                            const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx_in,
                                             int32_t k, float sm_log2, int r, int j0, int nkeys,
-                                            uint16_t* __restrict__ out, float* __restrict__ lse,
-                                            float* __restrict__ part_o, float* __restrict__ part_ml) {
+                                            uint16_t* __restrict__ out_in, float* __restrict__ lse_in,
+                                            float* __restrict__ part_o_in, float* __restrict__ part_ml_in) {
+  // The stream kernel runs this body out of line, where pointer arguments arrive as generic
+  // (flat) pointers; flat accesses count against the LDS counter as well, so every wait for
+  // them would also wait for LDS.  Global data is therefore reached through global-space
+  // pointers, and the page table's fields are read once.
+  const DSA_GLOBAL uint16_t* __restrict__ q = (const DSA_GLOBAL uint16_t*)q_in;
+  const DSA_GLOBAL int32_t* __restrict__ req = (const DSA_GLOBAL int32_t*)req_in;
+  const DSA_GLOBAL int32_t* __restrict__ pos = (const DSA_GLOBAL int32_t*)pos_in;
+  const DSA_GLOBAL int32_t* __restrict__ idx = (const DSA_GLOBAL int32_t*)idx_in;
+  DSA_GLOBAL uint16_t* __restrict__ out = (DSA_GLOBAL uint16_t*)out_in;
+  DSA_GLOBAL float* __restrict__ lse = (DSA_GLOBAL float*)lse_in;
+  DSA_GLOBAL float* __restrict__ part_o = (DSA_GLOBAL float*)part_o_in;
+  DSA_GLOBAL float* __restrict__ part_ml = (DSA_GLOBAL float*)part_ml_in;
+  const DSA_GLOBAL int32_t* __restrict__ pt = (const DSA_GLOBAL int32_t*)pg.pt;
+  const int64_t pt_stride = pg.pt_stride, num_pages = pg.num_pages;
+  const int32_t num_reqs = pg.num_reqs;
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[kBufs][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float pl[2][kHeads * kPRow];          // P of a tile, fp32
+  __shared__ __attribute__((aligned(16))) uint16_t pl[2][kHeads * kPRowB];     // P of a tile, bf16
   __shared__ __attribute__((aligned(16))) float alpha_s[2][kHeads];
   __shared__ __attribute__((aligned(16))) int resc_s[2][4];     // per QK wave: some alpha != 1
   __shared__ float m_s[kHeads], l_s[kHeads];
@@ -291,35 +314,79 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q, cons
   i32x4 qraw[4][4];
   bf16x8 qr_raw[2];
   if (is_qk) {
-    const uint16_t* qh = q + ((int64_t)r * kHeads + 16 * qw + c16) * kLat;
+    const DSA_GLOBAL uint16_t* qh = q + ((int64_t)r * kHeads + 16 * qw + c16) * kLat;
 #pragma unroll
     for (int b = 0; b < 4; b++)
 #pragma unroll
       for (int u = 0; u < 4; u++)
-        qraw[b][u] = *reinterpret_cast<const i32x4*>(qh + 128 * b + 64 * (u >> 1) + 16 * g + 8 * (u & 1));
+        qraw[b][u] = *reinterpret_cast<const DSA_GLOBAL i32x4*>(qh + 128 * b + 64 * (u >> 1) + 16 * g + 8 * (u & 1));
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++) qr_raw[ks] = *reinterpret_cast<const bf16x8*>(qh + kVal + 32 * ks + 8 * g);
+    for (int ks = 0; ks < 2; ks++) qr_raw[ks] = *reinterpret_cast<const DSA_GLOBAL bf16x8*>(qh + kVal + 32 * ks + 8 * g);
   }
 
-  // resolve record addresses (physical token index) of this split's keys
+  // resolve record addresses (physical token index) of this split's keys: every thread's
+  // index loads, then every page-table load, so the segment waits two memory round trips
   for (int t = tid; t < ntiles; t += kThreads) tile_bad[t] = 0;
   __syncthreads();
-  for (int j = tid; j < ntiles * kTile; j += kThreads) {
-    int ph = -1;
-    if (j < nkeys) {
-      const int s = idx[(int64_t)r * k + j0 + j];
-      if (p >= 0 && s >= 0 && s <= p) {
-        const int64_t page = page_of(pg, rq, s);
-        if (page >= 0) ph = (int)(page * kPage + (s & 63));
+  {
+    constexpr int kPer = kMaxSplitKeys / kThreads;
+    int sv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      const int j = tid + u * kThreads;
+      sv[u] = j < nkeys ? idx[(int64_t)r * k + j0 + j] : -1;
+    }
+    // unconditional page-table reads (slot 0 stands in for keys that need none), range
+    // checks after all of them, so the reads stay batched
+    const bool req_ok = rq >= 0 && rq < num_reqs;
+    const bool table = num_reqs > 0 && pt_stride > 0;            // uniform
+    int64_t pv[kPer];
+    bool want[kPer], col_ok[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      want[u] = p >= 0 && sv[u] >= 0 && sv[u] <= p;
+      col_ok[u] = req_ok && (sv[u] >> 6) < pt_stride;
+      pv[u] = -1;
+    }
+    if (table) {
+      int64_t raw[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; u++)
+        raw[u] = pt[want[u] && col_ok[u] ? (int64_t)rq * pt_stride + (sv[u] >> 6) : 0];
+#pragma unroll
+      for (int u = 0; u < kPer; u++) pv[u] = want[u] && col_ok[u] ? raw[u] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      if (want[u] && !col_ok[u]) raise_device_error(kErrRequest);
+      if (want[u] && col_ok[u] && (pv[u] < 0 || pv[u] >= num_pages)) { raise_device_error(kErrPageId); pv[u] = -1; }
+      const int j = tid + u * kThreads;
+      if (j < ntiles * kTile) {
+        const int ph = want[u] && pv[u] >= 0 ? (int)(pv[u] * kPage + (sv[u] & 63)) : -1;
+        phys[j] = ph;
+        if (ph < 0) tile_bad[j / kTile] = 1;
       }
     }
-    phys[j] = ph;
-    if (ph < 0) tile_bad[j / kTile] = 1;
   }
 
   __syncthreads();                              // phys ready
-  if (is_qk)
-    for (int t = 0; t < kDepth && t < ntiles; t++) issue_tile(cache, phl, t * kTile, tl + t * kTileBytes, wave, lane);
+  int phn[kDmaPerWave];                          // QK waves: record ids of the next tile to copy
+  if (is_qk) {
+    // every lookup before the first copy, so no LDS read waits for the copies in flight
+    // The first kDepth tiles are always copied (tiles past the segment copy the pool's first
+    // record into their unused buffer), so the number of copies after the q loads is fixed
+    // and the q operands wait for the q loads only.
+    int ph0[kDepth][kDmaPerWave];
+#pragma unroll
+    for (int t = 0; t < kDepth; t++) {
+      read_tile_phys(phl, t * kTile, wave, lane, ph0[t]);      // t * kTile + 31 < kMaxSplitKeys
+#pragma unroll
+      for (int u = 0; u < kDmaPerWave; u++) ph0[t][u] = t < ntiles ? ph0[t][u] : -1;
+    }
+    if (kDepth < ntiles) read_tile_phys(phl, kDepth * kTile, wave, lane, phn);
+#pragma unroll
+    for (int t = 0; t < kDepth; t++) issue_tile_ph(cache, ph0[t], tl + t * kTileBytes, wave, lane);
+  }
 
   // Start of every iteration (both roles, same barriers in the same order): wait for this
   // wave's copies of tile `it`, then a barrier so that all of tile `it` is in LDS and every
@@ -393,9 +460,9 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q, cons
       wait_tile(it);
       const int par = it & 1;
       qk_step(cache, phl, it, ntiles, tile_bad[it] != 0, tl + ((it + kDepth) % kBufs) * kTileBytes,
-              tl + (it % kBufs) * kTileBytes, (DSA_LDS float*)pl[par], (DSA_LDS float*)alpha_s[par],
+              tl + (it % kBufs) * kTileBytes, (DSA_LDS uint16_t*)pl[par], (DSA_LDS float*)alpha_s[par],
               (DSA_LDS int*)resc_s[par], Q, sm_log2,
-              m_run, l_part, qw, wave, lane, tid);
+              m_run, l_part, qw, wave, lane, tid, phn);
     }
     wait_tile(ntiles);                          // the PV waves' last step
     const float l_tot = rows_sum(l_part);
@@ -455,12 +522,16 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q, cons
       bf16x8 pa[4];
 #pragma unroll
       for (int ht = 0; ht < 4; ht++) {
-        const float* prow = &pl[par][(16 * ht + c16) * kPRow + 8 * g];
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
-        const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
-        const int w0 = pack2_bf16(p0[0] * ks[0][0], p0[1] * ks[0][1]), w1 = pack2_bf16(p0[2] * ks[0][2], p0[3] * ks[0][3]);
-        const int w2 = pack2_bf16(p1[0] * ks[1][0], p1[1] * ks[1][1]), w3 = pack2_bf16(p1[2] * ks[1][2], p1[3] * ks[1][3]);
-        pa[ht] = __builtin_bit_cast(bf16x8, i32x4{w0, w1, w2, w3});
+        const i32x4 pw = *reinterpret_cast<const DSA_LDS i32x4*>((const DSA_LDS uint16_t*)pl[par] +
+                                                                 (16 * ht + c16) * kPRowB + 8 * g);
+        int w[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {            // keys 8g + 2j, 8g + 2j + 1
+          const uint32_t x = (uint32_t)pw[j];
+          w[j] = pack2_bf16(__uint_as_float(x << 16) * ks[j >> 1][2 * (j & 1)],
+                            __uint_as_float(x & 0xFFFF0000u) * ks[j >> 1][2 * (j & 1) + 1]);
+        }
+        pa[ht] = __builtin_bit_cast(bf16x8, i32x4{w[0], w[1], w[2], w[3]});
       }
       // tr8: lane i of a 16-lane group points at key 8g + i/2, dims +8*(i%2); gets 8 keys of dim c16
 #pragma unroll
@@ -482,7 +553,7 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q, cons
           const int h = 16 * ht + 4 * g + i;
           const float l = l_s[h];
           const float inv = l > 0.f ? 1.f / l : 0.f;
-          uint16_t* orow = out + ((int64_t)r * kHeads + h) * kVal + 128 * qw + c16;
+          DSA_GLOBAL uint16_t* orow = out + ((int64_t)r * kHeads + h) * kVal + 128 * qw + c16;
 #pragma unroll
           for (int dt = 0; dt < 8; dt++) orow[16 * dt] = f32_to_bf16_bits(O[ht][dt][i] * inv);
         }
