@@ -28,6 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "liboracle.so")
 
 IDX_PAGE_BYTES = 8448
+IDX_MXFP4_PAGE_BYTES = 64 * 68
 LAT_PAGE_BYTES = 64 * 656
 
 
@@ -62,6 +63,11 @@ def lib():
             "orc_topk": [p, i64, p, i64, i32, p, p],
             "orc_sparse_mla": [p, p, p, i64, p, i64, p, p, i32, d, p, p],
             "orc_layer_is_shared": [ctypes.c_char_p, i32, i32, ctypes.c_char_p, i32, i32, i32, i32],
+            "orc_fp4_encode_array": [p, i64, p, ctypes.c_int],
+            "orc_fp4_decode_array": [p, i64, p],
+            "orc_ue8m0_fp4_array": [p, i64, p],
+            "orc_index_k_store_mxfp4": [p, p, p, i64, p, i64, p, d, d],
+            "orc_indexer_logits_mxfp4": [p, p, p, p, p, i64, p, i64, p, p, i64],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -98,6 +104,28 @@ def ue8m0(amax) -> np.ndarray:
     a = _c(amax, np.float64)
     out = np.empty(a.shape, np.float64)
     lib().orc_ue8m0_array(a.ctypes.data, a.size, out.ctypes.data)
+    return out
+
+
+def fp4_decode(codes) -> np.ndarray:
+    """MXFP4 element codes (the low 4 bits of each byte) -> values."""
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().orc_fp4_decode_array(c.ctypes.data, c.size, out.ctypes.data)
+    return out
+
+
+def fp4_encode(x, brute: bool = False) -> np.ndarray:
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_fp4_encode_array(x.ctypes.data, x.size, out.ctypes.data, int(brute))
+    return out
+
+
+def ue8m0_fp4(amax) -> np.ndarray:
+    a = _c(amax, np.float64)
+    out = np.empty(a.shape, np.float64)
+    lib().orc_ue8m0_fp4_array(a.ctypes.data, a.size, out.ctypes.data)
     return out
 
 
@@ -145,6 +173,16 @@ def index_k_store(k_bf16, req, pos, page_table, cache, eps=1e-6, theta=10000.0, 
     return pre
 
 
+def index_k_store_mxfp4(k_bf16, req, pos, page_table, cache, eps=1e-6, theta=10000.0):
+    """Writes into ``cache`` (uint8 [pages, 4352], the MXFP4 index-K layout) in place."""
+    k = _c(k_bf16, np.uint16).reshape(-1, 128)
+    req, pos = _c(req, np.int32), _c(pos, np.int32)
+    pt = _c(page_table, np.int32)
+    assert cache.dtype == np.uint8 and cache.flags.c_contiguous and cache.shape[-1] == IDX_MXFP4_PAGE_BYTES
+    lib().orc_index_k_store_mxfp4(k.ctypes.data, req.ctypes.data, pos.ctypes.data, k.shape[0],
+                                  pt.ctypes.data, pt.shape[1], cache.ctypes.data, eps, theta)
+
+
 def latent_store(kv_bf16, req, pos, page_table, cache):
     kv = _c(kv_bf16, np.uint16).reshape(-1, 576)
     req, pos, pt = _c(req, np.int32), _c(pos, np.int32), _c(page_table, np.int32)
@@ -170,6 +208,20 @@ def indexer_logits(q8, q_scale, w, req, pos, page_table, cache, stride=None):
     lib().orc_indexer_logits(q8.ctypes.data, qs.ctypes.data, w.ctypes.data, req.ctypes.data,
                              pos.ctypes.data, R, pt.ctypes.data, pt.shape[1],
                              _c(cache, np.uint8).ctypes.data, out.ctypes.data, stride)
+    return out
+
+
+def indexer_logits_mxfp4(q8, q_scale, w, req, pos, page_table, cache, stride=None):
+    q8 = _c(q8, np.uint8).reshape(-1, 32, 128)
+    R = q8.shape[0]
+    qs, w = _c(q_scale, np.float32).reshape(R, 32), _c(w, np.float32).reshape(R, 32)
+    req, pos, pt = _c(req, np.int32), _c(pos, np.int32), _c(page_table, np.int32)
+    if stride is None:
+        stride = logits_stride(int(pos.max()))
+    out = np.empty((R, stride), np.float32)
+    lib().orc_indexer_logits_mxfp4(q8.ctypes.data, qs.ctypes.data, w.ctypes.data, req.ctypes.data,
+                                   pos.ctypes.data, R, pt.ctypes.data, pt.shape[1],
+                                   _c(cache, np.uint8).ctypes.data, out.ctypes.data, stride)
     return out
 
 

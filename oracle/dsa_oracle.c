@@ -393,6 +393,150 @@ int orc_layer_is_shared(const char* types, int32_t n_types, int32_t cli_factor,
     return v % topk_freq != 0;
 }
 
+/* ------------------------------------------------------------------ MXFP4 index-K
+ * The compressed indexer-cache format ([IDXC] §读取路径里的两条"非缓存"字节, the
+ * paragraph on vLLM's kv_cache_as_quant_view): head_dim/2 bytes of packed 4-bit codes
+ * plus one ue8m0 scale per block of 32 dims, 128/2 + 128/32 = 68 B per token.
+ * Readings (the page names the format only): the elements are OCP MX e2m1 (1 sign,
+ * 2 exponent bits with bias 1, 1 mantissa bit; largest finite 6), rounded to nearest
+ * with ties to the even code; each scale is the smallest power of two s with
+ * amax <= 6*s (the same rule as the FP8 path with 6 in place of 448, so nothing
+ * saturates), stored as its biased exponent byte (E8M0: 2^(byte-127)).  Two codes
+ * per byte, the lower dim in the low nibble.  Page: [64 x 64 B codes][64 x 4 scale
+ * bytes] = 4352 B (planar, like the FP8 page). */
+#define FP4_MAX        6.0
+#define MX4_TOKEN_B    64
+#define MX4_PAGE_B     (PAGE * (MX4_TOKEN_B + 4))
+#define MX4_SCALE_OFF  (PAGE * MX4_TOKEN_B)
+
+double orc_fp4_decode(uint8_t c) {
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* RNE over the magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}: within each binade the step is a
+ * quarter, half or one unit; the rounding is done on the mantissa, as for FP8. */
+uint8_t orc_fp4_encode(double x) {
+    uint8_t sign;
+    double a, r;
+    int e, m;
+    if (isnan(x)) return 0x7;              /* no NaN code: the largest magnitude */
+    sign = signbit(x) ? 0x8 : 0x0;
+    a = fabs(x);
+    if (a >= FP4_MAX) return sign | 0x7;
+    if (a < 1.0) {                         /* subnormal binade: quantum 0.5; 2 -> code 2 (1.0) */
+        r = nearbyint(a / 0.5);
+        return sign | (uint8_t)r;
+    }
+    frexp(a, &e);
+    e -= 1;                                /* a = f * 2^e, f in [1, 2) */
+    r = nearbyint((a / ldexp(1.0, e) - 1.0) * 2.0);   /* mantissa in halves, RNE */
+    m = (int)r;
+    if (m == 2) { m = 0; e += 1; }
+    if (e + 1 > 3) return sign | 0x7;      /* rounds past 6 */
+    return sign | (uint8_t)(((e + 1) << 1) | m);
+}
+
+uint8_t orc_fp4_encode_bruteforce(double x) {
+    uint8_t sign, best = 0;
+    double a, bd = INFINITY;
+    int c;
+    if (isnan(x)) return 0x7;
+    sign = signbit(x) ? 0x8 : 0x0;
+    a = fabs(x);
+    for (c = 0; c < 8; c++) {
+        double d = fabs(a - orc_fp4_decode((uint8_t)c));
+        if (d < bd || (d == bd && (c & 1) == 0)) { bd = d; best = (uint8_t)c; }
+    }
+    return sign | best;
+}
+
+/* Smallest power of two s with amax <= 6*s; amax == 0 -> 1. */
+double orc_ue8m0_scale_fp4(double amax) {
+    int e;
+    if (!(amax > 0.0)) return 1.0;
+    e = ilogb(amax) - 2;
+    while (amax > ldexp(FP4_MAX, e)) e++;
+    while (amax <= ldexp(FP4_MAX, e - 1)) e--;
+    return ldexp(1.0, e);
+}
+
+void orc_index_k_store_mxfp4(const uint16_t* k_bf16, const int32_t* req, const int32_t* pos, int64_t n,
+                             const int32_t* page_table, int64_t pt_stride,
+                             uint8_t* cache, double eps, double theta) {
+    int64_t t;
+    if (!cache) return;                    /* shared layer: no index-K of its own */
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < n; t++) {
+        double x[IDX_DIM], y[IDX_DIM];
+        int64_t p = pos[t], page;
+        uint8_t* base;
+        uint8_t* codes;
+        int d, b;
+        if (p < 0) continue;
+        for (d = 0; d < IDX_DIM; d++) x[d] = orc_bf16_to_double(k_bf16[t * IDX_DIM + d]);
+        orc_layernorm128(x, y, eps);
+        orc_rope64(y, p, theta, 0);
+        page = page_of(page_table, pt_stride, req[t], p);
+        base = cache + page * MX4_PAGE_B;
+        codes = base + (p % PAGE) * MX4_TOKEN_B;
+        for (b = 0; b < IDX_DIM / 32; b++) {
+            double amax = 0.0, s;
+            int e;
+            for (d = 32 * b; d < 32 * b + 32; d++) if (fabs(y[d]) > amax) amax = fabs(y[d]);
+            s = orc_ue8m0_scale_fp4(amax);
+            frexp(s, &e);                  /* s = 2^(e-1) */
+            base[MX4_SCALE_OFF + (p % PAGE) * 4 + b] = (uint8_t)(e - 1 + 127);
+            for (d = 32 * b; d < 32 * b + 32; d += 2) {
+                uint8_t lo = orc_fp4_encode(y[d] / s), hi = orc_fp4_encode(y[d + 1] / s);
+                codes[d / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+}
+
+/* The indexer score against an MXFP4 cache: as orc_indexer_logits, with each key dim
+ * dequantised as its 4-bit code times its block's scale. */
+void orc_indexer_logits_mxfp4(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                              const int32_t* req, const int32_t* pos, int64_t R,
+                              const int32_t* page_table, int64_t pt_stride, const uint8_t* cache,
+                              float* logits, int64_t stride) {
+    double tab[256];
+    int64_t r;
+    int c;
+    for (c = 0; c < 256; c++) tab[c] = orc_fp8_decode((uint8_t)c);
+    for (r = 0; r < R; r++) {
+        double q[IDX_HEADS][IDX_DIM];
+        int64_t p = pos[r], s;
+        int h, d;
+        for (h = 0; h < IDX_HEADS; h++)
+            for (d = 0; d < IDX_DIM; d++)
+                q[h][d] = tab[q_fp8[(r * IDX_HEADS + h) * IDX_DIM + d]] * (double)q_scale[r * IDX_HEADS + h];
+#pragma omp parallel for schedule(static)
+        for (s = 0; s < stride; s++) {
+            const uint8_t* page;
+            const uint8_t* key;
+            double k[IDX_DIM], acc = 0.0;
+            int hh, dd;
+            if (p < 0 || s > p) { logits[r * stride + s] = -INFINITY; continue; }
+            page = cache + page_of(page_table, pt_stride, req[r], s) * MX4_PAGE_B;
+            key = page + (s % PAGE) * MX4_TOKEN_B;
+            for (dd = 0; dd < IDX_DIM; dd++) {
+                uint8_t code = (uint8_t)((key[dd / 2] >> (4 * (dd & 1))) & 0xF);
+                double sc = ldexp(1.0, (int)page[MX4_SCALE_OFF + (s % PAGE) * 4 + dd / 32] - 127);
+                k[dd] = orc_fp4_decode(code) * sc;
+            }
+            for (hh = 0; hh < IDX_HEADS; hh++) {
+                double dot = 0.0;
+                for (dd = 0; dd < IDX_DIM; dd++) dot += q[hh][dd] * k[dd];
+                acc += (double)w[r * IDX_HEADS + hh] * (dot > 0.0 ? dot : 0.0);
+            }
+            logits[r * stride + s] = (float)acc;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ array helpers (for tests) */
 void orc_fp8_encode_array(const double* x, int64_t n, uint8_t* out, int brute) {
     int64_t i;
@@ -424,4 +568,19 @@ void orc_ln_rope_array(const double* x, const int64_t* pos, int64_t n, double ep
         else for (d = 0; d < 128; d++) out[t * 128 + d] = x[t * 128 + d];
         orc_rope64(out + t * 128, pos[t], theta, inverse);
     }
+}
+
+void orc_fp4_encode_array(const double* x, int64_t n, uint8_t* out, int brute) {
+    int64_t i;
+    for (i = 0; i < n; i++) out[i] = brute ? orc_fp4_encode_bruteforce(x[i]) : orc_fp4_encode(x[i]);
+}
+
+void orc_fp4_decode_array(const uint8_t* c, int64_t n, double* out) {
+    int64_t i;
+    for (i = 0; i < n; i++) out[i] = orc_fp4_decode(c[i]);
+}
+
+void orc_ue8m0_fp4_array(const double* amax, int64_t n, double* out) {
+    int64_t i;
+    for (i = 0; i < n; i++) out[i] = orc_ue8m0_scale_fp4(amax[i]);
 }

@@ -20,6 +20,8 @@
  *   index-K page  (8448 B)  = [64 x 128 B fp8 keys, token-major][64 x fp32 scale]
  *   latent record ( 656 B)  = [512 B fp8 latent][4 x fp32 block scale][64 x bf16 rope]
  *   latent page   (41984 B) = 64 latent records, token-major
+ *   MXFP4 index-K page (4352 B) = [64 x 64 B packed e2m1 codes, token-major, lower dim in
+ *                    the low nibble][64 x 4 E8M0 scale bytes, one per 32 dims]
  */
 #ifndef DSA_ORACLE_H
 #define DSA_ORACLE_H
@@ -36,6 +38,13 @@ uint8_t orc_fp8_encode_bruteforce(double x);
 
 /* ue8m0 block scale: smallest power of two s with amax <= 448*s; amax==0 -> 1. */
 double  orc_ue8m0_scale(double amax);
+
+/* MXFP4 elements (OCP e2m1, a 4-bit code): decode; RNE encode saturating to +-6; the
+ * same encode by exhaustive search; the scale rule with 6 in place of 448. */
+double  orc_fp4_decode(uint8_t code);
+uint8_t orc_fp4_encode(double x);
+uint8_t orc_fp4_encode_bruteforce(double x);
+double  orc_ue8m0_scale_fp4(double amax);
 
 /* bf16 <-> double; double -> bf16 rounds to nearest even (directly, no fp32 step). */
 double   orc_bf16_to_double(uint16_t h);
@@ -65,6 +74,18 @@ void orc_indexer_logits(const uint8_t* q_fp8, const float* q_scale, const float*
                         const int32_t* req, const int32_t* pos, int64_t R,
                         const int32_t* page_table, int64_t pt_stride, const uint8_t* cache,
                         float* logits, int64_t stride);
+
+/* MXFP4 index-K store: LN -> RoPE(dims 0..63) -> per-32-dim ue8m0 (max 6) + e2m1 codes,
+ * written into a 4352-B page. */
+void orc_index_k_store_mxfp4(const uint16_t* k_bf16, const int32_t* req, const int32_t* pos, int64_t n,
+                             const int32_t* page_table, int64_t pt_stride,
+                             uint8_t* cache, double eps, double theta);
+
+/* Indexer logits against an MXFP4 index-K cache. */
+void orc_indexer_logits_mxfp4(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                              const int32_t* req, const int32_t* pos, int64_t R,
+                              const int32_t* page_table, int64_t pt_stride, const uint8_t* cache,
+                              float* logits, int64_t stride);
 
 /* Top-k as a set: the k largest by (score desc, position asc), written ascending by
  * position; -1 tail.  If pos[r]+1 <= k all visible positions are returned.
