@@ -34,12 +34,13 @@ MLA_BYTES_PER_ROW = 2048 * 656 + 64 * 576 * 2 + 64 * 512 * 2 + 2048 * 4   # 1,49
 MLA_FLOPS_PER_ROW = 2 * 64 * 2048 * (576 + 512)                            # 285,212,672
 
 
-def indexer_bytes(ctx, rows):
-    """Algorithmic bytes of one indexer-logits launch: every visible key once (128 B + 4 B
-    scale), the page-table entries, and per row the fp8 query, its scales and head weights."""
+def indexer_bytes(ctx, rows, key_bytes=132):
+    """Algorithmic bytes of one indexer-logits launch: every visible key once (FP8: 128 B + a
+    4-B scale; MXFP4: 64 B + four 1-B scales), the page-table entries, and per row the fp8
+    query, its scales and head weights."""
     import numpy as np
     L = np.asarray(ctx, dtype=np.int64)
-    return int((132 * L + 4 * ((L + 63) // 64)).sum() + rows * (32 * 128 + 32 * 4 + 32 * 4))
+    return int((key_bytes * L + 4 * ((L + 63) // 64)).sum() + rows * (32 * 128 + 32 * 4 + 32 * 4))
 
 
 def source_digest(files):
@@ -257,6 +258,30 @@ def main():
         e1.record(stream)
     torch.cuda.synchronize()
     per["logits"] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in lev])) * 1e3
+    idx_fp8 = D.idx.clone()      # the last step's FP8 top-k
+
+    # MXFP4 index-K variant: the same keys stored at 68 B per token, scored and selected on it
+    mx = D.build_mxfp4_index(0)
+
+    def timed(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        fn()
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+    mx_logits_us = timed(lambda: dsa.dsa_indexer_logits_mxfp4(D.q8, D.qs, D.w_head, D.rows, D.pages, mx, D.logits),
+                         a.steps)
+    mx_topk_us = timed(lambda: dsa.dsa_indexer_topk_mxfp4(D.q8, D.qs, D.w_head, D.rows, D.pages, mx, D.logits,
+                                                          2048, D.idx, D.ws_topk), a.steps)
+    a8, a4 = idx_fp8.cpu().numpy(), D.idx.cpu().numpy()
+    overlap = float(np.mean([len(np.intersect1d(x[x >= 0], y[y >= 0])) / max(1, int((x >= 0).sum()))
+                             for x, y in zip(a8, a4)]))
+    mxb = indexer_bytes(w.ctx, w.R, key_bytes=68)
+    del mx
     R, nl = w.R, len(D.layers)
     full_us = per["store"] + per["quant"] + per["indexer_topk"] + per["mla0"]
     shared_us = float(np.mean([per[f"mla{l}"] for l in D.layers[1:]]))
@@ -295,6 +320,15 @@ def main():
         "full_layer_query_tokens_per_s": R / (full_us * 1e-6),
         "shared_layer_query_tokens_per_s": R / (shared_us * 1e-6),
         "kernel_us": {k: round(v, 2) for k, v in per.items()},
+        "mxfp4_index": {
+            "about": "the same keys in the MXFP4 index-K format (68 B/token); indexer on it, same workload",
+            "logits_us": round(mx_logits_us, 2), "algorithmic_bytes_per_launch": mxb,
+            "logits_GBps": round(mxb / (mx_logits_us * 1e-6) / 1e9, 1),
+            "logits_frac_of_peak": round(mxb / (mx_logits_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "indexer_topk_us": round(mx_topk_us, 2),
+            "topk_overlap_with_fp8": round(overlap, 4),
+            "full_layer_us": round(per["store"] + per["quant"] + mx_topk_us + per["mla0"], 2),
+        },
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on host cores (bounded sample)", file=sys.stderr, flush=True)

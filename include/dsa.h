@@ -56,6 +56,7 @@ extern "C" {
 #define DSA_INDEX_DIM 128
 #define DSA_INDEX_HEADS 32
 #define DSA_INDEX_PAGE_BYTES 8448
+#define DSA_INDEX_MXFP4_PAGE_BYTES 4352
 #define DSA_MLA_HEADS 64
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
@@ -143,6 +144,18 @@ dsa_status dsa_quant_fp8(const uint16_t* x_bf16, int64_t n_blocks, uint8_t* y_fp
 dsa_status dsa_index_k_store(const uint16_t* k_bf16, const dsa_rows* tok, const dsa_pages* pt,
                              uint8_t* index_cache, double ln_eps, double rope_theta, void* stream);
 
+/* MXFP4 index-K store: the compressed indexer-cache format ([IDXC] §读取路径里的两条
+ * "非缓存"字节, the paragraph on vLLM's two indexer-cache formats: 128/2 code bytes plus
+ * 128/32 ue8m0 scales, 68 B per token).  Same LayerNorm and RoPE as dsa_index_k_store;
+ * then per 32 dims the smallest power of two 2^e with amax <= 6 * 2^e, stored as the byte
+ * e + 127 (E8M0), and e2m1 codes (OCP MX FP4) of x / 2^e, round to nearest even, two per
+ * byte with the lower dim in the low nibble.  Page layout (4352 B): [64 tokens x 64 code
+ * bytes][64 tokens x 4 scale bytes].  index_cache: device [pt->num_pages][4352], or NULL
+ * (shared layer: no-op).  Tokens with pos < 0 are skipped.  Same argument errors as
+ * dsa_index_k_store. */
+dsa_status dsa_index_k_store_mxfp4(const uint16_t* k_bf16, const dsa_rows* tok, const dsa_pages* pt,
+                                   uint8_t* index_cache, double ln_eps, double rope_theta, void* stream);
+
 /* Latent store: 576 bf16 -> one 656-B record per token (layout above).
  * kv_bf16: device [tok->n][576]; latent_cache: device [pt->num_pages][41984].
  * Bit-exact.  Tokens with pos < 0 are skipped. */
@@ -169,6 +182,14 @@ dsa_status dsa_indexer_logits(const uint8_t* q_fp8, const float* q_scale, const 
                               const dsa_rows* rows, const dsa_pages* pt, const uint8_t* index_cache,
                               float* logits, int64_t stride, void* stream);
 
+/* The same scores against an MXFP4 index-K cache (written by dsa_index_k_store_mxfp4):
+ *   logits[r][s] = sum_h w[r][h] * ReLU(q_scale[r][h] * sum_b 2^(e_b[s]-127) * <q_fp8[r][h], k4[s]>_b)
+ * over the four 32-dim blocks b.  index_cache: device [pt->num_pages][4352].  Other
+ * arguments, layout and errors as dsa_indexer_logits. */
+dsa_status dsa_indexer_logits_mxfp4(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                                    const dsa_rows* rows, const dsa_pages* pt, const uint8_t* index_cache,
+                                    float* logits, int64_t stride, void* stream);
+
 /* ---------------------------------------------------------------- top-k */
 
 /* Workspace for dsa_topk, in bytes. */
@@ -183,18 +204,28 @@ size_t dsa_topk_workspace_size(int32_t R, int64_t stride, int32_t k);
 dsa_status dsa_topk(const float* logits, int64_t stride, const dsa_rows* rows, int32_t k,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
-/* Fused indexer + top-k: the same idx as dsa_indexer_logits followed by dsa_topk, with the
- * logits kernel also producing the per-row logit range the top-k needs, which saves the
- * top-k one pass over the logits.  `logits` is scratch here: it holds the same values as
- * dsa_indexer_logits would write, except that a row group (rows->group consecutive rows)
- * whose rows all have pos + 1 <= k is not scored at all and its logits rows are left as
- * they were ([IDXC] §优化二:短上下文直接跳过打分: such rows select every position).
- * Arguments as for the two calls; ws sized by dsa_topk_workspace_size(R, stride, k).
- * index_cache must not be NULL (a shared layer reuses the full layer's idx instead). */
+/* Fused indexer + top-k: the same idx as dsa_indexer_logits followed by dsa_topk, without
+ * writing the full logits.  Scores of one page in sixteen set a per-row threshold; the
+ * full scoring pass keeps only the (score, position) pairs at or above it, and the exact
+ * top-k runs over those.  A row whose pairs come out fewer than k or more than the list
+ * holds is scored in full and takes the radix top-k instead, so the selection never
+ * depends on the sample.  `logits` is scratch: on return it holds the sampled pages'
+ * scores and the full scores of rows that fell back; other entries are unspecified.  A
+ * row group (rows->group consecutive rows) whose rows all have pos + 1 <= k is not scored
+ * ([IDXC] §优化二:短上下文直接跳过打分).  Arguments as for the two calls; ws sized by
+ * dsa_topk_workspace_size(R, stride, k).  index_cache must not be NULL (a shared layer
+ * reuses the full layer's idx instead). */
 dsa_status dsa_indexer_topk(const uint8_t* q_fp8, const float* q_scale, const float* w,
                             const dsa_rows* rows, const dsa_pages* pt, const uint8_t* index_cache,
                             float* logits, int64_t stride, int32_t k, int32_t* idx,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* The fused indexer + top-k against an MXFP4 index-K cache: the same idx as
+ * dsa_indexer_logits_mxfp4 followed by dsa_topk.  Arguments and errors as dsa_indexer_topk. */
+dsa_status dsa_indexer_topk_mxfp4(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                                  const dsa_rows* rows, const dsa_pages* pt, const uint8_t* index_cache,
+                                  float* logits, int64_t stride, int32_t k, int32_t* idx,
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- sparse MLA */
 

@@ -79,19 +79,33 @@ dsa_status dsa_quant_fp8(const uint16_t* x, int64_t n_blocks, uint8_t* y, float*
   return hip_status(dsa::launch_quant_fp8(x, n_blocks, y, scale, (hipStream_t)stream), "dsa_quant_fp8");
 }
 
-dsa_status dsa_index_k_store(const uint16_t* k, const dsa_rows* tok, const dsa_pages* pt, uint8_t* cache,
-                             double ln_eps, double rope_theta, void* stream) {
-  dsa_status st = check_rows(tok, "dsa_index_k_store", false);
+static dsa_status index_k_store_impl(const uint16_t* k, const dsa_rows* tok, const dsa_pages* pt, uint8_t* cache,
+                                     double ln_eps, double rope_theta, void* stream, int fmt, const char* name) {
+  dsa_status st = check_rows(tok, name, false);
   if (st) return st;
   if (!cache) return DSA_OK;              // shared layer: owns no index-K pages
-  if ((st = check_pages(pt, tok->max_pos, "dsa_index_k_store"))) return st;
-  if (tok->n > 0 && !k) return fail(DSA_ERR_ARG, "dsa_index_k_store: k is NULL");
-  if (!aligned(k, 16) || !aligned(cache, 16)) return fail(DSA_ERR_ARG, "dsa_index_k_store: misaligned pointer");
-  if (!(ln_eps >= 0.0) || !(rope_theta > 0.0)) return fail(DSA_ERR_ARG, "dsa_index_k_store: bad eps/theta");
+  if ((st = check_pages(pt, tok->max_pos, name))) return st;
+  if (tok->n > 0 && !k) return fail(DSA_ERR_ARG, "%s: k is NULL", name);
+  if (!aligned(k, 16) || !aligned(cache, 16)) return fail(DSA_ERR_ARG, "%s: misaligned pointer", name);
+  if (!(ln_eps >= 0.0) || !(rope_theta > 0.0)) return fail(DSA_ERR_ARG, "%s: bad eps/theta", name);
   double inv_freq[32];
   for (int i = 0; i < 32; i++) inv_freq[i] = pow(rope_theta, -(2.0 * i) / 64.0);
-  return hip_status(dsa::launch_index_k_store(k, view(tok), view(pt), cache, ln_eps, inv_freq, (hipStream_t)stream),
-                    "dsa_index_k_store");
+  const hipError_t e =
+      fmt == dsa::kIdxMxfp4
+          ? dsa::launch_index_k_store_mxfp4(k, view(tok), view(pt), cache, ln_eps, inv_freq, (hipStream_t)stream)
+          : dsa::launch_index_k_store(k, view(tok), view(pt), cache, ln_eps, inv_freq, (hipStream_t)stream);
+  return hip_status(e, name);
+}
+
+dsa_status dsa_index_k_store(const uint16_t* k, const dsa_rows* tok, const dsa_pages* pt, uint8_t* cache,
+                             double ln_eps, double rope_theta, void* stream) {
+  return index_k_store_impl(k, tok, pt, cache, ln_eps, rope_theta, stream, dsa::kIdxFp8, "dsa_index_k_store");
+}
+
+dsa_status dsa_index_k_store_mxfp4(const uint16_t* k, const dsa_rows* tok, const dsa_pages* pt, uint8_t* cache,
+                                   double ln_eps, double rope_theta, void* stream) {
+  return index_k_store_impl(k, tok, pt, cache, ln_eps, rope_theta, stream, dsa::kIdxMxfp4,
+                            "dsa_index_k_store_mxfp4");
 }
 
 dsa_status dsa_latent_store(const uint16_t* kv, const dsa_rows* tok, const dsa_pages* pt, uint8_t* cache,
@@ -116,43 +130,57 @@ int64_t dsa_logits_rows_per_chunk(int64_t num_rows, int64_t row_bytes, int64_t b
   return rows < num_rows ? rows : 0;
 }
 
-dsa_status dsa_indexer_logits(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
-                              const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride,
-                              void* stream) {
-  dsa_status st = check_rows(rows, "dsa_indexer_logits", true);
+static dsa_status indexer_logits_impl(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
+                                      const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride,
+                                      void* stream, int fmt, const char* name) {
+  dsa_status st = check_rows(rows, name, true);
   if (st) return st;
   if (!cache) return DSA_OK;              // shared layer: no indexer
   if (rows->n == 0) return DSA_OK;
-  if ((st = check_pages(pt, rows->max_pos, "dsa_indexer_logits"))) return st;
-  if (!q8 || !qs || !w || !logits) return fail(DSA_ERR_ARG, "dsa_indexer_logits: NULL pointer");
+  if ((st = check_pages(pt, rows->max_pos, name))) return st;
+  if (!q8 || !qs || !w || !logits) return fail(DSA_ERR_ARG, "%s: NULL pointer", name);
   if (!aligned(q8, 16) || !aligned(cache, 16) || !aligned(logits, 16) || !aligned(qs, 4) || !aligned(w, 4))
-    return fail(DSA_ERR_ARG, "dsa_indexer_logits: misaligned pointer");
+    return fail(DSA_ERR_ARG, "%s: misaligned pointer", name);
   if (stride < dsa_logits_stride(rows->max_pos) || stride % 256)
-    return fail(DSA_ERR_ARG, "dsa_indexer_logits: stride %lld < %lld or not a multiple of 256", (long long)stride,
+    return fail(DSA_ERR_ARG, "%s: stride %lld < %lld or not a multiple of 256", name, (long long)stride,
                 (long long)dsa_logits_stride(rows->max_pos));
-  return hip_status(dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride, dsa::LogitsMode{},
+  return hip_status(dsa::launch_indexer_logits(q8, qs, w, view(rows), view(pt), cache, logits, stride, dsa::LogitsMode{}, fmt,
                                                (hipStream_t)stream),
-                    "dsa_indexer_logits");
+                    name);
 }
 
-dsa_status dsa_indexer_topk(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
-                            const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride, int32_t k,
-                            int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  dsa_status st = check_rows(rows, "dsa_indexer_topk", true);
+dsa_status dsa_indexer_logits(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
+                              const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride,
+                              void* stream) {
+  return indexer_logits_impl(q8, qs, w, rows, pt, cache, logits, stride, stream, dsa::kIdxFp8, "dsa_indexer_logits");
+}
+
+dsa_status dsa_indexer_logits_mxfp4(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
+                                    const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride,
+                                    void* stream) {
+  return indexer_logits_impl(q8, qs, w, rows, pt, cache, logits, stride, stream, dsa::kIdxMxfp4,
+                             "dsa_indexer_logits_mxfp4");
+}
+
+static dsa_status indexer_topk_impl(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
+                                    const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride,
+                                    int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream, int fmt,
+                                    const char* name) {
+  dsa_status st = check_rows(rows, name, true);
   if (st) return st;
-  if (!cache) return fail(DSA_ERR_ARG, "dsa_indexer_topk: a shared layer has no indexer (reuse the full layer's idx)");
-  if (k < 1 || k > DSA_TOPK_MAX) return fail(DSA_ERR_ARG, "dsa_indexer_topk: k = %d not in [1, %d]", k, DSA_TOPK_MAX);
+  if (!cache) return fail(DSA_ERR_ARG, "%s: a shared layer has no indexer (reuse the full layer's idx)", name);
+  if (k < 1 || k > DSA_TOPK_MAX) return fail(DSA_ERR_ARG, "%s: k = %d not in [1, %d]", name, k, DSA_TOPK_MAX);
   if (rows->n == 0) return DSA_OK;
-  if ((st = check_pages(pt, rows->max_pos, "dsa_indexer_topk"))) return st;
-  if (!q8 || !qs || !w || !logits || !idx) return fail(DSA_ERR_ARG, "dsa_indexer_topk: NULL pointer");
+  if ((st = check_pages(pt, rows->max_pos, name))) return st;
+  if (!q8 || !qs || !w || !logits || !idx) return fail(DSA_ERR_ARG, "%s: NULL pointer", name);
   if (!aligned(q8, 16) || !aligned(cache, 16) || !aligned(logits, 16) || !aligned(qs, 4) || !aligned(w, 4) ||
       !aligned(idx, 4))
-    return fail(DSA_ERR_ARG, "dsa_indexer_topk: misaligned pointer");
+    return fail(DSA_ERR_ARG, "%s: misaligned pointer", name);
   if (stride < dsa_logits_stride(rows->max_pos) || stride % 256)
-    return fail(DSA_ERR_ARG, "dsa_indexer_topk: stride %lld too small or not a multiple of 256", (long long)stride);
+    return fail(DSA_ERR_ARG, "%s: stride %lld too small or not a multiple of 256", name, (long long)stride);
   const size_t need = dsa_topk_workspace_size(rows->n, stride, k);
   if (!ws || ws_bytes < need || !aligned(ws, 256))
-    return fail(DSA_ERR_WORKSPACE, "dsa_indexer_topk: workspace %zu B < %zu B (256-B aligned)", ws_bytes, need);
+    return fail(DSA_ERR_WORKSPACE, "%s: workspace %zu B < %zu B (256-B aligned)", name, ws_bytes, need);
   // threshold-filtered: scores of one page in sixteen set a per-row threshold; the full pass
   // keeps only the scores at or above it (the logits are not written); the exact top-k runs
   // over those candidates; rows whose candidates turn out short (fewer than k) or overflow
@@ -164,15 +192,29 @@ dsa_status dsa_indexer_topk(const uint8_t* q8, const float* qs, const float* w, 
   const int R = rows->n;
   hipError_t e = dsa::launch_topk_init(R, k, ws, s);
   if (e == hipSuccess)
-    e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_sample_mode(ws, R, k, k), s);
+    e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_sample_mode(ws, R, k, k), fmt, s);
   if (e == hipSuccess) e = dsa::launch_topk_threshold(logits, stride, rv, k, ws, s);
   if (e == hipSuccess)
-    e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_filter_mode(ws, R, k, k), s);
+    e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_filter_mode(ws, R, k, k), fmt, s);
   if (e == hipSuccess) e = dsa::launch_topk_filtered_final(rv, stride, k, idx, ws, s);
   if (e == hipSuccess)
-    e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_fallback_mode(ws, R, k), s);
+    e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_fallback_mode(ws, R, k), fmt, s);
   if (e == hipSuccess) e = dsa::launch_topk_fallback(logits, stride, rv, k, idx, ws, s);
-  return hip_status(e, "dsa_indexer_topk");
+  return hip_status(e, name);
+}
+
+dsa_status dsa_indexer_topk(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
+                            const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride, int32_t k,
+                            int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return indexer_topk_impl(q8, qs, w, rows, pt, cache, logits, stride, k, idx, ws, ws_bytes, stream, dsa::kIdxFp8,
+                           "dsa_indexer_topk");
+}
+
+dsa_status dsa_indexer_topk_mxfp4(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
+                                  const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride,
+                                  int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return indexer_topk_impl(q8, qs, w, rows, pt, cache, logits, stride, k, idx, ws, ws_bytes, stream, dsa::kIdxMxfp4,
+                           "dsa_indexer_topk_mxfp4");
 }
 
 size_t dsa_topk_workspace_size(int32_t R, int64_t stride, int32_t k) {

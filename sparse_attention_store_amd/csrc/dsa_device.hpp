@@ -11,6 +11,11 @@ constexpr int kIdxDim = 128;
 constexpr int kIdxHeads = 32;
 constexpr int kIdxPageBytes = 8448;     // 64 x 128 B keys + 64 x 4 B scales
 constexpr int kIdxScaleOff = 8192;
+// MXFP4 index-K page: 64 x 64 B of packed e2m1 codes (lower dim in the low nibble), then
+// 64 x 4 E8M0 scale bytes, one per 32 dims: 68 B per token
+constexpr int kMx4KeyBytes = 64;
+constexpr int kMx4ScaleOff = kPage * kMx4KeyBytes;          // 4096
+constexpr int kMx4PageBytes = kPage * (kMx4KeyBytes + 4);   // 4352
 constexpr int kHeads = 64;
 constexpr int kLat = 576;
 constexpr int kVal = 512;

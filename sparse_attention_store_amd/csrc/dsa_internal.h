@@ -23,6 +23,11 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t n_blocks, uint8_t* y, flo
 hipError_t launch_index_k_store(const uint16_t* k, RowsView tok, PagesView pg, uint8_t* cache,
                                 double eps, const double* inv_freq32, hipStream_t s);
 hipError_t launch_latent_store(const uint16_t* kv, RowsView tok, PagesView pg, uint8_t* cache, hipStream_t s);
+hipError_t launch_index_k_store_mxfp4(const uint16_t* k, RowsView tok, PagesView pg, uint8_t* cache,
+                                      double eps, const double* inv_freq32, hipStream_t s);
+
+// Index-K cache formats: FP8 (132 B per token) and MXFP4 (68 B per token).
+enum { kIdxFp8 = 0, kIdxMxfp4 = 1 };
 
 // What a launch of the indexer-logits kernel does with the scores.
 enum { kLogitsPlain = 0, kLogitsSample = 1, kLogitsFilter = 2, kLogitsFallback = 3 };
@@ -48,7 +53,7 @@ struct LogitsMode {
 };
 hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float* w, RowsView rows,
                                  PagesView pg, const uint8_t* cache, float* logits, int64_t stride,
-                                 const LogitsMode& md, hipStream_t s);
+                                 const LogitsMode& md, int fmt, hipStream_t s);
 
 size_t topk_workspace_bytes(int32_t R, int64_t stride, int32_t k);
 hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,

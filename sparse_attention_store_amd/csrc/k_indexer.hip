@@ -1,6 +1,12 @@
-// k_indexer.hip -- lightning-indexer logits over the paged FP8 index-K cache.
+// k_indexer.hip -- lightning-indexer logits over the paged index-K cache (FP8, or the
+// MXFP4 variant of the same page scheme).
 //
 //   logits[r][s] = sum_h w[r][h] * ReLU(q_scale[r][h] * k_scale[s] * <q8[r][h], k8[s]>)
+//
+// MXFP4 keys ("GLM-5.3 推理全链路(十一)", the paragraph on vLLM's two indexer-cache
+// formats): 64 B of e2m1 codes and four E8M0 scales per token, one per 32 dims; the
+// block scales enter the product inside the MFMA (per-lane scale bytes), so the score is
+// sum_h w * ReLU(q_scale * sum_b s_b <q8, k4>_b).
 //
 // for s <= pos[r], -inf after it ("vLLM 推理链路概览: 以 GLM-5.2 为例", section DSA
 // Indexer for the score; section Sparse MLA Attention for the causal j <= i rule).
@@ -52,19 +58,66 @@ __device__ inline f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-struct PageRegs {
-  i32x8 b[4];   // four 16-key tiles
-  float ks;     // scale of key `lane` of the page
+// One page of keys in registers, as MFMA B operands of its four 16-key tiles.
+template <int FMT> struct PageRegs;
+template <> struct PageRegs<kIdxFp8> {
+  i32x8 b[4];   // FP8: bytes [16g,16g+16) and [64+16g,64+16g+16) of key 16t + l%16
+  float ks;     // scale of key `lane` of the page, applied after the head reduction
 };
+template <> struct PageRegs<kIdxMxfp4> {
+  i32x4 b[4];   // MXFP4: dims [32g, 32g+32) of key 16t + l%16 (16 packed bytes)
+  int sb;       // byte t: the E8M0 scale of that 32-dim block (the MFMA's per-lane scale)
+};
+template <int FMT> constexpr int kPageBytes = FMT == kIdxFp8 ? kIdxPageBytes : kMx4PageBytes;
 
-__device__ inline void load_page(PageRegs& P, const uint8_t* page, int lane) {
+__device__ inline void load_page(PageRegs<kIdxFp8>& P, const uint8_t* page, int lane) {
   const int g = lane >> 4, k16 = lane & 15;
 #pragma unroll
   for (int t = 0; t < 4; t++) P.b[t] = load_b_operand(page + (16 * t + k16) * kIdxDim, g);
   P.ks = *reinterpret_cast<const float*>(page + kIdxScaleOff + 4 * lane);
 }
+__device__ inline void load_page(PageRegs<kIdxMxfp4>& P, const uint8_t* page, int lane) {
+  const int g = lane >> 4, k16 = lane & 15;
+  uint32_t sw[4];
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    P.b[t] = *reinterpret_cast<const i32x4*>(page + (16 * t + k16) * kMx4KeyBytes + 16 * g);
+    sw[t] = *reinterpret_cast<const uint32_t*>(page + kMx4ScaleOff + 4 * (16 * t + k16));
+  }
+  uint32_t sb = 0;
+#pragma unroll
+  for (int t = 0; t < 4; t++) sb |= ((sw[t] >> (8 * g)) & 0xFFu) << (8 * t);
+  P.sb = (int)sb;
+}
+__device__ inline float key_scale(const PageRegs<kIdxFp8>& P) { return P.ks; }
+__device__ inline float key_scale(const PageRegs<kIdxMxfp4>&) { return 1.0f; }   // inside the MFMA
 
-template <int RG, int KIND>
+// A (16 heads x 128 dims of q, FP8, unit scale: q's own scale is folded into w) times the
+// keys of tile T.  The MXFP4 product is the block-scaled MFMA with an e2m1 B operand: each
+// lane's 32 codes take that lane's scale byte (byte T of P.sb, chosen by the op_sel).  On
+// this MFMA the FP8 operand's K order is bytes [16g,16g+16) -> K 16g.., [16..32) -> 64+16g..
+// and the FP4 operand's is dims 32g.. in nibble order, so both see key dim k at K = k.
+template <int T>
+__device__ inline f32x4 mfma_tile(const i32x8& a, const PageRegs<kIdxFp8>& P) { return mfma_fp8(a, P.b[T]); }
+template <int T>
+__device__ inline f32x4 mfma_tile(const i32x8& a, const PageRegs<kIdxMxfp4>& P) {
+  const i32x8 b = {P.b[T][0], P.b[T][1], P.b[T][2], P.b[T][3], 0, 0, 0, 0};
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, T, P.sb);
+}
+
+// tile index as a run-time value; the unrolled callers make it a constant
+template <int FMT>
+__device__ inline f32x4 mfma_tile_at(int t, const i32x8& a, const PageRegs<FMT>& P) {
+  switch (t) {
+    case 0: return mfma_tile<0>(a, P);
+    case 1: return mfma_tile<1>(a, P);
+    case 2: return mfma_tile<2>(a, P);
+    default: return mfma_tile<3>(a, P);
+  }
+}
+
+template <int RG, int KIND, int FMT>
 __global__ void __launch_bounds__(256, 4)
 k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
                 const int32_t* __restrict__ req, const int32_t* __restrict__ pos, DevPages pg,
@@ -127,7 +180,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     // row's keys is all the radix select needs, so the group's union serves each of its rows)
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
     // score one page (held in registers) for all RG rows
-    auto process = [&](const PageRegs& P, int64_t vi, int64_t pid) {
+    auto process = [&](const PageRegs<FMT>& P, int64_t vi, int64_t pid) {
       // keep the per-page LDS reads of q / w inside the loop (hoisting them would pin all
       // rows' operands in registers again)
       __asm__ volatile("" ::: "memory");
@@ -147,8 +200,8 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         float part[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-          const f32x4 c0 = mfma_fp8(A[0], P.b[t]);
-          const f32x4 c1 = mfma_fp8(A[1], P.b[t]);
+          const f32x4 c0 = mfma_tile_at(t, A[0], P);
+          const f32x4 c1 = mfma_tile_at(t, A[1], P);
           float acc = wr[0].x * relu(c0[0]);
           acc = fmaf(wr[0].y, relu(c0[1]), acc);
           acc = fmaf(wr[0].z, relu(c0[2]), acc);
@@ -168,7 +221,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(keep0), __float_as_uint(keep1), false, false);
         const float mine = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
         const bool vis = pid >= 0 && s <= prow[r];
-        const float v = vis ? mine * P.ks : -INFINITY;
+        const float v = vis ? mine * key_scale(P) : -INFINITY;
         const uint32_t u = __float_as_uint(v);
         const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
         if (KIND == kLogitsFilter) {
@@ -187,19 +240,19 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       }
     };
     // two register buffers in ping-pong: the next page loads while this one is scored
-    PageRegs pa, pb;
+    PageRegs<FMT> pa, pb;
     int64_t pi = pg0 + wave;
     int64_t ida = pi < pend ? page_of(pg, rq, pi * step * 64) : -1;
-    if (pi < pend && ida >= 0) load_page(pa, cache + ida * kIdxPageBytes, lane);
+    if (pi < pend && ida >= 0) load_page(pa, cache + ida * kPageBytes<FMT>, lane);
     for (; pi < pend; pi += 2 * kWaves) {
       const int64_t pn = pi + kWaves;
       const int64_t idb = pn < pend ? page_of(pg, rq, pn * step * 64) : -1;
-      if (pn < pend && idb >= 0) load_page(pb, cache + idb * kIdxPageBytes, lane);
+      if (pn < pend && idb >= 0) load_page(pb, cache + idb * kPageBytes<FMT>, lane);
       process(pa, pi, ida);
       if (pn >= pend) break;
       const int64_t pn2 = pn + kWaves;
       ida = pn2 < pend ? page_of(pg, rq, pn2 * step * 64) : -1;
-      if (pn2 < pend && ida >= 0) load_page(pa, cache + ida * kIdxPageBytes, lane);
+      if (pn2 < pend && ida >= 0) load_page(pa, cache + ida * kPageBytes<FMT>, lane);
       process(pb, pn, idb);
     }
     if (KIND != kLogitsFilter && md.range != nullptr) {
@@ -251,7 +304,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
   }
 }
 
-template <int RG, int KIND>
+template <int RG, int KIND, int FMT>
 hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsView rows, DevPages g,
                      const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md, hipStream_t s) {
   const int64_t n_groups = rows.n / RG;
@@ -263,27 +316,25 @@ hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsVie
   int chunk = 32;
   while (chunk > 4 && n_groups * ((total_pages + chunk - 1) / chunk) < want) chunk >>= 1;
   const int64_t nchunks = (total_pages + chunk - 1) / chunk;
-  hipLaunchKernelGGL((k_logits_decode<RG, KIND>), dim3((unsigned)nchunks, (unsigned)n_groups), dim3(256), 0, s, q8, qs,
+  hipLaunchKernelGGL((k_logits_decode<RG, KIND, FMT>), dim3((unsigned)nchunks, (unsigned)n_groups), dim3(256), 0, s, q8, qs,
                      w, rows.req, rows.pos, g, cache, logits, stride, chunk, md);
   return hipGetLastError();
 }
 
-template <int RG>
+template <int RG, int FMT>
 hipError_t launch_kind(const uint8_t* q8, const float* qs, const float* w, RowsView rows, DevPages g,
                        const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md, hipStream_t s) {
   switch (md.kind) {
-    case kLogitsSample: return launch_rg<RG, kLogitsSample>(q8, qs, w, rows, g, cache, logits, stride, md, s);
-    case kLogitsFilter: return launch_rg<RG, kLogitsFilter>(q8, qs, w, rows, g, cache, logits, stride, md, s);
-    case kLogitsFallback: return launch_rg<RG, kLogitsFallback>(q8, qs, w, rows, g, cache, logits, stride, md, s);
-    default: return launch_rg<RG, kLogitsPlain>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case kLogitsSample: return launch_rg<RG, kLogitsSample, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case kLogitsFilter: return launch_rg<RG, kLogitsFilter, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case kLogitsFallback: return launch_rg<RG, kLogitsFallback, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    default: return launch_rg<RG, kLogitsPlain, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
   }
 }
 
-}  // namespace
-
-hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float* w, RowsView rows, PagesView pg,
-                                 const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md,
-                                 hipStream_t s) {
+template <int FMT>
+hipError_t launch_fmt(const uint8_t* q8, const float* qs, const float* w, RowsView rows, PagesView pg,
+                      const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md, hipStream_t s) {
   if (rows.n <= 0) return hipSuccess;
   DevPages g{pg.pt, pg.pt_stride, pg.num_reqs, pg.num_pages};
   // rows of a group are processed in sub-groups of the largest divisor of `group` <= 6
@@ -292,13 +343,22 @@ hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float
   for (int d = 6; d >= 1; d--)
     if (rows.group % d == 0) { rg = d; break; }
   switch (rg) {
-    case 6: return launch_kind<6>(q8, qs, w, rows, g, cache, logits, stride, md, s);
-    case 5: return launch_kind<5>(q8, qs, w, rows, g, cache, logits, stride, md, s);
-    case 4: return launch_kind<4>(q8, qs, w, rows, g, cache, logits, stride, md, s);
-    case 3: return launch_kind<3>(q8, qs, w, rows, g, cache, logits, stride, md, s);
-    case 2: return launch_kind<2>(q8, qs, w, rows, g, cache, logits, stride, md, s);
-    default: return launch_kind<1>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case 6: return launch_kind<6, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case 5: return launch_kind<5, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case 4: return launch_kind<4, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case 3: return launch_kind<3, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    case 2: return launch_kind<2, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
+    default: return launch_kind<1, FMT>(q8, qs, w, rows, g, cache, logits, stride, md, s);
   }
+}
+
+}  // namespace
+
+hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float* w, RowsView rows, PagesView pg,
+                                 const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md, int fmt,
+                                 hipStream_t s) {
+  return fmt == kIdxMxfp4 ? launch_fmt<kIdxMxfp4>(q8, qs, w, rows, pg, cache, logits, stride, md, s)
+                          : launch_fmt<kIdxFp8>(q8, qs, w, rows, pg, cache, logits, stride, md, s);
 }
 
 DSA_DEFINE_ERROR_ACCESSOR(take_device_errors_indexer)

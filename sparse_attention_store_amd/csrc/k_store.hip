@@ -60,21 +60,13 @@ __global__ void __launch_bounds__(256) k_quant_fp8(const uint16_t* __restrict__ 
 
 struct InvFreq { double v[32]; };
 
-// LN and RoPE in fp64 so the stored codes do not depend on fp32 rounding; the
-// final fp64 -> fp8 step rounds once.
-__global__ void __launch_bounds__(256) k_index_k_store(const uint16_t* __restrict__ k, const int32_t* __restrict__ req,
-                                                       const int32_t* __restrict__ pos, int32_t n, DevPages pg,
-                                                       uint8_t* __restrict__ cache, double eps, InvFreq f) {
-  int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
-  int l16 = threadIdx.x & 15;
-  if (t >= n) return;
-  int64_t p = pos[t];
-  if (p < 0) return;                    // padded row: nothing stored
-  int64_t page = page_of(pg, req[t], p);
-  if (page < 0) return;
+// LayerNorm then interleaved RoPE of one 128-dim key in fp64, spread over a 16-lane group
+// (dims 8*l16 .. 8*l16+7 per lane), so the stored codes do not depend on fp32 rounding.
+__device__ inline void ln_rope_group16(const uint16_t* kt, int l16, int64_t p, double eps, const InvFreq& f,
+                                       double* x) {
   float xf[8];
-  load8_bf16(k + t * 128 + l16 * 8, xf);
-  double x[8], sum = 0.0;
+  load8_bf16(kt + l16 * 8, xf);
+  double sum = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; i++) { x[i] = (double)xf[i]; sum += x[i]; }
   double mu = group_sum_d<16>(sum) / 128.0;
@@ -95,6 +87,21 @@ __global__ void __launch_bounds__(256) k_index_k_store(const uint16_t* __restric
       x[2 * j + 1] = a * s + b * c;
     }
   }
+}
+
+// The final fp64 -> fp8 step rounds once.
+__global__ void __launch_bounds__(256) k_index_k_store(const uint16_t* __restrict__ k, const int32_t* __restrict__ req,
+                                                       const int32_t* __restrict__ pos, int32_t n, DevPages pg,
+                                                       uint8_t* __restrict__ cache, double eps, InvFreq f) {
+  int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  int l16 = threadIdx.x & 15;
+  if (t >= n) return;
+  int64_t p = pos[t];
+  if (p < 0) return;                    // padded row: nothing stored
+  int64_t page = page_of(pg, req[t], p);
+  if (page < 0) return;
+  double x[8];
+  ln_rope_group16(k + t * 128, l16, p, eps, f, x);
   double amax = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; i++) amax = fmax(amax, fabs(x[i]));
@@ -115,6 +122,62 @@ __global__ void __launch_bounds__(256) k_index_k_store(const uint16_t* __restric
   uint8_t* base = cache + page * kIdxPageBytes;
   *reinterpret_cast<uint2*>(base + (p & 63) * 128 + l16 * 8) = make_uint2(lo, hi);
   if (l16 == 0) *reinterpret_cast<float*>(base + kIdxScaleOff + (p & 63) * 4) = __builtin_ldexpf(1.0f, e);
+}
+
+// e2m1 code of v (|v| <= 6 by the scale choice): round to nearest, ties to the even code.
+// Magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6: below 1 the step is 1/2; from 1 on, one mantissa bit
+// per binade, rounded on the fp64 mantissa.
+__device__ inline uint32_t fp4_from_f64_rne(double v) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(v);
+  const uint32_t sign = (uint32_t)(bits >> 63) << 3;
+  const uint64_t a = bits & 0x7FFFFFFFFFFFFFFFULL;
+  const double av = __longlong_as_double((long long)a);
+  if (av >= 6.0) return sign | 7u;
+  if (av < 1.0) return sign | (uint32_t)rint(av * 2.0);      // 0, 1, or 2 (= 1.0)
+  int e = (int)(a >> 52) - 1023;                              // 0, 1 or 2
+  uint64_t mant = a & ((1ULL << 52) - 1);
+  uint32_t q = (uint32_t)(mant >> 51);
+  const uint64_t rem = mant & ((1ULL << 51) - 1), half = 1ULL << 50;
+  if (rem > half || (rem == half && (q & 1))) q++;
+  if (q == 2) { q = 0; e++; }
+  const uint32_t code = (uint32_t)((e + 1) << 1) | q;
+  return sign | (code > 7u ? 7u : code);
+}
+
+// MXFP4 index-K store: the same LN + RoPE, then per 32 dims (four lanes) the smallest power
+// of two 2^e with amax <= 6 * 2^e, stored as the E8M0 byte e + 127, and e2m1 codes of
+// x / 2^e, two per byte with the lower dim in the low nibble ("GLM-5.3 推理全链路(十一)",
+// the paragraph on vLLM's MXFP4 indexer-cache format: 68 B per token).
+__global__ void __launch_bounds__(256) k_index_k_store_mxfp4(const uint16_t* __restrict__ k,
+                                                             const int32_t* __restrict__ req,
+                                                             const int32_t* __restrict__ pos, int32_t n, DevPages pg,
+                                                             uint8_t* __restrict__ cache, double eps, InvFreq f) {
+  int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  int l16 = threadIdx.x & 15;
+  if (t >= n) return;
+  int64_t p = pos[t];
+  if (p < 0) return;
+  int64_t page = page_of(pg, req[t], p);
+  if (page < 0) return;
+  double x[8];
+  ln_rope_group16(k + t * 128, l16, p, eps, f, x);
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) amax = fmax(amax, fabs(x[i]));
+  amax = group_max_d<4>(amax);          // the four lanes of this 32-dim block
+  int e = 0;
+  if (amax > 0.0) {                     // 6 = 1.5 * 2^2
+    const uint64_t b = (uint64_t)__double_as_longlong(amax);
+    const int E = (int)(b >> 52) - 1023;
+    e = E - 2 + ((b & ((1ULL << 52) - 1)) > (1ULL << 51) ? 1 : 0);
+  }
+  const double sinv = __builtin_ldexp(1.0, -e);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) word |= fp4_from_f64_rne(x[i] * sinv) << (4 * i);
+  uint8_t* base = cache + page * kMx4PageBytes;
+  *reinterpret_cast<uint32_t*>(base + (p & 63) * kMx4KeyBytes + l16 * 4) = word;
+  if ((l16 & 3) == 0) base[kMx4ScaleOff + (p & 63) * 4 + (l16 >> 2)] = (uint8_t)(e + 127);
 }
 
 // One wave per token: lanes 0..63 quantise latent dims 8l..8l+7 (16 lanes per block);
@@ -148,6 +211,18 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t n_blocks, uint8_t* y, flo
   if (n_blocks <= 0) return hipSuccess;
   int64_t grid = (n_blocks + 15) / 16;
   hipLaunchKernelGGL(k_quant_fp8, dim3((unsigned)grid), dim3(256), 0, s, x, n_blocks, y, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_k_store_mxfp4(const uint16_t* k, RowsView tok, PagesView pg, uint8_t* cache, double eps,
+                                      const double* inv_freq32, hipStream_t s) {
+  if (tok.n <= 0) return hipSuccess;
+  InvFreq f;
+  for (int i = 0; i < 32; i++) f.v[i] = inv_freq32[i];
+  DevPages g{pg.pt, pg.pt_stride, pg.num_reqs, pg.num_pages};
+  int64_t grid = ((int64_t)tok.n + 15) / 16;
+  hipLaunchKernelGGL(k_index_k_store_mxfp4, dim3((unsigned)grid), dim3(256), 0, s, k, tok.req, tok.pos, tok.n, g,
+                     cache, eps, f);
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 PAGE_SIZE = 64
 INDEX_PAGE_BYTES = 8448
+INDEX_MXFP4_PAGE_BYTES = 4352
 LATENT_PAGE_BYTES = 41984
 TOPK_MAX = 2048
 
@@ -61,13 +62,16 @@ def _load():
         "dsa_layer_is_shared": ([ctypes.POINTER(_Rule), i32], ctypes.c_int),
         "dsa_quant_fp8": ([p, i64, p, p, p], ctypes.c_int),
         "dsa_index_k_store": ([p, R, P, p, f64, f64, p], ctypes.c_int),
+        "dsa_index_k_store_mxfp4": ([p, R, P, p, f64, f64, p], ctypes.c_int),
         "dsa_latent_store": ([p, R, P, p, p], ctypes.c_int),
         "dsa_logits_stride": ([i32], i64),
         "dsa_logits_rows_per_chunk": ([i64, i64, i64], i64),
         "dsa_indexer_logits": ([p, p, p, R, P, p, p, i64, p], ctypes.c_int),
+        "dsa_indexer_logits_mxfp4": ([p, p, p, R, P, p, p, i64, p], ctypes.c_int),
         "dsa_topk_workspace_size": ([i32, i64, i32], sz),
         "dsa_topk": ([p, i64, R, i32, p, p, sz, p], ctypes.c_int),
         "dsa_indexer_topk": ([p, p, p, R, P, p, p, i64, i32, p, p, sz, p], ctypes.c_int),
+        "dsa_indexer_topk_mxfp4": ([p, p, p, R, P, p, p, i64, i32, p, p, sz, p], ctypes.c_int),
         "dsa_sparse_mla_workspace_size": ([i32, i32], sz),
         "dsa_sparse_mla_decode": ([p, R, P, p, p, i32, f32, p, p, p, sz, p], ctypes.c_int),
         "dsa_sparse_mla_prefill": ([p, R, P, p, p, i32, f32, p, p, p, sz, p], ctypes.c_int),
@@ -82,8 +86,9 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("dsa_abi_version", "dsa_last_error", "dsa_layer_is_shared", "dsa_quant_fp8",
-            "dsa_index_k_store", "dsa_latent_store", "dsa_logits_stride", "dsa_logits_rows_per_chunk",
-            "dsa_indexer_logits", "dsa_topk_workspace_size", "dsa_topk", "dsa_indexer_topk", "dsa_sparse_mla_workspace_size",
+            "dsa_index_k_store", "dsa_index_k_store_mxfp4", "dsa_latent_store", "dsa_logits_stride",
+            "dsa_logits_rows_per_chunk", "dsa_indexer_logits", "dsa_indexer_logits_mxfp4", "dsa_topk_workspace_size",
+            "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_mxfp4", "dsa_sparse_mla_workspace_size",
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_check_device_errors")
 
 
@@ -150,6 +155,13 @@ def dsa_index_k_store(k, rows: Rows, pages: Pages, index_cache, ln_eps=1e-6, rop
                                   rope_theta, _stream(stream)))
 
 
+def dsa_index_k_store_mxfp4(k, rows: Rows, pages: Pages, index_cache, ln_eps=1e-6, rope_theta=10000.0,
+                            stream=None):
+    r, p = rows.c(), pages.c()
+    _check(_lib.dsa_index_k_store_mxfp4(_ptr(k), ctypes.byref(r), ctypes.byref(p), _ptr(index_cache), ln_eps,
+                                        rope_theta, _stream(stream)))
+
+
 def dsa_latent_store(kv, rows: Rows, pages: Pages, latent_cache, stream=None):
     r, p = rows.c(), pages.c()
     _check(_lib.dsa_latent_store(_ptr(kv), ctypes.byref(r), ctypes.byref(p), _ptr(latent_cache), _stream(stream)))
@@ -169,6 +181,12 @@ def dsa_indexer_logits(q8, q_scale, w, rows: Rows, pages: Pages, index_cache, lo
                                    _ptr(index_cache), _ptr(logits), logits.shape[-1], _stream(stream)))
 
 
+def dsa_indexer_logits_mxfp4(q8, q_scale, w, rows: Rows, pages: Pages, index_cache, logits, stream=None):
+    r, p = rows.c(), pages.c()
+    _check(_lib.dsa_indexer_logits_mxfp4(_ptr(q8), _ptr(q_scale), _ptr(w), ctypes.byref(r), ctypes.byref(p),
+                                         _ptr(index_cache), _ptr(logits), logits.shape[-1], _stream(stream)))
+
+
 def dsa_topk_workspace_size(R: int, stride: int, k: int) -> int:
     return _lib.dsa_topk_workspace_size(R, stride, k)
 
@@ -184,6 +202,14 @@ def dsa_indexer_topk(q8, q_scale, w, rows: Rows, pages: Pages, index_cache, logi
     _check(_lib.dsa_indexer_topk(_ptr(q8), _ptr(q_scale), _ptr(w), ctypes.byref(r), ctypes.byref(p),
                                  _ptr(index_cache), _ptr(logits), logits.shape[-1], k, _ptr(idx), _ptr(ws),
                                  0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsa_indexer_topk_mxfp4(q8, q_scale, w, rows: Rows, pages: Pages, index_cache, logits, k: int, idx, ws,
+                           stream=None):
+    r, p = rows.c(), pages.c()
+    _check(_lib.dsa_indexer_topk_mxfp4(_ptr(q8), _ptr(q_scale), _ptr(w), ctypes.byref(r), ctypes.byref(p),
+                                       _ptr(index_cache), _ptr(logits), logits.shape[-1], k, _ptr(idx), _ptr(ws),
+                                       0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dsa_sparse_mla_workspace_size(R: int, k: int) -> int:

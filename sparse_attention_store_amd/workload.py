@@ -112,6 +112,22 @@ class DeviceLayer:
                     dsa.dsa_latent_store(kv, rows, self.pages, self.latent_cache[l])
         torch.cuda.synchronize()
 
+    def build_mxfp4_index(self, layer: int = 0) -> torch.Tensor:
+        """An MXFP4 index-K cache (68 B per token) of the same keys as the layer's FP8 one."""
+        w = self.w
+        cache = torch.zeros((w.num_pages, dsa.INDEX_MXFP4_PAGE_BYTES), dtype=torch.uint8, device=self.device)
+        for b in range(w.B):
+            L = int(w.ctx[b])
+            for p0 in range(0, L, self._chunk):
+                p1 = min(L, p0 + self._chunk)
+                n = p1 - p0
+                req = torch.full((n,), b, dtype=torch.int32, device=self.device)
+                pos = torch.arange(p0, p1, dtype=torch.int32, device=self.device)
+                k = self._gen(gi.T_RAW_K, (int(self.token_base[b]) + p0) * 128, n * 128).view(n, 128)
+                dsa.dsa_index_k_store_mxfp4(k, dsa.Rows(req, pos, p1 - 1), self.pages, cache, LN_EPS, ROPE_THETA)
+        torch.cuda.synchronize()
+        return cache
+
     # ------------------------------------------------------------------ layer steps
     def tok_rows(self) -> dsa.Rows:
         return self.rows

@@ -1,0 +1,110 @@
+"""GPU parity of the MXFP4 index-K variant (68 B per token; "GLM-5.3 推理全链路(十一)", the
+paragraph on vLLM's two indexer-cache formats) against the CPU oracle on the same seeded inputs:
+the store byte for byte, the logits within the indexer tolerance, and the fused indexer + top-k
+equal to the separate calls and to the oracle's sets."""
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as gi
+import oracle as orc
+from parity import LN_EPS, THETA, all_tokens, assert_logits_close, queries, raw_k, topk_sets_match
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from sparse_attention_store_amd import dsa  # noqa: E402
+
+DEV = "cuda"
+MX_PAGE = 64 * 68
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def _announce(name):
+    print(f"\n[gpu] {name}", flush=True)
+
+
+def oracle_mx_cache(w):
+    req, pos = all_tokens(w)
+    cache = np.zeros((w.num_pages, MX_PAGE), np.uint8)
+    orc.index_k_store_mxfp4(raw_k(w), req, pos, w.page_table, cache, LN_EPS, THETA)
+    return cache
+
+
+def gpu_mx_cache(w):
+    req, pos = all_tokens(w)
+    cache = torch.zeros((w.num_pages, MX_PAGE), dtype=torch.uint8, device=DEV)
+    tok = dsa.Rows(dev(req), dev(pos), int(pos.max()), 1)
+    pages = dsa.Pages(dev(w.page_table), w.num_pages)
+    dsa.dsa_index_k_store_mxfp4(dev(raw_k(w).view(np.int16)), tok, pages, cache, LN_EPS, THETA)
+    torch.cuda.synchronize()
+    return cache
+
+
+def rows_pages(w):
+    return (dsa.Rows(dev(w.row_req), dev(w.row_pos), w.max_pos, w.rows_per_req),
+            dsa.Pages(dev(w.page_table), w.num_pages))
+
+
+def q_inputs(w):
+    q, wt, _ = queries(w, [])
+    q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+    return q8.reshape(w.R, 32, 128), qs.reshape(w.R, 32), wt
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2])
+def test_mxfp4_store_bit_exact(cid):
+    _announce(f"mxfp4 store c{cid}")
+    w = gi.config(cid, "small")
+    got = host(gpu_mx_cache(w))
+    ref = oracle_mx_cache(w)
+    diff = np.argwhere(got != ref)
+    assert len(diff) == 0, f"{len(diff)} MXFP4 index-K bytes differ, first at {diff[:5].tolist()}"
+    dsa.dsa_check_device_errors()
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2, 3])
+def test_mxfp4_logits_stage(cid):
+    _announce(f"mxfp4 logits c{cid}")
+    w = gi.config(cid, "small")
+    cache = oracle_mx_cache(w)
+    q8, qs, wt = q_inputs(w)
+    ref = orc.indexer_logits_mxfp4(q8, qs, wt, w.row_req, w.row_pos, w.page_table, cache)
+    rows, pages = rows_pages(w)
+    logits = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_logits_mxfp4(dev(q8), dev(qs), dev(wt), rows, pages, dev(cache), logits)
+    torch.cuda.synchronize()
+    assert_logits_close(host(logits), ref)
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2])
+def test_mxfp4_fused_topk(cid):
+    _announce(f"mxfp4 fused indexer+topk c{cid}")
+    w = gi.config(cid, "small")
+    cache = gpu_mx_cache(w)
+    q8, qs, wt = q_inputs(w)
+    rows, pages = rows_pages(w)
+    stride = orc.logits_stride(w.max_pos)
+    logits = torch.empty((w.R, stride), dtype=torch.float32, device=DEV)
+    idx = torch.full((w.R, 2048), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(dsa.dsa_topk_workspace_size(w.R, stride, 2048), dtype=torch.uint8, device=DEV)
+    dq8, dqs, dwt = dev(q8), dev(qs), dev(wt)
+    dsa.dsa_indexer_topk_mxfp4(dq8, dqs, dwt, rows, pages, cache, logits, 2048, idx, ws)
+    torch.cuda.synchronize()
+    fused = host(idx).copy()
+    dsa.dsa_indexer_logits_mxfp4(dq8, dqs, dwt, rows, pages, cache, logits)
+    dsa.dsa_topk(logits, rows, 2048, idx, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), fused)              # same scores, same exact selection
+    ref_lg = orc.indexer_logits_mxfp4(q8, qs, wt, w.row_req, w.row_pos, w.page_table, host(cache))
+    ridx, kth = orc.topk(ref_lg, w.row_pos, 2048)
+    topk_sets_match(fused, ridx, ref_lg, kth)

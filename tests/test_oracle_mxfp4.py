@@ -165,3 +165,24 @@ def test_logits_mxfp4_invariants(orc):
 def test_mxfp4_bytes_per_token(orc):
     # 128/2 B of codes + 128/32 scale bytes = 68 B, about half of FP8's 132
     assert orc.IDX_MXFP4_PAGE_BYTES == 64 * (128 // 2 + 128 // 32) == 4352
+
+
+def test_mxfp4_topk_overlap_with_fp8(orc):
+    """Measurement, not a pin: the share of the FP8 cache's top-2048 that the MXFP4 cache keeps
+    on the decode-batch inputs (the page leaves the effect of the coarser keys on the top-k
+    open).  A loose floor only guards against a broken variant."""
+    from parity import LN_EPS, THETA, all_tokens, oracle_index_cache, queries, raw_k
+    w = gi.config(1, "small")
+    q, wt, _ = queries(w, [])
+    q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+    q8, qs = q8.reshape(w.R, 32, 128), qs.reshape(w.R, 32)
+    req, pos = all_tokens(w)
+    mx = np.zeros((w.num_pages, 64 * 68), np.uint8)
+    orc.index_k_store_mxfp4(raw_k(w), req, pos, w.page_table, mx, LN_EPS, THETA)
+    lg8 = orc.indexer_logits(q8, qs, wt, w.row_req, w.row_pos, w.page_table, oracle_index_cache(w))
+    lg4 = orc.indexer_logits_mxfp4(q8, qs, wt, w.row_req, w.row_pos, w.page_table, mx)
+    i8, _ = orc.topk(lg8, w.row_pos, 2048)
+    i4, _ = orc.topk(lg4, w.row_pos, 2048)
+    ov = [len(set(a[a >= 0]) & set(b[b >= 0])) / max(1, int((a >= 0).sum())) for a, b in zip(i8, i4)]
+    print(f"MXFP4 keeps {np.mean(ov):.3f} of the FP8 top-2048 on average (min {np.min(ov):.3f})")
+    assert np.mean(ov) > 0.5
