@@ -76,10 +76,11 @@ _TOPK_SRC = ["sparse_attention_store_amd/csrc/k_topk.hip", "sparse_attention_sto
              "sparse_attention_store_amd/csrc/dsa_internal.h"]
 # kernel name as rocprofv3 prints it, up to the opening parenthesis -> the sources it is built from
 KERNEL_SOURCES = {
-    "k_logits_decode<6, 0>": _IDX_SRC,    # dsa_indexer_logits: every score written
-    "k_logits_decode<6, 1>": _IDX_SRC,    # dsa_indexer_topk: sampled pages
-    "k_logits_decode<6, 2>": _IDX_SRC,    # dsa_indexer_topk: filter pass (candidates only)
-    "k_sparse_mla_stream": _MLA_SRC,      # sparse MLA, 256+ rows
+    "k_logits_decode<6, 0, 0>": _IDX_SRC,    # dsa_indexer_logits (FP8 keys): every score written
+    "k_logits_decode<6, 1, 0>": _IDX_SRC,    # dsa_indexer_topk: sampled pages
+    "k_logits_decode<6, 2, 0>": _IDX_SRC,    # dsa_indexer_topk: filter pass (candidates only)
+    "k_logits_decode<6, 0, 1>": _IDX_SRC,    # dsa_indexer_logits_mxfp4 (68-B keys)
+    "k_sparse_mla_stream": _MLA_SRC,         # sparse MLA, 256+ rows
     "k_filt_thresh": _TOPK_SRC,
     "k_filt_final": _TOPK_SRC,
 }
@@ -292,8 +293,8 @@ def main():
     mla_tflops = MLA_FLOPS_PER_ROW * R / (per["mla0"] * 1e-6) / 1e12
     mla_total = sum(per[f"mla{l}"] for l in D.layers)
     dominant = "logits"      # the metric's named kernel: index-K cache streaming
-    roof_idx = {"kernel": "k_logits_decode (dsa_indexer_logits)", "bound": "hbm", "achieved": round(idx_gbps, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("k_logits_decode<6, 0>"),
+    roof_idx = {"kernel": "k_logits_decode<6, 0, 0> (dsa_indexer_logits)", "bound": "hbm", "achieved": round(idx_gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("k_logits_decode<6, 0, 0>"),
                 "algorithmic_bytes_per_launch": ib, "avg_launch_us": round(per["logits"], 2)}
     roof_mla = {"kernel": "k_sparse_mla_stream (dsa_sparse_mla_decode)", "bound": "hbm", "achieved": round(mla_gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(mla_gbps / HBM_PEAK_GBPS, 4),
