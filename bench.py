@@ -283,6 +283,12 @@ def main():
                              for x, y in zip(a8, a4)]))
     mxb = indexer_bytes(w.ctx, w.R, key_bytes=68)
     del mx
+
+    # MTP draft iteration: 5 steps, one row per request, over layer 0's caches; with the top-k
+    # carry steps 1-4 reuse step 0's idx, without it every step scores and selects
+    n_mtp = max(3, a.steps // 4)
+    mtp_carry_us = timed(lambda: D.mtp_draft_round(carry=True, steps=5), n_mtp)
+    mtp_plain_us = timed(lambda: D.mtp_draft_round(carry=False, steps=5), n_mtp)
     R, nl = w.R, len(D.layers)
     full_us = per["store"] + per["quant"] + per["indexer_topk"] + per["mla0"]
     shared_us = float(np.mean([per[f"mla{l}"] for l in D.layers[1:]]))
@@ -329,6 +335,12 @@ def main():
             "indexer_topk_us": round(mx_topk_us, 2),
             "topk_overlap_with_fp8": round(overlap, 4),
             "full_layer_us": round(per["store"] + per["quant"] + mx_topk_us + per["mla0"], 2),
+        },
+        "mtp_draft_round": {
+            "about": "one MTP draft iteration: 5 steps x 64 rows (one per request), indexer + top-k + "
+                     "sparse MLA per step; the carry reuses step 0's top-k in steps 1-4",
+            "with_carry_us": round(mtp_carry_us, 2), "without_carry_us": round(mtp_plain_us, 2),
+            "indexer_read_bytes_saved": 4 * indexer_bytes(w.ctx, 0),
         },
     }
     if not a.no_cpu_baseline:

@@ -124,6 +124,19 @@ typedef struct {
  * §模型侧的另一道门:should_run_indexer). */
 int dsa_layer_is_shared(const dsa_layer_rule* rule, int32_t layer_id);
 
+/* MTP draft-step top-k carry ([IDXC] §优化三:MTP 迭代内复用 topk).  The draft steps of one
+ * MTP iteration reuse the top-k seed of its first step instead of scoring the MTP layer's own
+ * index-K cache again: step 0 runs dsa_indexer_topk, steps 1.. pass that idx tensor (the same
+ * device pointer, no copy) to dsa_sparse_mla_decode, as a shared layer does.  The saving is
+ * (steps - 1) x 132 L bytes of indexer reads per iteration.
+ * dsa_mtp_seed_width: the seed's width, index_topk + index_kpool - 1 (2048 with index_kpool
+ * 1); -1 if index_topk is not in [1, 2048] or index_kpool < 1.
+ * dsa_mtp_carry_allowed: 1 when the carry is valid, which needs a single draft chain
+ * (eagle_topk == 1: wider drafts reorder rows and the seed no longer lines up); 0 otherwise;
+ * -1 if eagle_topk < 1.  Host-only; no device work. */
+int32_t dsa_mtp_seed_width(int32_t index_topk, int32_t index_kpool);
+int dsa_mtp_carry_allowed(int32_t eagle_topk);
+
 /* ---------------------------------------------------------------- quantisation */
 
 /* Per-128-element block FP8 quantisation with a ue8m0 scale (the indexer query

@@ -296,6 +296,28 @@ def index_read_seconds(b: int, L: int, hbm_bytes_per_s: float, n_full: int = 21)
     return n_full * index_k_bytes_per_token() * b * L / hbm_bytes_per_s
 
 
+def mtp_seed_width(index_topk: int = 2048, index_kpool: int = 1) -> int:
+    """Width of the top-k seed an MTP draft iteration carries across its steps:
+    index_topk + index_kpool - 1 ([IDXC] §优化三:MTP 迭代内复用 topk)."""
+    return index_topk + index_kpool - 1
+
+
+def mtp_carry_allowed(eagle_topk: int) -> bool:
+    """The carry is valid only for a single draft chain ([IDXC] §优化三: top-k > 1 reorders rows)."""
+    return eagle_topk == 1
+
+
+def mtp_carry_saved_read_bytes(L: int, draft_steps: int = 5) -> int:
+    """Indexer-cache reads the carry saves per MTP iteration: all draft steps but the first skip
+    scoring the MTP layer's own cache ([IDXC] §优化三)."""
+    return (draft_steps - 1) * index_k_bytes_per_token() * L
+
+
+def mtp_carry_saved_fraction(draft_steps: int = 5, n_full: int = 21) -> float:
+    """The saving relative to the main model's indexer reads per step (n_full x 132 L)."""
+    return mtp_carry_saved_read_bytes(1, draft_steps) / read_bytes_per_step(1, n_full)
+
+
 def logits_bytes(R: int, L: int) -> int:
     return 4 * R * math.ceil(L / 256) * 256
 

@@ -71,6 +71,16 @@ int dsa_layer_is_shared(const dsa_layer_rule* rule, int32_t layer_id) {
   return (v > 0 ? v : 0) % rule->topk_freq != 0;
 }
 
+int32_t dsa_mtp_seed_width(int32_t index_topk, int32_t index_kpool) {
+  if (index_topk < 1 || index_topk > DSA_TOPK_MAX || index_kpool < 1) return -1;
+  return index_topk + index_kpool - 1;
+}
+
+int dsa_mtp_carry_allowed(int32_t eagle_topk) {
+  if (eagle_topk < 1) return -1;
+  return eagle_topk == 1;
+}
+
 dsa_status dsa_quant_fp8(const uint16_t* x, int64_t n_blocks, uint8_t* y, float* scale, void* stream) {
   if (n_blocks < 0) return fail(DSA_ERR_ARG, "dsa_quant_fp8: n_blocks < 0");
   if (n_blocks == 0) return DSA_OK;

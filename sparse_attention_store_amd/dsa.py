@@ -60,6 +60,8 @@ def _load():
         "dsa_abi_version": ([], ctypes.c_int),
         "dsa_last_error": ([], ctypes.c_char_p),
         "dsa_layer_is_shared": ([ctypes.POINTER(_Rule), i32], ctypes.c_int),
+        "dsa_mtp_seed_width": ([i32, i32], i32),
+        "dsa_mtp_carry_allowed": ([i32], ctypes.c_int),
         "dsa_quant_fp8": ([p, i64, p, p, p], ctypes.c_int),
         "dsa_index_k_store": ([p, R, P, p, f64, f64, p], ctypes.c_int),
         "dsa_index_k_store_mxfp4": ([p, R, P, p, f64, f64, p], ctypes.c_int),
@@ -85,7 +87,8 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("dsa_abi_version", "dsa_last_error", "dsa_layer_is_shared", "dsa_quant_fp8",
+EXPORTED = ("dsa_abi_version", "dsa_last_error", "dsa_layer_is_shared", "dsa_mtp_seed_width", "dsa_mtp_carry_allowed",
+            "dsa_quant_fp8",
             "dsa_index_k_store", "dsa_index_k_store_mxfp4", "dsa_latent_store", "dsa_logits_stride",
             "dsa_logits_rows_per_chunk", "dsa_indexer_logits", "dsa_indexer_logits_mxfp4", "dsa_topk_workspace_size",
             "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_mxfp4", "dsa_sparse_mla_workspace_size",
@@ -147,6 +150,14 @@ def dsa_layer_is_shared(layer_id: int, indexer_types: str | None = None, cli_fac
 
 def dsa_quant_fp8(x, y, scale, stream=None):
     _check(_lib.dsa_quant_fp8(_ptr(x), x.numel() // 128, _ptr(y), _ptr(scale), _stream(stream)))
+
+
+def dsa_mtp_seed_width(index_topk: int = 2048, index_kpool: int = 1) -> int:
+    return int(_lib.dsa_mtp_seed_width(index_topk, index_kpool))
+
+
+def dsa_mtp_carry_allowed(eagle_topk: int) -> int:
+    return int(_lib.dsa_mtp_carry_allowed(eagle_topk))
 
 
 def dsa_index_k_store(k, rows: Rows, pages: Pages, index_cache, ln_eps=1e-6, rope_theta=10000.0, stream=None):

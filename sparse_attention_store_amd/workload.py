@@ -152,6 +152,54 @@ class DeviceLayer:
         """A shared layer reuses the last full layer's top-k tensor as is (same device pointer)."""
         self.mla(layer)
 
+    # ------------------------------------------------------------------ MTP draft round
+    def _mtp_setup(self, steps: int):
+        """Per-step inputs of an MTP draft iteration: step s of request b is the request's row s
+        (position p_b + s) as a one-row-per-request batch, with that row's queries."""
+        m = getattr(self, "_mtp", None)
+        if m is not None and m["steps"] == steps:
+            return m
+        w, dev = self.w, self.device
+        g = w.rows_per_req
+        assert steps <= g, "a draft step per row of the request"
+        B = w.R // g
+        reqs = torch.arange(B, dtype=torch.int32, device=dev)
+        m = {"steps": steps, "B": B, "rows": [], "q_idx": [], "w": [], "q_mla": [], "out": [], "lse": [], "idx": []}
+        for st in range(steps):
+            sel = torch.arange(B, device=dev) * g + st
+            pos = self.rows.pos[sel].contiguous()
+            m["rows"].append(dsa.Rows(reqs, pos, int(w.row_pos.max()), 1))
+            m["q_idx"].append(self.q_idx[sel].contiguous())
+            m["w"].append(self.w_head[sel].contiguous())
+            m["q_mla"].append(self.q_mla[self.layers[0]][sel].contiguous())
+            m["out"].append(torch.empty((B, 64, 512), dtype=torch.int16, device=dev))
+            m["lse"].append(torch.empty((B, 64), dtype=torch.float32, device=dev))
+            m["idx"].append(torch.empty((B, TOPK), dtype=torch.int32, device=dev))
+        m["q8"] = torch.empty((B, 32, 128), dtype=torch.uint8, device=dev)
+        m["qs"] = torch.empty((B, 32), dtype=torch.float32, device=dev)
+        m["logits"] = torch.empty((B, self.stride), dtype=torch.float32, device=dev)
+        m["ws_topk"] = torch.empty(max(dsa.dsa_topk_workspace_size(B, self.stride, TOPK), 256), dtype=torch.uint8,
+                                   device=dev)
+        nm = dsa.dsa_sparse_mla_workspace_size(B, TOPK)
+        m["ws_mla"] = torch.empty(max(nm, 256), dtype=torch.uint8, device=dev) if nm else None
+        self._mtp = m
+        return m
+
+    def mtp_draft_round(self, carry: bool = True, steps: int = 5, layer: int = 0):
+        """One MTP draft iteration over `layer`'s caches (standing in for the MTP layer's own):
+        step 0 scores and selects; with the carry, steps 1.. reuse step 0's idx tensor as is
+        (the same device pointer); without it, every step scores and selects again."""
+        m = self._mtp_setup(steps)
+        for st in range(steps):
+            idx = m["idx"][0 if carry else st]
+            if st == 0 or not carry:
+                dsa.dsa_quant_fp8(m["q_idx"][st], m["q8"], m["qs"])
+                dsa.dsa_indexer_topk(m["q8"], m["qs"], m["w"][st], m["rows"][st], self.pages, self.index_cache[layer],
+                                     m["logits"], TOPK, idx, m["ws_topk"])
+            dsa.dsa_sparse_mla_decode(m["q_mla"][st], m["rows"][st], self.pages, self.latent_cache[layer], idx,
+                                      m["out"][st], m["lse"][st], m["ws_mla"], SM_SCALE)
+        return m
+
     def group_step(self):
         for l in self.layers:
             if l in self.w.full_layers:

@@ -31,6 +31,16 @@ def test_exports_every_declared_symbol(lib):
     assert lib.abi_version() == 1
 
 
+def test_mtp_carry_helpers_match_oracle(lib, orc):
+    for topk, kpool in [(2048, 1), (2048, 4), (8, 1), (1, 1)]:
+        assert lib.dsa_mtp_seed_width(topk, kpool) == orc.mtp_seed_width(topk, kpool)
+    assert lib.dsa_mtp_seed_width(0, 1) == -1 and lib.dsa_mtp_seed_width(4096, 1) == -1
+    assert lib.dsa_mtp_seed_width(2048, 0) == -1
+    for t in (1, 2, 4):
+        assert lib.dsa_mtp_carry_allowed(t) == int(orc.mtp_carry_allowed(t))
+    assert lib.dsa_mtp_carry_allowed(0) == -1
+
+
 def test_layer_rule_matches_oracle(lib, orc):
     for kw in [dict(topk_freq=4, skip_topk_offset=3), dict(topk_freq=4), dict(cli_factor=3),
                dict(topk_pattern="FSSFSF"), dict(indexer_types="FFFSSSF")]:

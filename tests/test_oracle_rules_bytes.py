@@ -78,6 +78,15 @@ def test_bytes_against_pages(orc):
     _close("mtp_layer_read_1M", orc.read_bytes_per_full_layer(10 ** 6))
     _close("mxfp4_index_bytes_per_token", 128 // 2 + 128 // 32)
     _close("mla_flops_per_token_layer", 2 * 64 * 512 * 2048)
+    _close("mtp_seed_width", orc.mtp_seed_width(2048, 1))
+    _close("mtp_saved_read_per_132L", orc.mtp_carry_saved_read_bytes(1000) / (132 * 1000))
+    _close("mtp_saved_fraction", orc.mtp_carry_saved_fraction())
+
+
+def test_mtp_carry_rule(orc):
+    # only a single draft chain may carry the seed; a kpool > 1 widens it by the tail slots
+    assert orc.mtp_carry_allowed(1) and not orc.mtp_carry_allowed(2) and not orc.mtp_carry_allowed(4)
+    assert orc.mtp_seed_width(2048, 4) == 2051
 
 
 def test_rows_per_chunk_rule(orc):
