@@ -59,6 +59,7 @@ def lib():
             "orc_quant_fp8": [p, i64, p, p],
             "orc_index_k_store": [p, p, p, i64, p, i64, p, d, d, p],
             "orc_latent_store": [p, p, p, i64, p, i64, p],
+            "orc_fused_norm_rope_store": [p, i64, p, p, p, p, i64, p, i64, p, p, p, i64, i64, d, d, d, d],
             "orc_indexer_logits": [p, p, p, p, p, i64, p, i64, p, p, i64],
             "orc_topk": [p, i64, p, i64, i32, p, p],
             "orc_sparse_mla": [p, p, p, i64, p, i64, p, p, i32, d, p, p],
@@ -189,6 +190,35 @@ def latent_store(kv_bf16, req, pos, page_table, cache):
     assert cache.dtype == np.uint8 and cache.flags.c_contiguous and cache.shape[-1] == LAT_PAGE_BYTES
     lib().orc_latent_store(kv.ctypes.data, req.ctypes.data, pos.ctypes.data, kv.shape[0],
                            pt.ctypes.data, pt.shape[1], cache.ctypes.data)
+
+
+def fused_norm_rope_store(kv_bf16, req, pos, page_table, latent_cache, index_cache=None, k_idx=None,
+                          gamma=None, q=None, q_off=0, rms_eps=1e-6, ln_eps=1e-6, theta=10000.0,
+                          index_theta=10000.0, kv_off=0):
+    """RMSNorm(kv[:, o:o+512]) * gamma and RoPE(kv[:, o+512:o+576]) (o = ``kv_off``) into the
+    656-B records of ``latent_cache``; the index-K entries of ``k_idx`` into ``index_cache``
+    when both are given; ``q`` (uint16 [n, 64, W], C-contiguous, nullable) has its 64 rope dims
+    per head at ``q_off`` rotated in place.  ``kv_bf16`` is [n, S] (S is the row stride)."""
+    kv = _c(kv_bf16, np.uint16)
+    assert kv.ndim == 2 and 0 <= kv_off and kv_off + 576 <= kv.shape[1]
+    n = kv.shape[0]
+    req, pos, pt = _c(req, np.int32), _c(pos, np.int32), _c(page_table, np.int32)
+    assert latent_cache.dtype == np.uint8 and latent_cache.flags.c_contiguous
+    assert latent_cache.shape[-1] == LAT_PAGE_BYTES
+    g = None if gamma is None else _c(gamma, np.uint16)
+    ki = None if k_idx is None else _c(k_idx, np.uint16).reshape(-1, 128)
+    if index_cache is not None:
+        assert index_cache.dtype == np.uint8 and index_cache.flags.c_contiguous
+        assert index_cache.shape[-1] == IDX_PAGE_BYTES
+    qp, qrs, qhs = None, 0, 0
+    if q is not None:
+        assert q.dtype == np.uint16 and q.flags.c_contiguous and q.shape[:2] == (n, 64)
+        assert 0 <= q_off and q_off + 64 <= q.shape[2]
+        qp = q.ctypes.data + 2 * q_off
+        qrs, qhs = 64 * q.shape[2], q.shape[2]
+    lib().orc_fused_norm_rope_store(kv.ctypes.data + 2 * kv_off, kv.shape[1], _ptr(g), _ptr(ki), req.ctypes.data,
+                                    pos.ctypes.data, n, pt.ctypes.data, pt.shape[1], latent_cache.ctypes.data,
+                                    _ptr(index_cache), qp, qrs, qhs, rms_eps, ln_eps, theta, index_theta)
 
 
 def logits_stride(max_pos: int) -> int:

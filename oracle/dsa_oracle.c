@@ -179,6 +179,21 @@ static int64_t page_of(const int32_t* pt, int64_t pt_stride, int32_t req, int64_
     return (int64_t)pt[(int64_t)req * pt_stride + p / PAGE];
 }
 
+/* One token's index-K entry: LN, RoPE at p, ue8m0 + fp8 into its page slot. */
+static void index_k_entry(const uint16_t* k_row, int32_t r, int64_t p, const int32_t* page_table,
+                          int64_t pt_stride, uint8_t* cache, double eps, double theta, double* pre) {
+    double x[IDX_DIM], y[IDX_DIM];
+    uint8_t* base;
+    int d;
+    float s;
+    for (d = 0; d < IDX_DIM; d++) x[d] = orc_bf16_to_double(k_row[d]);
+    orc_layernorm128(x, y, eps);
+    orc_rope64(y, p, theta, 0);
+    base = cache + page_of(page_table, pt_stride, r, p) * IDX_PAGE_B;
+    s = quant_block(y, base + (p % PAGE) * IDX_DIM, pre);
+    memcpy(base + IDX_SCALE_OFF + (p % PAGE) * 4, &s, 4);
+}
+
 void orc_index_k_store(const uint16_t* k_bf16, const int32_t* req, const int32_t* pos, int64_t n,
                        const int32_t* page_table, int64_t pt_stride,
                        uint8_t* cache, double eps, double theta, double* pre_quant) {
@@ -186,19 +201,9 @@ void orc_index_k_store(const uint16_t* k_bf16, const int32_t* req, const int32_t
     if (!cache) return;                    /* shared layer: no index-K of its own */
 #pragma omp parallel for schedule(static)
     for (t = 0; t < n; t++) {
-        double x[IDX_DIM], y[IDX_DIM];
-        int64_t p = pos[t], page;
-        uint8_t* base;
-        int d;
-        float s;
-        if (p < 0) continue;               /* padded row: nothing written */
-        for (d = 0; d < IDX_DIM; d++) x[d] = orc_bf16_to_double(k_bf16[t * IDX_DIM + d]);
-        orc_layernorm128(x, y, eps);
-        orc_rope64(y, p, theta, 0);
-        page = page_of(page_table, pt_stride, req[t], p);
-        base = cache + page * IDX_PAGE_B;
-        s = quant_block(y, base + (p % PAGE) * IDX_DIM, pre_quant ? pre_quant + t * IDX_DIM : NULL);
-        memcpy(base + IDX_SCALE_OFF + (p % PAGE) * 4, &s, 4);
+        if (pos[t] < 0) continue;          /* padded row: nothing written */
+        index_k_entry(k_bf16 + t * IDX_DIM, req[t], pos[t], page_table, pt_stride, cache, eps, theta,
+                      pre_quant ? pre_quant + t * IDX_DIM : NULL);
     }
 }
 
@@ -219,6 +224,63 @@ void orc_latent_store(const uint16_t* kv_bf16, const int32_t* req, const int32_t
             memcpy(rec + LAT_DIM + 4 * b, &s, 4);
         }
         memcpy(rec + LAT_DIM + 16, kv_bf16 + t * 576 + LAT_DIM, ROPE_DIM * 2);  /* rope tail stays bf16 */
+    }
+}
+
+/* ------------------------------------------------------------------ fused norm + RoPE + cache writes
+ * The step after the KV A projection ([VLLM] §KV 低秩投影与缓存; [REQ] §4.3 两个 RMSNorm 与
+ * RoPE, the fused_norm_rope kernel with its has_indexer switch), per token at position p:
+ *   c^ = c / sqrt(mean(c^2) + eps) * gamma      over the 512 latent dims (RMSNorm as in
+ *                                              [VLLM] §RMSNorm 与残差路径; gamma = 1 if NULL)
+ *   k~ = RoPE_p(k_R)                            over the 64 rope dims (interleaved pairs)
+ * c^ goes into the 656-B record as four ue8m0-scaled fp8 blocks, rounded once from double;
+ * k~ is rounded once to bf16 into the record's tail.  With an index-K cache (a layer that
+ * runs its own indexer) the token's index key is stored exactly as orc_index_k_store does;
+ * q_pe (NULL to skip) holds the token's 64 per-head 64-dim rope parts, rotated in place with
+ * the same angles as k~.  Padded tokens (p < 0) are left alone. */
+void orc_fused_norm_rope_store(const uint16_t* kv, int64_t kv_stride, const uint16_t* gamma,
+                               const uint16_t* k_idx, const int32_t* req, const int32_t* pos, int64_t n,
+                               const int32_t* page_table, int64_t pt_stride, uint8_t* latent_cache,
+                               uint8_t* index_cache, uint16_t* q_pe, int64_t q_row_stride,
+                               int64_t q_head_stride, double rms_eps, double ln_eps, double rope_theta,
+                               double index_rope_theta) {
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < n; t++) {
+        double c[LAT_DIM], kr[ROPE_DIM], ms = 0.0, rms;
+        int64_t p = pos[t];
+        const uint16_t* src = kv + t * kv_stride;
+        uint8_t* rec;
+        int b, d, h;
+        if (p < 0) continue;
+        for (d = 0; d < LAT_DIM; d++) {
+            c[d] = orc_bf16_to_double(src[d]);
+            ms += c[d] * c[d];
+        }
+        rms = sqrt(ms / LAT_DIM + rms_eps);
+        for (d = 0; d < LAT_DIM; d++) c[d] = c[d] / rms * (gamma ? orc_bf16_to_double(gamma[d]) : 1.0);
+        rec = latent_cache + page_of(page_table, pt_stride, req[t], p) * LAT_PAGE_B + (p % PAGE) * LAT_REC_B;
+        for (b = 0; b < 4; b++) {
+            float s = quant_block(c + 128 * b, rec + 128 * b, NULL);
+            memcpy(rec + LAT_DIM + 4 * b, &s, 4);
+        }
+        for (d = 0; d < ROPE_DIM; d++) kr[d] = orc_bf16_to_double(src[LAT_DIM + d]);
+        orc_rope64(kr, p, rope_theta, 0);
+        for (d = 0; d < ROPE_DIM; d++) {
+            uint16_t hb = orc_double_to_bf16(kr[d]);
+            memcpy(rec + LAT_DIM + 16 + 2 * d, &hb, 2);
+        }
+        if (index_cache && k_idx)
+            index_k_entry(k_idx + t * IDX_DIM, req[t], p, page_table, pt_stride, index_cache, ln_eps,
+                          index_rope_theta, NULL);
+        if (q_pe)
+            for (h = 0; h < MLA_HEADS; h++) {
+                uint16_t* q = q_pe + t * q_row_stride + h * q_head_stride;
+                double v[ROPE_DIM];
+                for (d = 0; d < ROPE_DIM; d++) v[d] = orc_bf16_to_double(q[d]);
+                orc_rope64(v, p, rope_theta, 0);
+                for (d = 0; d < ROPE_DIM; d++) q[d] = orc_double_to_bf16(v[d]);
+            }
     }
 }
 

@@ -65,6 +65,16 @@ void orc_index_k_store(const uint16_t* k_bf16, const int32_t* req, const int32_t
                        const int32_t* page_table, int64_t pt_stride,
                        uint8_t* cache, double eps, double theta, double* pre_quant);
 
+/* Fused norm + RoPE + cache writes: RMSNorm(kv[0:512]) * gamma -> 4 scaled fp8 blocks,
+ * RoPE(kv[512:576]) -> bf16 tail of the 656-B record; the index-K entry when index_cache and
+ * k_idx are given; q_pe (nullable) rotated in place, 64 heads x 64 dims per token. */
+void orc_fused_norm_rope_store(const uint16_t* kv, int64_t kv_stride, const uint16_t* gamma,
+                               const uint16_t* k_idx, const int32_t* req, const int32_t* pos, int64_t n,
+                               const int32_t* page_table, int64_t pt_stride, uint8_t* latent_cache,
+                               uint8_t* index_cache, uint16_t* q_pe, int64_t q_row_stride,
+                               int64_t q_head_stride, double rms_eps, double ln_eps, double rope_theta,
+                               double index_rope_theta);
+
 /* Latent store: 576 bf16 -> 656-B record (4 scaled fp8 blocks + bf16 rope tail). */
 void orc_latent_store(const uint16_t* kv_bf16, const int32_t* req, const int32_t* pos, int64_t n,
                       const int32_t* page_table, int64_t pt_stride, uint8_t* cache);
