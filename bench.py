@@ -72,6 +72,8 @@ def measured_traffic(kernel):
 _IDX_SRC = ["sparse_attention_store_amd/csrc/k_indexer.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp",
             "sparse_attention_store_amd/csrc/dsa_internal.h"]
 _MLA_SRC = ["sparse_attention_store_amd/csrc/k_mla.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp"]
+_STORE_SRC = ["sparse_attention_store_amd/csrc/k_store.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp",
+              "sparse_attention_store_amd/csrc/dsa_internal.h"]
 _TOPK_SRC = ["sparse_attention_store_amd/csrc/k_topk.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp",
              "sparse_attention_store_amd/csrc/dsa_internal.h"]
 # kernel name as rocprofv3 prints it, up to the opening parenthesis -> the sources it is built from
@@ -83,7 +85,11 @@ KERNEL_SOURCES = {
     "k_sparse_mla_stream": _MLA_SRC,         # sparse MLA, 256+ rows
     "k_filt_thresh": _TOPK_SRC,
     "k_filt_final": _TOPK_SRC,
+    "k_fused_norm_rope_store": _STORE_SRC,   # fused norm + RoPE + dual write, 8192-token prefill chunk
 }
+# per token of the fused store: kv latent + k_pe (576 bf16), index key (128 bf16), 64 query rope
+# parts read and written (64 x 64 bf16 each way), the 656-B record, the 132-B index entry, req + pos
+FUSED_STORE_BYTES_PER_TOKEN = 576 * 2 + 128 * 2 + 2 * 64 * 64 * 2 + 656 + 132 + 8
 
 
 def write_traffic(fetch_csv, write_csv, command):
@@ -109,8 +115,9 @@ def write_traffic(fetch_csv, write_csv, command):
     gib_kib = float(1 << 20)
     copy_f = max(v for name, vs in fetch.items() if "copyBuffer" in name for v in vs)
     copy_w = max(v for name, vs in write.items() if "copyBuffer" in name for v in vs)
-    out = {"about": "HBM traffic per dispatch of the c2 verify workload (64 x 6 rows at 128K), from rocprofv3 "
-                    "--pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, median over dispatches); factors make a "
+    out = {"about": "HBM traffic per dispatch of the benchmark's kernels, from rocprofv3 --pmc FETCH_SIZE and "
+                    "WRITE_SIZE (KiB per dispatch, median over dispatches): the c2 verify workload (64 x 6 rows at "
+                    "128K), and k_fused_norm_rope_store on the 8192-token chunked-prefill chunk; factors make a "
                     "1 GiB device copy read and write 1 GiB",
            "command": command, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
            "fetch_factor": gib_kib / copy_f, "write_factor": gib_kib / copy_w, "kernels": {}}
@@ -265,14 +272,24 @@ def main():
     mx = D.build_mxfp4_index(0)
 
     def timed(fn, n):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        """Microseconds per call of `fn`, run n times back to back.  A spin kernel queued first
+        keeps the device busy while the host enqueues the n calls, so host-side call overhead
+        does not show as idle time inside the timed span."""
         fn()
-        for e0, e1 in ev:
-            e0.record(stream)
-            fn()
-            e1.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+        h0 = time.perf_counter()
+        for _ in range(3):
+            fn()
+        host_us = (time.perf_counter() - h0) / 3 * 1e6
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(min(2.0 * n * host_us + 200.0, 5e5) * 2000))     # ~2 GHz shader clock
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
 
     mx_logits_us = timed(lambda: dsa.dsa_indexer_logits_mxfp4(D.q8, D.qs, D.w_head, D.rows, D.pages, mx, D.logits),
                          a.steps)
@@ -289,6 +306,30 @@ def main():
     n_mtp = max(3, a.steps // 4)
     mtp_carry_us = timed(lambda: D.mtp_draft_round(carry=True, steps=5), n_mtp)
     mtp_plain_us = timed(lambda: D.mtp_draft_round(carry=False, steps=5), n_mtp)
+    # fused norm + RoPE + dual-cache write on the chunked-prefill chunk (8192 new tokens on a
+    # 65,536-token prefix), a layer with its own indexer, query rope parts rotated in place
+    fw = gi.config(4)
+    nf, cs = fw.R, stream.cuda_stream
+    fkv = torch.empty((nf, gi.KV_A_WIDTH), dtype=torch.int16, device="cuda")
+    fg = torch.empty(512, dtype=torch.int16, device="cuda")
+    fk = torch.empty((nf, 128), dtype=torch.int16, device="cuda")
+    fq = torch.empty((nf, 64, 576), dtype=torch.int16, device="cuda")
+    for t_id, buf in ((gi.T_KV_A, fkv), (gi.T_GAMMA, fg), (gi.T_RAW_K, fk), (gi.T_MLA_Q, fq)):
+        gi.dev_normal_bf16(fw.seed, t_id, 0, buf.numel(), buf.data_ptr(), cs)
+    flat = torch.zeros((fw.num_pages, 41984), dtype=torch.uint8, device="cuda")
+    fidx = torch.zeros((fw.num_pages, 8448), dtype=torch.uint8, device="cuda")
+    frows = dsa.Rows(torch.from_numpy(fw.row_req).cuda(), torch.from_numpy(fw.row_pos).cuda(),
+                     int(fw.row_pos.max()), 1)
+    fpages = dsa.Pages(torch.from_numpy(fw.page_table).cuda(), fw.num_pages)
+    fkv_c = fkv[:, 2048:].contiguous()
+    fused_us = timed(lambda: dsa.dsa_fused_norm_rope_store(fkv[:, 2048:], frows, fpages, flat, index_cache=fidx,
+                                                           k_idx=fk, gamma=fg, q_pe=fq[:, :, 512:]), a.steps)
+    sep_us = timed(lambda: (dsa.dsa_latent_store(fkv_c, frows, fpages, flat),
+                            dsa.dsa_index_k_store(fk, frows, fpages, fidx, 1e-6, 10000.0)), a.steps)
+    fused_b = FUSED_STORE_BYTES_PER_TOKEN * nf + 512 * 2
+    fused_gbps = fused_b / (fused_us * 1e-6) / 1e9
+    del fkv, fq, flat, fidx, fkv_c
+
     R, nl = w.R, len(D.layers)
     full_us = per["store"] + per["quant"] + per["indexer_topk"] + per["mla0"]
     shared_us = float(np.mean([per[f"mla{l}"] for l in D.layers[1:]]))
@@ -341,6 +382,15 @@ def main():
                      "sparse MLA per step; the carry reuses step 0's top-k in steps 1-4",
             "with_carry_us": round(mtp_carry_us, 2), "without_carry_us": round(mtp_plain_us, 2),
             "indexer_read_bytes_saved": 4 * indexer_bytes(w.ctx, 0),
+        },
+        "fused_norm_rope_store": {
+            "about": "RMSNorm + RoPE + 656-B latent record + 132-B index-K entry + in-place query rope "
+                     "rotation for the 8192-token chunk of the chunked prefill (65,536-token prefix)",
+            "kernel": "k_fused_norm_rope_store", "us": round(fused_us, 2),
+            "algorithmic_bytes_per_launch": fused_b, "GBps": round(fused_gbps, 1),
+            "frac_of_peak": round(fused_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic("k_fused_norm_rope_store"),
+            "separate_latent_and_index_stores_us": round(sep_us, 2),
         },
     }
     if not a.no_cpu_baseline:

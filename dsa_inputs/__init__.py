@@ -40,6 +40,9 @@ DEV_LIB = os.path.join(HERE, "libdsa_gen_dev.so")
 
 SEED_BASE = 0x5EED0000
 T_IDX_Q, T_RAW_K, T_W, T_MLA_Q, T_LATENT0, T_PERM, T_CTX, T_NEEDLE = 1, 2, 3, 4, 5, 9, 10, 11
+# A projection output rows [q_c 2048 | kv_c 512 | k_pe 64] and the kv_a RMSNorm weight
+T_KV_A, T_GAMMA = 12, 13
+KV_A_WIDTH = 2048 + 576
 PAGE = 64
 
 

@@ -175,6 +175,36 @@ dsa_status dsa_index_k_store_mxfp4(const uint16_t* k_bf16, const dsa_rows* tok, 
 dsa_status dsa_latent_store(const uint16_t* kv_bf16, const dsa_rows* tok, const dsa_pages* pt,
                             uint8_t* latent_cache, void* stream);
 
+/* Fused norm + RoPE + dual-cache write: the step after the KV A projection, one pass per
+ * token ([VLLM] §KV 低秩投影与缓存: RMSNorm of the 512-dim KV latent and RoPE of the 64-dim
+ * rope key are what the main cache holds; [REQ] §4.3 两个 RMSNorm 与 RoPE: fused_norm_rope also
+ * rotates the query's rope part and, with has_indexer, writes the indexer key too).
+ * For each token with pos >= 0, in double precision:
+ *   c^ = c / sqrt(mean(c^2) + rms_eps) * gamma over the 512 latent dims (kv[0..511]);
+ *   k~ = RoPE_pos(kv[512..575]) (interleaved pairs, angle pos * rope_theta^(-i/32));
+ * the token's 656-B record gets c^ as four ue8m0-scaled fp8 blocks (one rounding from double)
+ * and k~ rounded once to bf16.  With index_cache (a layer that runs its own indexer) the
+ * token's index key k_idx is stored exactly as dsa_index_k_store stores it (ln_eps,
+ * index_rope_theta).  With q_pe, the token's 64 query heads have their 64 rope dims rotated in
+ * place with the same angles as k~ (one rounding to bf16).
+ *   kv:           device bf16, row t at kv + t * kv_stride (kv_stride >= 576, multiple of 8;
+ *                 e.g. the latent columns of the A projection's output row).
+ *   gamma:        device bf16 [512], or NULL for gamma = 1.
+ *   k_idx:        device bf16 [tok->n][128]; required when index_cache is given, else unused.
+ *   latent_cache: device [pt->num_pages][41984].
+ *   index_cache:  device [pt->num_pages][8448], or NULL (no indexer of its own: no index write).
+ *   q_pe:         device bf16, head h of token t at q_pe + t * q_row_stride + h * q_head_stride
+ *                 (64 contiguous dims; strides multiples of 8, q_head_stride >= 64 and heads of
+ *                 different tokens not overlapping), or NULL.  Rewritten in place.
+ * Pointers are 16-B aligned.  Padded tokens (pos < 0) are left alone everywhere, their q
+ * included.  Argument errors: DSA_ERR_ARG (NULL latent_cache or kv, index_cache without
+ * k_idx, bad strides or alignment, eps < 0 or theta <= 0). */
+dsa_status dsa_fused_norm_rope_store(const uint16_t* kv, int64_t kv_stride, const uint16_t* gamma,
+                                     const uint16_t* k_idx, const dsa_rows* tok, const dsa_pages* pt,
+                                     uint8_t* latent_cache, uint8_t* index_cache, uint16_t* q_pe,
+                                     int64_t q_row_stride, int64_t q_head_stride, double rms_eps, double ln_eps,
+                                     double rope_theta, double index_rope_theta, void* stream);
+
 /* ---------------------------------------------------------------- indexer */
 
 /* Logits row stride: (max_pos + 1) rounded up to 256 elements ([IDXC]

@@ -128,6 +128,39 @@ dsa_status dsa_latent_store(const uint16_t* kv, const dsa_rows* tok, const dsa_p
   return hip_status(dsa::launch_latent_store(kv, view(tok), view(pt), cache, (hipStream_t)stream), "dsa_latent_store");
 }
 
+dsa_status dsa_fused_norm_rope_store(const uint16_t* kv, int64_t kv_stride, const uint16_t* gamma,
+                                     const uint16_t* k_idx, const dsa_rows* tok, const dsa_pages* pt,
+                                     uint8_t* latent_cache, uint8_t* index_cache, uint16_t* q_pe,
+                                     int64_t q_row_stride, int64_t q_head_stride, double rms_eps, double ln_eps,
+                                     double rope_theta, double index_rope_theta, void* stream) {
+  const char* name = "dsa_fused_norm_rope_store";
+  dsa_status st = check_rows(tok, name, false);
+  if (st) return st;
+  if ((st = check_pages(pt, tok->max_pos, name))) return st;
+  if (!latent_cache) return fail(DSA_ERR_ARG, "%s: latent_cache is NULL", name);
+  if (tok->n > 0 && !kv) return fail(DSA_ERR_ARG, "%s: kv is NULL", name);
+  if (index_cache && tok->n > 0 && !k_idx) return fail(DSA_ERR_ARG, "%s: index_cache given without k_idx", name);
+  if (kv_stride < DSA_LATENT_DIM || kv_stride % 8) return fail(DSA_ERR_ARG, "%s: kv_stride must be >= 576 and a multiple of 8", name);
+  if (!aligned(kv, 16) || !aligned(gamma, 16) || !aligned(latent_cache, 16) ||
+      (index_cache && (!aligned(k_idx, 16) || !aligned(index_cache, 16))))
+    return fail(DSA_ERR_ARG, "%s: misaligned pointer", name);
+  if (q_pe) {
+    if (!aligned(q_pe, 16) || q_head_stride < 64 || q_head_stride % 8 || q_row_stride % 8 ||
+        q_row_stride < 63 * q_head_stride + 64)
+      return fail(DSA_ERR_ARG, "%s: q_pe must be 16-B aligned with head stride >= 64, rows not overlapping, "
+                  "strides multiples of 8", name);
+  }
+  if (!(rms_eps >= 0.0) || !(ln_eps >= 0.0) || !(rope_theta > 0.0) || !(index_rope_theta > 0.0))
+    return fail(DSA_ERR_ARG, "%s: bad eps/theta", name);
+  dsa::FusedStoreParams f{kv, kv_stride, gamma, index_cache ? k_idx : nullptr, latent_cache, index_cache,
+                          q_pe, q_row_stride, q_head_stride, rms_eps, ln_eps, {}, {}};
+  for (int i = 0; i < 32; i++) {
+    f.inv_freq[i] = pow(rope_theta, -(2.0 * i) / 64.0);
+    f.index_inv_freq[i] = pow(index_rope_theta, -(2.0 * i) / 64.0);
+  }
+  return hip_status(dsa::launch_fused_norm_rope_store(f, view(tok), view(pt), (hipStream_t)stream), name);
+}
+
 int64_t dsa_logits_stride(int32_t max_pos) {
   if (max_pos < 0) return 256;
   return ((int64_t)max_pos + 1 + 255) / 256 * 256;

@@ -26,6 +26,22 @@ hipError_t launch_latent_store(const uint16_t* kv, RowsView tok, PagesView pg, u
 hipError_t launch_index_k_store_mxfp4(const uint16_t* k, RowsView tok, PagesView pg, uint8_t* cache,
                                       double eps, const double* inv_freq32, hipStream_t s);
 
+// Fused norm + RoPE + cache writes: arguments as the C entry point validated them, plus the two
+// inverse-frequency tables evaluated on the host.
+struct FusedStoreParams {
+  const uint16_t* kv;
+  int64_t kv_stride;
+  const uint16_t* gamma;
+  const uint16_t* k_idx;
+  uint8_t* latent_cache;
+  uint8_t* index_cache;
+  uint16_t* q_pe;
+  int64_t q_row_stride, q_head_stride;
+  double rms_eps, ln_eps;
+  double inv_freq[32], index_inv_freq[32];
+};
+hipError_t launch_fused_norm_rope_store(const FusedStoreParams& f, RowsView tok, PagesView pg, hipStream_t s);
+
 // Index-K cache formats: FP8 (132 B per token) and MXFP4 (68 B per token).
 enum { kIdxFp8 = 0, kIdxMxfp4 = 1 };
 

@@ -9,6 +9,12 @@
 //                    section 4.5 on the interleaved indexer RoPE).
 //  * latent_store:   576 bf16 -> 656-B record: 4 scaled fp8 blocks + bf16 rope tail
 //                    ("GLM-5.3 推理全链路(十一)", section on the main KV cache).
+//  * fused_norm_rope_store: the step after the KV A projection in one pass per token:
+//                    RMSNorm of the 512-dim latent (times gamma) and RoPE of k_pe into the
+//                    656-B record, the index-K entry when the layer runs its own indexer, and
+//                    the query's rope parts rotated in place ("vLLM 推理链路概览", section on
+//                    the KV low-rank projection and cache; "GLM-5.3 推理全链路(一)", section
+//                    4.3 on fused_norm_rope and has_indexer).
 //
 // These writers are off the per-step critical path (a decode step stores one token
 // per request); they are written for exactness first.  16 lanes own one 128-element
@@ -205,7 +211,254 @@ __global__ void __launch_bounds__(256) k_latent_store(const uint16_t* __restrict
         *reinterpret_cast<const uint4*>(src + kVal + lane * 8);
 }
 
+// fp64 -> bf16 bits with one rounding (RNE): round to odd into fp32 (16 more bits than bf16,
+// so the second rounding cannot land on a false tie), then RNE on the fp32 bits.
+__device__ inline uint32_t bf16_from_f64_rne(double v) {
+  const float f = (float)v;
+  uint32_t b = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != v) {
+    if (fabs(back) > fabs(v)) b -= 1;   // truncate toward zero (f != 0 here)
+    b |= 1;                              // sticky
+  }
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Rotates the interleaved pairs (x[2j], x[2j+1]) by the angles whose cosines and sines are
+// c[j], s[j] (fused multiply-adds: within an ulp of double of the unfused expressions).
+__device__ inline void rotate4(double* x, const double* c, const double* s) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const double a = x[2 * j], b = x[2 * j + 1];
+    x[2 * j] = a * c[j] - b * s[j];
+    x[2 * j + 1] = a * s[j] + b * c[j];
+  }
+}
+
+// Eight doubles (|v| <= 448) -> eight e4m3 codes, each rounded once to nearest even.  As for
+// bf16: the hardware rounds to fp32 and then to e4m3, which is one rounding unless an fp32
+// value sits exactly on an e4m3 midpoint (low 20 bits 0x80000 in the normal range) or in the
+// e4m3 subnormal range (below 2^-6); lanes with such a value round from the double's bits.
+__device__ inline uint2 fp8x8_from_f64(const double* x) {
+  float f[8];
+  bool slow = false;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    f[i] = (float)x[i];
+    slow |= (__float_as_uint(f[i]) & 0xFFFFFu) == 0x80000u || fabsf(f[i]) < 0x1p-6f;
+  }
+  uint2 out;
+  if (__builtin_expect(slow, 0)) {
+    out.x = out.y = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      out.x |= fp8_from_f64_rne(x[i]) << (8 * i);
+      out.y |= fp8_from_f64_rne(x[4 + i]) << (8 * i);
+    }
+  } else {
+    out.x = pack4_fp8(f[0], f[1], f[2], f[3]);
+    out.y = pack4_fp8(f[4], f[5], f[6], f[7]);
+  }
+  return out;
+}
+
+// ue8m0 exponent from a positive fp64 amax: the smallest e with amax <= 448 * 2^e.
+__device__ inline int ue8m0_exponent_d(double amax) {
+  if (!(amax > 0.0)) return 0;
+  const uint64_t b = (uint64_t)__double_as_longlong(amax);
+  const int E = (int)(b >> 52) - 1023;
+  return E - 8 + ((b & ((1ULL << 52) - 1)) > (3ULL << 50) ? 1 : 0);
+}
+
+struct FusedStoreArgs {
+  const uint16_t* kv;        // [n][kv_stride]; latent at 0..511, k_pe at 512..575
+  int64_t kv_stride;
+  const uint16_t* gamma;     // [512] or null (1)
+  const uint16_t* k_idx;     // [n][128]; used when idx is not null
+  const int32_t* req;
+  const int32_t* pos;
+  int32_t n;
+  uint8_t* lat;
+  uint8_t* idx;              // null: no index-K entry (a layer without its own indexer)
+  uint16_t* q_pe;            // null, or head h of token t at q_pe + t*q_row + h*q_head
+  int64_t q_row, q_head;
+  double rms_eps, ln_eps;
+};
+
+__device__ inline void unpack8_bf16(const uint4& u, double* x) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    x[2 * i] = (double)__uint_as_float(w[i] << 16);
+    x[2 * i + 1] = (double)__uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// Eight doubles -> eight bf16, each rounded once to nearest even.  The hardware rounds to fp32
+// and then to bf16; the pair rounds as one step unless the fp32 value sits exactly on a bf16
+// midpoint (low 16 bits 0x8000): only then can the first rounding have made the tie, and the
+// lane redoes its eight values with the one-step rounding.
+__device__ inline uint4 pack8_bf16_rne(const double* x) {
+  float f[8];
+  bool tie = false;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    f[i] = (float)x[i];
+    tie |= (uint16_t)__float_as_uint(f[i]) == 0x8000u;
+  }
+  uint32_t o[4];
+  if (__builtin_expect(tie, 0)) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) o[i] = bf16_from_f64_rne(x[2 * i]) | (bf16_from_f64_rne(x[2 * i + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){f[2 * i], f[2 * i + 1]}, bf16x2));
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// One wave per token (four per work-group).  Lane l owns latent dims 8l..8l+7 (a 16-lane group
+// per fp8 block); lanes 0..7 own the 64 rope dims; lanes 0..15 own the index key; lane l rotates
+// dims 8m..8m+7 (m = l mod 8) of query heads 8k + l/8.  Every load of the token is issued first
+// (none depends on its position), so their latency overlaps the position lookup and the angles.
+// The 32 main and 32 index RoPE angles are evaluated once, in double, by lanes 0..31 and 32..63;
+// each lane fetches the four of each it needs by shuffle.
+__global__ void __launch_bounds__(256, 4) k_fused_norm_rope_store(FusedStoreArgs a, DevPages pg, InvFreq fm,
+                                                               InvFreq fi) {
+  // the wave index is uniform: position and page-table reads become scalar loads, which do
+  // not wait behind the vector loads below
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 7;
+  if (t >= a.n) return;                 // whole waves exit together
+
+  const double freq = lane < 32 ? fm.v[lane & 31] : fi.v[lane & 31];   // issued first: needed first
+  const uint16_t* src = a.kv + t * a.kv_stride;
+  const uint4 kv_u = *reinterpret_cast<const uint4*>(src + lane * 8);
+  const uint4 kpe_u = *reinterpret_cast<const uint4*>(src + kVal + m * 8);
+  // optional operands are loaded unconditionally (from the token's own kv row when absent) so
+  // every path has the same loads in flight and the waits below stay partial
+  const uint4 g_u = *reinterpret_cast<const uint4*>((a.gamma ? a.gamma : src) + lane * 8);
+  const uint4 ki_u =
+      *reinterpret_cast<const uint4*>((a.idx ? a.k_idx + t * kIdxDim : src) + (lane & 15) * 8);
+  uint16_t* qt = a.q_pe ? a.q_pe + t * a.q_row + m * 8 : nullptr;
+  const int64_t qh = a.q_pe ? a.q_head : 0;
+  const uint16_t* qsrc = a.q_pe ? qt : src + m * 8;
+  uint4 qv[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) qv[k] = *reinterpret_cast<const uint4*>(qsrc + (8 * k + (lane >> 3)) * qh);
+
+  const int64_t p = a.pos[t];
+  if (p < 0) return;                    // padded token: nothing stored, q left alone
+  const int64_t page = page_of(pg, a.req[t], p);
+  if (page < 0) return;
+
+  double ang_s, ang_c;
+  sincos((double)p * freq, &ang_s, &ang_c);
+
+  // latent: RMSNorm over 512 dims in double, times gamma, then four ue8m0-scaled fp8 blocks
+  double x[8], g[8], sq = 0.0;
+  unpack8_bf16(kv_u, x);
+  unpack8_bf16(g_u, g);
+#pragma unroll
+  for (int i = 0; i < 8; i++) sq += x[i] * x[i];
+  const double rinv = 1.0 / sqrt(group_sum_d<64>(sq) / 512.0 + a.rms_eps);
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    x[i] = x[i] * rinv * (a.gamma ? g[i] : 1.0);
+    amax = fmax(amax, fabs(x[i]));
+  }
+  const int e = ue8m0_exponent_d(group_max_d<16>(amax));
+  const double sinv = __builtin_ldexp(1.0, -e);
+#pragma unroll
+  for (int i = 0; i < 8; i++) x[i] *= sinv;            // exact: a power of two
+  uint8_t* rec = a.lat + page * kLatPageBytes + (p & 63) * kRecBytes;
+  *reinterpret_cast<uint2*>(rec + lane * 8) = fp8x8_from_f64(x);
+  if ((lane & 15) == 0) *reinterpret_cast<float*>(rec + kRecScaleOff + (lane >> 4) * 4) = __builtin_ldexpf(1.0f, e);
+
+  // index-K entry: LayerNorm, RoPE on dims 0..63, ue8m0 + fp8.  All four 16-lane groups
+  // compute the key (the group reductions need every lane); group 0 stores it.
+  if (a.idx) {
+    const int l16 = lane & 15;
+    double y[8], sum = 0.0;
+    unpack8_bf16(ki_u, y);
+#pragma unroll
+    for (int i = 0; i < 8; i++) sum += y[i];
+    const double mu = group_sum_d<16>(sum) / 128.0;
+    double s2 = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) { y[i] -= mu; s2 += y[i] * y[i]; }
+    const double inv = 1.0 / sqrt(group_sum_d<16>(s2) / 128.0 + a.ln_eps);
+#pragma unroll
+    for (int i = 0; i < 8; i++) y[i] *= inv;
+    double ci[4], si[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      ci[j] = __shfl(ang_c, 32 + 4 * m + j, 64);
+      si[j] = __shfl(ang_s, 32 + 4 * m + j, 64);
+    }
+    if (l16 < 8) rotate4(y, ci, si);
+    double am = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) am = fmax(am, fabs(y[i]));
+    const int ek = ue8m0_exponent_d(group_max_d<16>(am));
+    const double kinv = __builtin_ldexp(1.0, -ek);
+#pragma unroll
+    for (int i = 0; i < 8; i++) y[i] *= kinv;
+    const uint2 kc = fp8x8_from_f64(y);
+    if (lane < 16) {
+      uint8_t* base = a.idx + page * kIdxPageBytes;
+      *reinterpret_cast<uint2*>(base + (p & 63) * kIdxDim + l16 * 8) = kc;
+      if (l16 == 0) *reinterpret_cast<float*>(base + kIdxScaleOff + (p & 63) * 4) = __builtin_ldexpf(1.0f, ek);
+    }
+  }
+
+  // main RoPE angles for dims 8m..8m+7, shared by k_pe and the query heads
+  double cm[4], sm[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    cm[j] = __shfl(ang_c, 4 * m + j, 64);
+    sm[j] = __shfl(ang_s, 4 * m + j, 64);
+  }
+
+  // k_pe: RoPE in double, one rounding to bf16 (lanes 0..7 store)
+  if (lane < 8) {
+    double r[8];
+    unpack8_bf16(kpe_u, r);
+    rotate4(r, cm, sm);
+    *reinterpret_cast<uint4*>(rec + kRecRopeOff + lane * 16) = pack8_bf16_rne(r);
+  }
+
+  // query rope parts, rotated in place
+  if (qt) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      double r[8];
+      unpack8_bf16(qv[k], r);
+      rotate4(r, cm, sm);
+      *reinterpret_cast<uint4*>(qt + (8 * k + (lane >> 3)) * a.q_head) = pack8_bf16_rne(r);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fused_norm_rope_store(const FusedStoreParams& f, RowsView tok, PagesView pg, hipStream_t s) {
+  if (tok.n <= 0) return hipSuccess;
+  InvFreq fm, fi;
+  for (int i = 0; i < 32; i++) {
+    fm.v[i] = f.inv_freq[i];
+    fi.v[i] = f.index_inv_freq[i];
+  }
+  FusedStoreArgs a{f.kv, f.kv_stride, f.gamma, f.k_idx, tok.req, tok.pos, tok.n, f.latent_cache, f.index_cache,
+                   f.q_pe, f.q_row_stride, f.q_head_stride, f.rms_eps, f.ln_eps};
+  DevPages g{pg.pt, pg.pt_stride, pg.num_reqs, pg.num_pages};
+  const int64_t grid = ((int64_t)tok.n + 3) / 4;
+  hipLaunchKernelGGL(k_fused_norm_rope_store, dim3((unsigned)grid), dim3(256), 0, s, a, g, fm, fi);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n_blocks, uint8_t* y, float* scale, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;

@@ -66,6 +66,7 @@ def _load():
         "dsa_index_k_store": ([p, R, P, p, f64, f64, p], ctypes.c_int),
         "dsa_index_k_store_mxfp4": ([p, R, P, p, f64, f64, p], ctypes.c_int),
         "dsa_latent_store": ([p, R, P, p, p], ctypes.c_int),
+        "dsa_fused_norm_rope_store": ([p, i64, p, p, R, P, p, p, p, i64, i64, f64, f64, f64, f64, p], ctypes.c_int),
         "dsa_logits_stride": ([i32], i64),
         "dsa_logits_rows_per_chunk": ([i64, i64, i64], i64),
         "dsa_indexer_logits": ([p, p, p, R, P, p, p, i64, p], ctypes.c_int),
@@ -89,7 +90,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("dsa_abi_version", "dsa_last_error", "dsa_layer_is_shared", "dsa_mtp_seed_width", "dsa_mtp_carry_allowed",
             "dsa_quant_fp8",
-            "dsa_index_k_store", "dsa_index_k_store_mxfp4", "dsa_latent_store", "dsa_logits_stride",
+            "dsa_index_k_store", "dsa_index_k_store_mxfp4", "dsa_latent_store", "dsa_fused_norm_rope_store", "dsa_logits_stride",
             "dsa_logits_rows_per_chunk", "dsa_indexer_logits", "dsa_indexer_logits_mxfp4", "dsa_topk_workspace_size",
             "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_mxfp4", "dsa_sparse_mla_workspace_size",
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_check_device_errors")
@@ -176,6 +177,24 @@ def dsa_index_k_store_mxfp4(k, rows: Rows, pages: Pages, index_cache, ln_eps=1e-
 def dsa_latent_store(kv, rows: Rows, pages: Pages, latent_cache, stream=None):
     r, p = rows.c(), pages.c()
     _check(_lib.dsa_latent_store(_ptr(kv), ctypes.byref(r), ctypes.byref(p), _ptr(latent_cache), _stream(stream)))
+
+
+def dsa_fused_norm_rope_store(kv, rows: Rows, pages: Pages, latent_cache, index_cache=None, k_idx=None, gamma=None,
+                              q_pe=None, rms_eps=1e-6, ln_eps=1e-6, rope_theta=10000.0, index_rope_theta=10000.0,
+                              stream=None):
+    """kv: bf16 (int16) [n, >=576] view with unit column stride (its row stride is passed);
+    q_pe: None or a [n, 64, 64] view with unit last stride (e.g. q[:, :, 512:]), rotated in place."""
+    r, p = rows.c(), pages.c()
+    if kv.dim() != 2 or kv.stride(1) != 1:
+        raise ValueError("kv must be a 2-D view with unit column stride")
+    qrs = qhs = 0
+    if q_pe is not None:
+        if q_pe.dim() != 3 or q_pe.shape[1:] != (64, 64) or q_pe.stride(2) != 1:
+            raise ValueError("q_pe must be a [n, 64, 64] view with unit last stride")
+        qrs, qhs = q_pe.stride(0), q_pe.stride(1)
+    _check(_lib.dsa_fused_norm_rope_store(_ptr(kv), kv.stride(0), _ptr(gamma), _ptr(k_idx), ctypes.byref(r),
+                                          ctypes.byref(p), _ptr(latent_cache), _ptr(index_cache), _ptr(q_pe), qrs,
+                                          qhs, rms_eps, ln_eps, rope_theta, index_rope_theta, _stream(stream)))
 
 
 def dsa_logits_stride(max_pos: int) -> int:

@@ -67,10 +67,19 @@ def _expect(lib, status, fn, *a, **k):
 
 class _Fake:
     """Stands in for a device tensor in calls that fail validation before any launch."""
-    def __init__(self, ptr, shape=(1,), itemsize=1):
+    def __init__(self, ptr, shape=(1,), itemsize=1, strides=None):
         self.ptr, self.shape, self._n, self._is = ptr, shape, 1, itemsize
         for s in shape:
             self._n *= s
+        if strides is None:
+            strides = tuple(int(__import__("math").prod(shape[i + 1:])) for i in range(len(shape)))
+        self._st = strides
+
+    def dim(self):
+        return len(self.shape)
+
+    def stride(self, i):
+        return self._st[i]
 
     def data_ptr(self):
         return self.ptr
@@ -114,6 +123,21 @@ def test_argument_errors(lib):
     # bad sm_scale
     _expect(lib, 1, lib.dsa_sparse_mla_decode, _Fake(0x9000), rows, pt, _Fake(0xA000), idx, _Fake(0xB000),
             sm_scale=0.0)
+    # fused norm + RoPE + dual write
+    kv = _Fake(0x9000, (4, 576), 2)
+    fused = lib.dsa_fused_norm_rope_store
+    _expect(lib, 1, fused, kv, rows, pt, None)                                   # no latent cache
+    _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000), index_cache=_Fake(0xE000))  # index without k_idx
+    _expect(lib, 1, fused, _Fake(0x9000, (4, 520), 2), rows, pt, _Fake(0xA000))      # row stride < 576
+    _expect(lib, 1, fused, _Fake(0x9000, (4, 576), 2, (580, 1)), rows, pt, _Fake(0xA000))  # stride % 8
+    _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000), gamma=_Fake(0xF008))       # misaligned gamma
+    q_ok = (64 * 576, 576, 1)
+    _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000), q_pe=_Fake(0x10008 + 1024, (4, 64, 64), 2, q_ok))
+    _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000),
+            q_pe=_Fake(0x10000, (4, 64, 64), 2, (60 * 576, 576, 1)))                # rows overlap
+    _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000), q_pe=_Fake(0x10000, (4, 64, 64), 2, (64 * 48, 48, 1)))
+    _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000), rms_eps=-1.0)
+    _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000), index_rope_theta=0.0)
     # a shared layer (no index-K cache) makes store and logits a successful no-op
     lib.dsa_index_k_store(_Fake(0x9000), rows, pt, None)
     lib.dsa_indexer_logits(_Fake(0x7000), _Fake(0x7100), _Fake(0x7200), rows, pt, None, logits)
