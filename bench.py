@@ -89,6 +89,7 @@ KERNEL_SOURCES = {
 }
 # per token of the fused store: kv latent + k_pe (576 bf16), index key (128 bf16), 64 query rope
 # parts read and written (64 x 64 bf16 each way), the 656-B record, the 132-B index entry, req + pos
+PREFILL_LOGITS_BUDGET = 4 << 30   # logits scratch per indexer launch in the chunked prefill
 FUSED_STORE_BYTES_PER_TOKEN = 576 * 2 + 128 * 2 + 2 * 64 * 64 * 2 + 656 + 132 + 8
 
 
@@ -330,6 +331,41 @@ def main():
     fused_gbps = fused_b / (fused_us * 1e-6) / 1e9
     del fkv, fq, flat, fidx, fkv_c
 
+    # one 1,048,576-token prompt prefilled in 32 chunks of 32,768 rows over one full layer's
+    # caches: per chunk the store of its index keys, q quantisation, the indexer + top-2048 in
+    # row chunks (4 GiB of logits scratch per launch) and the sparse MLA over its rows
+    pw = gi.config(5)
+    n_chunk_rows = pw.extra["chunk"]
+    pbase, cp = None, []
+    for c in range((pw.R + n_chunk_rows - 1) // n_chunk_rows):
+        wc = gi.prefill_chunk(pw, c)
+        Lc = DeviceLayer(wc, latent_layers=[0], logits_budget_bytes=PREFILL_LOGITS_BUDGET, caches_from=pbase)
+        pbase = pbase or Lc
+        if c == 0:
+            Lc.full_layer(0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        dsa.dsa_index_k_store(Lc.k_new, Lc.rows, Lc.pages, Lc.index_cache[0], 1e-6, 10000.0)
+        dsa.dsa_quant_fp8(Lc.q_idx, Lc.q8, Lc.qs)
+        ev[1].record(stream)
+        Lc.indexer_topk(0)
+        ev[2].record(stream)
+        Lc.mla(0)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        cp.append([ev[i].elapsed_time(ev[i + 1]) for i in range(3)])
+        if Lc is not pbase:
+            del Lc
+    del pbase
+    torch.cuda.empty_cache()
+    cp = np.array(cp)                                           # ms: store + quant, indexer + top-k, MLA
+    ppos = pw.row_pos.astype(np.int64)
+    score_flops = int(((ppos + 1) * (ppos + 1 > 2048)).sum()) * 32 * 128 * 2
+    mla_flops = int(np.minimum(ppos + 1, 2048).sum()) * 2 * 64 * (576 + 512)
+    idx_s, mla_s = cp[:, 1].sum() / 1e3, cp[:, 2].sum() / 1e3
+    print(f"[bench] chunked prefill 1M: {len(cp)} chunks, layer {cp.sum():.1f} ms", file=sys.stderr, flush=True)
+
     R, nl = w.R, len(D.layers)
     full_us = per["store"] + per["quant"] + per["indexer_topk"] + per["mla0"]
     shared_us = float(np.mean([per[f"mla{l}"] for l in D.layers[1:]]))
@@ -382,6 +418,20 @@ def main():
                      "sparse MLA per step; the carry reuses step 0's top-k in steps 1-4",
             "with_carry_us": round(mtp_carry_us, 2), "without_carry_us": round(mtp_plain_us, 2),
             "indexer_read_bytes_saved": 4 * indexer_bytes(w.ctx, 0),
+        },
+        "chunked_prefill_1m": {
+            "about": "one 1,048,576-token prompt prefilled in 32 chunks of 32,768 rows, one full layer: store + "
+                     "q quantisation, indexer + top-2048 in row chunks (4 GiB logits scratch per launch), sparse "
+                     "MLA; the indexer's scoring FLOPs are the rows' visible keys x 32 heads x 128 dims x 2",
+            "chunks": int(len(cp)), "chunk_rows": int(n_chunk_rows), "logits_budget_bytes": PREFILL_LOGITS_BUDGET,
+            "layer_ms": round(float(cp.sum()), 2), "store_quant_ms": round(float(cp[:, 0].sum()), 2),
+            "indexer_topk_ms": round(float(cp[:, 1].sum()), 2), "sparse_mla_ms": round(float(cp[:, 2].sum()), 2),
+            "indexer_scoring_flops": score_flops,
+            "indexer_TFLOPs": round(score_flops / idx_s / 1e12, 1),
+            "indexer_frac_of_fp8_peak": round(score_flops / idx_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "mla_flops": mla_flops, "mla_TFLOPs": round(mla_flops / mla_s / 1e12, 1),
+            "mla_frac_of_bf16_peak": round(mla_flops / mla_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "chunk_ms_first_middle_last": [round(float(cp[i].sum()), 2) for i in (0, len(cp) // 2, len(cp) - 1)],
         },
         "fused_norm_rope_store": {
             "about": "RMSNorm + RoPE + 656-B latent record + 132-B index-K entry + in-place query rope "

@@ -30,7 +30,7 @@ import ctypes
 import math
 import os
 import subprocess
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -207,6 +207,16 @@ class Workload:
     def max_pos(self) -> int:
         return int(self.row_pos.max())
 
+    @property
+    def row0(self) -> int:
+        """Index of this batch's first query row among all rows of its workload (a chunk of a
+        chunked prefill starts past the earlier chunks' rows); seeded query offsets use it."""
+        return int(self.extra.get("row0", 0))
+
+    @property
+    def rows_total(self) -> int:
+        return int(self.extra.get("rows_total", self.R))
+
 
 def _page_table(seed: int, ctx: np.ndarray, spare_pages: int = 0):
     npg = (ctx + PAGE - 1) // PAGE
@@ -240,6 +250,16 @@ def make_prefill(name: str, seed: int, prefix: int, new: int) -> Workload:
                     extra={"prefix": prefix})
 
 
+def prefill_chunk(w: Workload, c: int) -> Workload:
+    """Chunk c of a chunked prefill (``w.extra["chunk"]`` rows each): the same request, page
+    table and caches, with the chunk's rows as the batch."""
+    n = int(w.extra["chunk"])
+    a, b = c * n, min(w.R, (c + 1) * n)
+    assert 0 <= a < b
+    return replace(w, name=f"{w.name}[chunk {c}]", row_req=w.row_req[a:b], row_pos=w.row_pos[a:b],
+                   rows_per_req=b - a, extra={**w.extra, "row0": a, "rows_total": w.R, "chunk_index": c})
+
+
 def config(cid: int, scale: str = "full") -> Workload:
     """The pages' five workload shapes.  scale="small" shrinks them for fast parity runs
     while keeping several tiles, ragged tails and the multi-row / multi-layer structure."""
@@ -264,6 +284,11 @@ def config(cid: int, scale: str = "full") -> Workload:
     if cid == 4:     # chunked prefill: 8192 new rows on a 65,536-token prefix
         prefix, new = (3000, 70) if small else (65536, 8192)
         return make_prefill("c4_chunked_prefill", seed, prefix, new)
+    if cid == 5:     # a whole 1M-token prompt prefilled in 32K-token chunks (prefill_chunk())
+        total, chunk = (9000, 3100) if small else (1 << 20, 32768)
+        w = make_prefill("c5_chunked_prefill_1m", seed, 0, total)
+        w.extra["chunk"] = chunk
+        return w
     raise ValueError(cid)
 
 

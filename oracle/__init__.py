@@ -348,6 +348,22 @@ def mtp_carry_saved_fraction(draft_steps: int = 5, n_full: int = 21) -> float:
     return mtp_carry_saved_read_bytes(1, draft_steps) / read_bytes_per_step(1, n_full)
 
 
+def chunked_prefill_indexer_read_bytes(L: int = 1 << 20, rows_per_read: int = 32, n_full: int = 21) -> int:
+    """Index-K bytes the prefill of an L-token prompt reads when each block of `rows_per_read`
+    consecutive query rows reads the keys visible to its last row once, 132 B per token, per
+    full layer.  The page's 1M prefill figure ([IDXC], the cross-layer section: about 47 TB,
+    a simplified per-layer whole-segment accounting) is this sum with 32-row blocks; a kernel
+    that reads the cache once per 32K-row chunk reads `rows_per_read` = 32768's worth."""
+    n = (L + rows_per_read - 1) // rows_per_read
+    return n_full * index_k_bytes_per_token() * sum(min(L, (b + 1) * rows_per_read) for b in range(n))
+
+
+def chunked_prefill_indexer_flops(L: int = 1 << 20, n_full: int = 21, heads: int = 32, dim: int = 128) -> int:
+    """Indexer scoring work of an L-token prefill: row i scores its i + 1 visible keys with
+    `heads` dot products of `dim` dims (2 flops per multiply-add), per full layer."""
+    return n_full * heads * dim * 2 * L * (L + 1) // 2
+
+
 def logits_bytes(R: int, L: int) -> int:
     return 4 * R * math.ceil(L / 256) * 256
 

@@ -332,11 +332,40 @@ hipError_t launch_kind(const uint8_t* q8, const float* qs, const float* w, RowsV
   }
 }
 
+// The same mode with its per-row arrays advanced by `r0` rows.
+LogitsMode shift_rows(const LogitsMode& md, int64_t r0) {
+  LogitsMode m = md;
+  if (m.range) m.range += 2 * r0;
+  if (m.thr) m.thr += r0;
+  if (m.fcnt) m.fcnt += r0;
+  if (m.fkey) m.fkey += r0 * m.fcap;
+  if (m.fpos) m.fpos += r0 * m.fcap;
+  if (m.flag) m.flag += r0;
+  return m;
+}
+
 template <int FMT>
 hipError_t launch_fmt(const uint8_t* q8, const float* qs, const float* w, RowsView rows, PagesView pg,
                       const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md, hipStream_t s) {
   if (rows.n <= 0) return hipSuccess;
   DevPages g{pg.pt, pg.pt_stride, pg.num_reqs, pg.num_pages};
+  // one request's long group (a prefill chunk) whose length six does not divide: its first
+  // 6 * floor(n / 6) rows go in sub-groups of six and the last one to five rows in a second
+  // launch; sub-groups of the largest divisor could shrink to one row, which re-reads every
+  // key once per row
+  if (rows.group == rows.n && rows.n > 6 && rows.n % 6 != 0) {
+    const int32_t head = rows.n - rows.n % 6;
+    RowsView a = rows, b = rows;
+    a.n = a.group = head;
+    b.req += head;
+    b.pos += head;
+    b.n = b.group = rows.n - head;
+    const hipError_t e = launch_kind<6, FMT>(q8, qs, w, a, g, cache, logits, stride, md, s);
+    if (e != hipSuccess) return e;
+    return launch_fmt<FMT>(q8 + (int64_t)head * kIdxHeads * kIdxDim, qs + (int64_t)head * kIdxHeads,
+                           w + (int64_t)head * kIdxHeads, b, pg, cache, logits + (int64_t)head * stride, stride,
+                           shift_rows(md, head), s);
+  }
   // rows of a group are processed in sub-groups of the largest divisor of `group` <= 6
   // (the q operands of six rows fill the register file without spilling)
   int rg = 1;

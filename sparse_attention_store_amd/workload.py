@@ -33,7 +33,8 @@ def _runs(req: np.ndarray, pos: np.ndarray):
 
 class DeviceLayer:
     def __init__(self, w: gi.Workload, device="cuda", latent_layers=None, k_overrides=None,
-                 populate_chunk_tokens: int = 1 << 18):
+                 populate_chunk_tokens: int = 1 << 18, logits_budget_bytes: int | None = None,
+                 caches_from: "DeviceLayer | None" = None):
         self.w = w
         self.device = device
         self.seed = w.seed
@@ -44,30 +45,60 @@ class DeviceLayer:
         self.rows = dsa.Rows(torch.from_numpy(w.row_req).to(device), torch.from_numpy(w.row_pos).to(device),
                              w.max_pos, w.rows_per_req)
         self.layers = list(range(w.n_layers)) if latent_layers is None else list(latent_layers)
-        self.index_cache = {l: torch.zeros((w.num_pages, dsa.INDEX_PAGE_BYTES), dtype=torch.uint8, device=device)
-                            for l in w.full_layers}
-        self.latent_cache = {l: torch.zeros((w.num_pages, dsa.LATENT_PAGE_BYTES), dtype=torch.uint8, device=device)
-                             for l in self.layers}
         self._chunk = populate_chunk_tokens
-        self.populate()
-        # per-step inputs
+        if caches_from is not None:
+            # another batch of the same request(s): same page table and caches, no re-population
+            self.pages = caches_from.pages
+            self.index_cache, self.latent_cache = caches_from.index_cache, caches_from.latent_cache
+        else:
+            self.index_cache = {l: torch.zeros((w.num_pages, dsa.INDEX_PAGE_BYTES), dtype=torch.uint8, device=device)
+                                for l in w.full_layers}
+            self.latent_cache = {l: torch.zeros((w.num_pages, dsa.LATENT_PAGE_BYTES), dtype=torch.uint8,
+                                                device=device) for l in self.layers}
+            self.populate()
+        # per-step inputs (seeded by the rows' index in the whole workload)
+        r0, rt = w.row0, w.rows_total
         self.k_new = self._gen_token_rows(gi.T_RAW_K, 128, w.row_req, w.row_pos, override=True)
-        self.q_idx = self._gen(gi.T_IDX_Q, 0, R * 32 * 128).view(R, 32, 128)
+        self.q_idx = self._gen(gi.T_IDX_Q, r0 * 32 * 128, R * 32 * 128).view(R, 32, 128)
         self.w_head = torch.empty((R, 32), dtype=torch.float32, device=device)
-        gi.dev_uniform_f32(self.seed, gi.T_W, 0, R * 32, gi.w_scale(), self.w_head.data_ptr(), self._stream())
-        self.q_mla = {l: self._gen(gi.T_MLA_Q, l * R * 64 * 576, R * 64 * 576).view(R, 64, 576) for l in self.layers}
+        gi.dev_uniform_f32(self.seed, gi.T_W, r0 * 32, R * 32, gi.w_scale(), self.w_head.data_ptr(), self._stream())
+        self.q_mla = {l: self._gen(gi.T_MLA_Q, (l * rt + r0) * 64 * 576, R * 64 * 576).view(R, 64, 576)
+                      for l in self.layers}
         # outputs and workspaces
         self.stride = dsa.dsa_logits_stride(w.max_pos)
+        self._plan_row_chunks(logits_budget_bytes)
         self.q8 = torch.empty((R, 32, 128), dtype=torch.uint8, device=device)
         self.qs = torch.empty((R, 32), dtype=torch.float32, device=device)
-        self.logits = torch.empty((R, self.stride), dtype=torch.float32, device=device)
+        self.logits = torch.empty((self.rows_per_chunk, self.stride), dtype=torch.float32, device=device)
         self.idx = torch.empty((R, TOPK), dtype=torch.int32, device=device)
         self.out = {l: torch.empty((R, 64, 512), dtype=torch.int16, device=device) for l in self.layers}
         self.lse = {l: torch.empty((R, 64), dtype=torch.float32, device=device) for l in self.layers}
-        nt = dsa.dsa_topk_workspace_size(R, self.stride, TOPK)
+        nt = dsa.dsa_topk_workspace_size(self.rows_per_chunk, self.stride, TOPK)
         self.ws_topk = torch.empty(max(nt, 256), dtype=torch.uint8, device=device)
         nm = dsa.dsa_sparse_mla_workspace_size(R, TOPK)
         self.ws_mla = torch.empty(max(nm, 256), dtype=torch.uint8, device=device) if nm else None
+
+    def _plan_row_chunks(self, budget):
+        """Row chunks for the indexer when R x stride fp32 logits exceed `budget` bytes
+        ("GLM-5.3 推理全链路(十一)", section on the logits temporary: rows_per_chunk =
+        budget // row_bytes).  Chunks hold whole request groups, or lie inside one request."""
+        w, R = self.w, self.w.R
+        rpc = dsa.dsa_logits_rows_per_chunk(R, self.stride * 4, budget) if budget else 0
+        if not rpc:
+            self.rows_per_chunk, self.row_chunks = R, None
+            return
+        g = w.rows_per_req
+        if g <= rpc:
+            rpc -= rpc % g
+        else:
+            assert w.B == 1, "a chunk inside a request group needs a single request"
+        self.rows_per_chunk = rpc
+        self.row_chunks = []
+        for a in range(0, R, rpc):
+            b = min(R, a + rpc)
+            rows = dsa.Rows(self.rows.req[a:b], self.rows.pos[a:b], int(w.row_pos[a:b].max()),
+                            g if g <= rpc else b - a)
+            self.row_chunks.append((a, b, rows))
 
     # ------------------------------------------------------------------ generation
     def _stream(self):
@@ -140,8 +171,13 @@ class DeviceLayer:
         self.mla(layer)
 
     def indexer_topk(self, layer: int = 0):
-        dsa.dsa_indexer_topk(self.q8, self.qs, self.w_head, self.rows, self.pages, self.index_cache[layer],
-                             self.logits, TOPK, self.idx, self.ws_topk)
+        if self.row_chunks is None:
+            dsa.dsa_indexer_topk(self.q8, self.qs, self.w_head, self.rows, self.pages, self.index_cache[layer],
+                                 self.logits, TOPK, self.idx, self.ws_topk)
+            return
+        for a, b, rows in self.row_chunks:
+            dsa.dsa_indexer_topk(self.q8[a:b], self.qs[a:b], self.w_head[a:b], rows, self.pages,
+                                 self.index_cache[layer], self.logits[:b - a], TOPK, self.idx[a:b], self.ws_topk)
 
     def mla(self, layer: int):
         fn = dsa.dsa_sparse_mla_prefill if self.w.rows_per_req > 64 else dsa.dsa_sparse_mla_decode

@@ -49,10 +49,11 @@ def oracle_latent_cache(w: gi.Workload, layer: int):
 
 
 def queries(w: gi.Workload, layers):
-    R = w.R
-    q = gi.normal_bf16(w.seed, gi.T_IDX_Q, 0, R * 32 * 128).reshape(R, 32, 128)
-    wt = gi.uniform_f32(w.seed, gi.T_W, 0, R * 32, gi.w_scale()).reshape(R, 32)
-    qm = {l: gi.normal_bf16(w.seed, gi.T_MLA_Q, l * R * 64 * 576, R * 64 * 576).reshape(R, 64, 576) for l in layers}
+    R, r0, rt = w.R, w.row0, w.rows_total
+    q = gi.normal_bf16(w.seed, gi.T_IDX_Q, r0 * 32 * 128, R * 32 * 128).reshape(R, 32, 128)
+    wt = gi.uniform_f32(w.seed, gi.T_W, r0 * 32, R * 32, gi.w_scale()).reshape(R, 32)
+    qm = {l: gi.normal_bf16(w.seed, gi.T_MLA_Q, (l * rt + r0) * 64 * 576, R * 64 * 576).reshape(R, 64, 576)
+          for l in layers}
     return q, wt, qm
 
 
@@ -155,9 +156,9 @@ def oracle_latent_cache_of(w: gi.Workload, b: int, layer: int, positions):
 
 def row_queries(w: gi.Workload, rows, layers):
     """Indexer q, head weights and MLA q of the given rows only (same values as queries())."""
-    rows = [int(r) for r in rows]
+    rows = [w.row0 + int(r) for r in rows]
     q = np.stack([gi.normal_bf16(w.seed, gi.T_IDX_Q, r * 32 * 128, 32 * 128) for r in rows]).reshape(-1, 32, 128)
     wt = np.stack([gi.uniform_f32(w.seed, gi.T_W, r * 32, 32, gi.w_scale()) for r in rows])
-    qm = {l: np.stack([gi.normal_bf16(w.seed, gi.T_MLA_Q, (l * w.R + r) * 64 * 576, 64 * 576)
+    qm = {l: np.stack([gi.normal_bf16(w.seed, gi.T_MLA_Q, (l * w.rows_total + r) * 64 * 576, 64 * 576)
                        for r in rows]).reshape(-1, 64, 576) for l in layers}
     return q, wt, qm

@@ -83,6 +83,22 @@ def test_bytes_against_pages(orc):
     _close("mtp_saved_fraction", orc.mtp_carry_saved_fraction())
 
 
+def test_chunked_prefill_accounting(orc):
+    # the page's 1M prefill figures: ~47 TB of index-K reads and ~94 PFLOP of scoring (21 layers)
+    _close("prefill_1m_indexer_read_bytes", orc.chunked_prefill_indexer_read_bytes())
+    _close("prefill_1m_indexer_flops", orc.chunked_prefill_indexer_flops())
+    # brute force on a tiny prompt: rows 0..L-1 each score i + 1 keys; blocks read their prefix
+    L, block = 10, 4
+    assert orc.chunked_prefill_indexer_flops(L, 1, 1, 1) == 2 * sum(i + 1 for i in range(L))
+    assert orc.chunked_prefill_indexer_read_bytes(L, block, 1) == 132 * (4 + 8 + 10)
+    # the reads grow with the square of the prompt: twice the blocks, about four times the bytes
+    r1 = orc.chunked_prefill_indexer_read_bytes(1 << 20, 32768, 1)
+    r2 = orc.chunked_prefill_indexer_read_bytes(1 << 21, 32768, 1)
+    assert 3.9 < r2 / r1 < 4.0
+    # one read per 32K chunk: 48 GB over 21 layers, a thousandth of the 32-row accounting
+    assert orc.chunked_prefill_indexer_read_bytes(1 << 20, 32768) == 21 * 132 * 32768 * 528
+
+
 def test_mtp_carry_rule(orc):
     # only a single draft chain may carry the seed; a kpool > 1 widens it by the tail slots
     assert orc.mtp_carry_allowed(1) and not orc.mtp_carry_allowed(2) and not orc.mtp_carry_allowed(4)
