@@ -40,8 +40,13 @@ namespace dsa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kStageAll = 768;          // filter mode: candidates held per work-group (all rows)
-constexpr int kQRow = kIdxDim + 16;     // q row pitch in LDS (padding spreads LDS banks)
+constexpr int kLongGroupRG = 8;         // rows per sub-group of a prefill chunk's long group
+// filter mode: candidates held per row and work-group (sized so that four work-groups of
+// eight rows fit a CU's LDS: 32 KiB of q + 1 KiB of weights + 8 x 104 x 8 B of candidates)
+template <int RG> constexpr int kStage = RG <= 6 ? 768 / RG : 104;
+// q rows are 128 B in LDS; the 16-B chunk c of row r sits at chunk c ^ (r & 7), so the 16
+// lanes reading chunk g of 16 consecutive rows hit distinct banks without padding
+__device__ __forceinline__ int qswz(int row, int c) { return row * kIdxDim + 16 * (c ^ (row & 7)); }
 
 __device__ inline i32x8 load_b_operand(const uint8_t* key_row, int g) {
   i32x4 lo = *reinterpret_cast<const i32x4*>(key_row + 16 * g);
@@ -123,10 +128,10 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
                 const int32_t* __restrict__ req, const int32_t* __restrict__ pos, DevPages pg,
                 const uint8_t* __restrict__ cache, float* __restrict__ logits, int64_t stride,
                 int chunk_pages, LogitsMode md) {
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[RG * kIdxHeads * kQRow];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[RG * kIdxHeads * kIdxDim];
   __shared__ __attribute__((aligned(16))) float w_lds[RG * kIdxHeads];
   // filter mode: candidates of this work-group, per row, before one append per row
-  constexpr int kStage = kStageAll / RG;     // per row
+  constexpr int kStage = dsa::kStage<RG>;     // per row
   __shared__ uint32_t st_key[KIND == kLogitsFilter ? RG : 1][KIND == kLogitsFilter ? kStage : 1];
   __shared__ int st_pos[KIND == kLogitsFilter ? RG : 1][KIND == kLogitsFilter ? kStage : 1];
   __shared__ int st_n[RG];
@@ -169,7 +174,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     // small enough for four waves per SIMD
     for (int i = tid; i < RG * kIdxHeads * kIdxDim / 16; i += 256) {
       const int row = i >> 3, c = i & 7;
-      *reinterpret_cast<i32x4*>(q_lds + row * kQRow + 16 * c) =
+      *reinterpret_cast<i32x4*>(q_lds + qswz(row, c)) =
           reinterpret_cast<const i32x4*>(q8 + row0 * kIdxHeads * kIdxDim)[i];
     }
     for (int i = tid; i < RG * kIdxHeads; i += 256) w_lds[i] = w[row0 * kIdxHeads + i] * qs[row0 * kIdxHeads + i];
@@ -191,9 +196,9 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         float4 wr[2];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-          const uint8_t* qrow = q_lds + (r * kIdxHeads + 16 * t + k16) * kQRow;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(qrow + 16 * g);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(qrow + 64 + 16 * g);
+          const int qr = r * kIdxHeads + 16 * t + k16;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(q_lds + qswz(qr, g));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(q_lds + qswz(qr, 4 + g));
           A[t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           wr[t] = *reinterpret_cast<const float4*>(w_lds + r * kIdxHeads + 16 * t + 4 * g);
         }
@@ -228,7 +233,17 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
           // keep the scores at or above the row's threshold (rare: a few per cent)
           if (vis && key >= thr[r]) {
             const int sl = atomicAdd(&st_n[r], 1);
-            if (sl < kStage) { st_key[r][sl] = key; st_pos[r][sl] = (int)s; }
+            if (sl < kStage) {
+              st_key[r][sl] = key;
+              st_pos[r][sl] = (int)s;
+            } else {
+              // stage full: straight to the row's list (a count past fcap still flags the row)
+              const int gi = atomicAdd(&md.fcnt[row0 + r], 1);
+              if (gi < md.fcap) {
+                md.fkey[(row0 + r) * md.fcap + gi] = key;
+                md.fpos[(row0 + r) * md.fcap + gi] = (int)s;
+              }
+            }
           }
         } else {
           logits[(row0 + r) * stride + s] = v;
@@ -279,9 +294,9 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       __syncthreads();
       if (tid < RG) {
         const int n = st_n[tid];
-        // a stage overflow makes the row's count exceed the list, which sends the row to the
-        // exact fallback
-        st_base[tid] = n == 0 ? 0 : atomicAdd(&md.fcnt[row0 + tid], n <= kStage ? n : md.fcap + 1);
+        // only the staged entries: the overflow went to the list directly
+        const int ns = min(n, kStage);
+        st_base[tid] = ns == 0 ? 0 : atomicAdd(&md.fcnt[row0 + tid], ns);
       }
       __syncthreads();
 #pragma unroll
@@ -314,6 +329,12 @@ hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsVie
   // reads few pages, so it stops at one round of resident work-groups to amortise the q staging
   const int64_t want = KIND == kLogitsSample ? 1024 : 2048;
   int chunk = 32;
+  if (KIND == kLogitsFilter) {
+    // a row keeps up to fcap of its visible keys: a work-group's share, chunk * 64 * fcap /
+    // visible, should fit its per-row stage
+    const int64_t lim = (int64_t)kStage<RG> * ((int64_t)rows.max_pos + 1) / ((int64_t)md.fcap * 64);
+    chunk = lim >= 32 ? 32 : lim >= 16 ? 16 : lim >= 8 ? 8 : 4;
+  }
   while (chunk > 4 && n_groups * ((total_pages + chunk - 1) / chunk) < want) chunk >>= 1;
   const int64_t nchunks = (total_pages + chunk - 1) / chunk;
   hipLaunchKernelGGL((k_logits_decode<RG, KIND, FMT>), dim3((unsigned)nchunks, (unsigned)n_groups), dim3(256), 0, s, q8, qs,
@@ -349,19 +370,19 @@ hipError_t launch_fmt(const uint8_t* q8, const float* qs, const float* w, RowsVi
                       const uint8_t* cache, float* logits, int64_t stride, const LogitsMode& md, hipStream_t s) {
   if (rows.n <= 0) return hipSuccess;
   DevPages g{pg.pt, pg.pt_stride, pg.num_reqs, pg.num_pages};
-  // one request's long group (a prefill chunk) whose length six does not divide: its first
-  // 6 * floor(n / 6) rows go in sub-groups of six and the last one to five rows in a second
-  // launch; sub-groups of the largest divisor could shrink to one row, which re-reads every
-  // key once per row
-  if (rows.group == rows.n && rows.n > 6 && rows.n % 6 != 0) {
-    const int32_t head = rows.n - rows.n % 6;
+  // one request's long group (a prefill chunk): its first 8 * floor(n / 8) rows go in
+  // sub-groups of eight (each page read once per eight rows) and the last one to seven rows in
+  // a second launch; sub-groups of the largest divisor of n could shrink to one row, which
+  // re-reads every key once per row
+  if (rows.group == rows.n && rows.n > kLongGroupRG) {
+    const int32_t head = rows.n - rows.n % kLongGroupRG;
     RowsView a = rows, b = rows;
     a.n = a.group = head;
     b.req += head;
     b.pos += head;
     b.n = b.group = rows.n - head;
-    const hipError_t e = launch_kind<6, FMT>(q8, qs, w, a, g, cache, logits, stride, md, s);
-    if (e != hipSuccess) return e;
+    const hipError_t e = launch_kind<kLongGroupRG, FMT>(q8, qs, w, a, g, cache, logits, stride, md, s);
+    if (e != hipSuccess || b.n == 0) return e;
     return launch_fmt<FMT>(q8 + (int64_t)head * kIdxHeads * kIdxDim, qs + (int64_t)head * kIdxHeads,
                            w + (int64_t)head * kIdxHeads, b, pg, cache, logits + (int64_t)head * stride, stride,
                            shift_rows(md, head), s);
