@@ -139,6 +139,8 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, k16 = lane & 15;
   const int64_t row0 = (int64_t)blockIdx.y * RG;
+  // only the sample and fallback passes of the fused top-k ask for row ranges
+  constexpr bool kRange = KIND == kLogitsSample || KIND == kLogitsFallback;
   // pages are numbered in steps of page_step (the sample mode scores every page_step-th page)
   const int step = KIND == kLogitsSample ? md.page_step : 1;
   const int64_t pg0 = (int64_t)blockIdx.x * chunk_pages;          // in units of `step` pages
@@ -189,7 +191,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       // keep the per-page LDS reads of q / w inside the loop (hoisting them would pin all
       // rows' operands in registers again)
       __asm__ volatile("" ::: "memory");
-      const int64_t s = vi * step * 64 + lane;
+      const int s = (int)(vi * step * 64) + lane;          // positions fit in int32
 #pragma unroll
       for (int r = 0; r < RG; r++) {
         i32x8 A[2];
@@ -225,7 +227,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         const float keep1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);   // rows 0,1: tile 1; rows 2,3: tile 3
         const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(keep0), __float_as_uint(keep1), false, false);
         const float mine = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
-        const bool vis = pid >= 0 && s <= prow[r];
+        const bool vis = pid >= 0 && s <= prow[r];        // pid < 0: a bad page id (flagged)
         const float v = vis ? mine * key_scale(P) : -INFINITY;
         const uint32_t u = __float_as_uint(v);
         const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -235,19 +237,19 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
             const int sl = atomicAdd(&st_n[r], 1);
             if (sl < kStage) {
               st_key[r][sl] = key;
-              st_pos[r][sl] = (int)s;
+              st_pos[r][sl] = s;
             } else {
               // stage full: straight to the row's list (a count past fcap still flags the row)
               const int gi = atomicAdd(&md.fcnt[row0 + r], 1);
               if (gi < md.fcap) {
                 md.fkey[(row0 + r) * md.fcap + gi] = key;
-                md.fpos[(row0 + r) * md.fcap + gi] = (int)s;
+                md.fpos[(row0 + r) * md.fcap + gi] = s;
               }
             }
           }
         } else {
           logits[(row0 + r) * stride + s] = v;
-          if (md.range != nullptr && s <= prow[r]) {
+          if (kRange && md.range != nullptr && s <= prow[r]) {
             kmn = min(kmn, key);
             kmx = max(kmx, key);
           }
@@ -270,7 +272,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       if (pn2 < pend && ida >= 0) load_page(pa, cache + ida * kPageBytes<FMT>, lane);
       process(pb, pn, idb);
     }
-    if (KIND != kLogitsFilter && md.range != nullptr) {
+    if (kRange && md.range != nullptr) {
       __shared__ uint32_t red[kWaves][2];
       uint32_t mn = kmn, mx = kmx;
 #pragma unroll
