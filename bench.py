@@ -101,9 +101,17 @@ def write_traffic(fetch_csv, write_csv, command):
     import statistics
 
     def per_kernel(path):
-        vals = {}
+        """Counter values per kernel name.  The benchmark runs the c2 steps first and the fused
+        store and the chunked prefill (which launch some of the same kernels) after them: only
+        dispatches before the first fused-store dispatch count for the other kernels."""
         with open(path) as fh:
-            for r in csv.DictReader(fh):
+            rows = list(csv.DictReader(fh))
+        cut = min((int(r["Dispatch_Id"]) for r in rows if "k_fused_norm_rope_store" in r["Kernel_Name"]),
+                  default=None)
+        vals = {}
+        for r in rows:
+            own = "k_fused_norm_rope_store" in r["Kernel_Name"] or "copyBuffer" in r["Kernel_Name"]
+            if cut is None or own or int(r["Dispatch_Id"]) < cut:
                 vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
@@ -118,8 +126,8 @@ def write_traffic(fetch_csv, write_csv, command):
     copy_w = max(v for name, vs in write.items() if "copyBuffer" in name for v in vs)
     out = {"about": "HBM traffic per dispatch of the benchmark's kernels, from rocprofv3 --pmc FETCH_SIZE and "
                     "WRITE_SIZE (KiB per dispatch, median over dispatches): the c2 verify workload (64 x 6 rows at "
-                    "128K), and k_fused_norm_rope_store on the 8192-token chunked-prefill chunk; factors make a "
-                    "1 GiB device copy read and write 1 GiB",
+                    "128K; dispatches before the fused-store section), and k_fused_norm_rope_store on the "
+                    "8192-token chunked-prefill chunk; factors make a 1 GiB device copy read and write 1 GiB",
            "command": command, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
            "fetch_factor": gib_kib / copy_f, "write_factor": gib_kib / copy_w, "kernels": {}}
     for k, src in KERNEL_SOURCES.items():
