@@ -272,7 +272,8 @@ dsa_status dsa_indexer_topk_mxfp4(const uint8_t* q_fp8, const float* q_scale, co
 
 /* ---------------------------------------------------------------- sparse MLA */
 
-/* Workspace for dsa_sparse_mla_decode / _prefill, in bytes (may be 0). */
+/* Workspace for dsa_sparse_mla_decode / _prefill, in bytes (may be 0).  Its contents need no
+ * initialisation; calls that share one workspace must not overlap. */
 size_t dsa_sparse_mla_workspace_size(int32_t R, int32_t k);
 
 /* Sparse MLA in absorbed (MQA) form ([VLLM] §Sparse MLA Attention; [REQ]

@@ -26,6 +26,8 @@
 //    and a combine kernel merges the splits; with one split the kernel normalises and writes
 //    bf16.  Many rows: a stream-K schedule, one persistent work-group per CU over equal
 //    ranges of all rows' tiles; a row cut between two work-groups is merged by the second.
+#include <atomic>
+
 #include "dsa_device.hpp"
 #include "dsa_internal.h"
 
@@ -634,13 +636,16 @@ __device__ __attribute__((noinline)) void mla_segment_call(const uint16_t* q, co
 // gridDim.x equal consecutive ranges, one per work-group, each covering at least one full
 // row; a work-group runs its range as row segments.  A row cut between work-groups g-1 and
 // g (never more than two parts) leaves one partial from each in slot g; each writer waits
-// for its coherent partial stores to complete, then counts the slot, and the second writer
-// merges both parts (no work-group ever waits for another).  ctr[] must be zero at launch.
+// for its coherent partial stores to complete, then tags the slot with this launch's number,
+// and the writer that finds the tag already there merges both parts (no work-group ever waits
+// for another).  Tags replace clearing the slots before each launch: 0 is never a tag, and a
+// slot left by an earlier launch holds that launch's (smaller) tag.
 __global__ void __launch_bounds__(kThreads)
 k_sparse_mla_stream(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, const int32_t* __restrict__ pos,
                     DevPages pg, const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx, int32_t k,
                     int32_t R, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-                    float* __restrict__ ws_o, float* __restrict__ ws_ml, int* __restrict__ ctr) {
+                    float* __restrict__ ws_o, float* __restrict__ ws_ml, unsigned long long* __restrict__ tag,
+                    unsigned long long launch) {
   __shared__ int s_old;
   const int G = gridDim.x, gi = blockIdx.x;
   const int T = (k + kTile - 1) / kTile;
@@ -660,19 +665,23 @@ k_sparse_mla_stream(const uint16_t* __restrict__ q, const int32_t* __restrict__ 
                        po + (int64_t)part * kHeads * kVal, pml + part * kHeads * 2);
       wait_vmcnt<0>();                          // this thread's part of the partial is stored ...
       __syncthreads();
-      if (threadIdx.x == 0)                     // ... before the part is counted
-        s_old = __hip_atomic_fetch_add(&ctr[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) {                   // ... before the part is tagged
+        // exactly two parts per cut row and launch: the writer that swaps this launch's tag
+        // in is the first; the other finds it there and is the second
+        const unsigned long long old = __hip_atomic_load(&tag[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned long long seen = old;
+        if (old != launch)
+          seen = __hip_atomic_compare_exchange_strong(&tag[slot], &seen, launch, __ATOMIC_RELAXED,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     ? old : seen;
+        s_old = seen == launch;
+      }
       __syncthreads();
-      if (s_old == 1) merge_two_parts(po, pml, r, out, lse);   // both parts are in: merge them
+      if (s_old) merge_two_parts(po, pml, r, out, lse);   // both parts are in: merge them
       __syncthreads();
     }
     u += t1 - t0;
   }
-}
-
-__global__ void k_zero_counters(int* __restrict__ ctr, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-    __hip_atomic_store(&ctr[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Merges the splits of one row: block = (row, head), 128 threads x 4 dims.
@@ -712,8 +721,8 @@ constexpr int kStreamGroups = 256;              // one persistent work-group per
 }  // namespace
 
 size_t mla_workspace_bytes(int32_t R, int32_t k) {
-  if (R >= kStreamGroups)      // stream-K: two partials and a counter per slot
-    return (size_t)(kStreamGroups + 1) * (2 * kHeads * (kVal + 2) * sizeof(float) + sizeof(int));
+  if (R >= kStreamGroups)      // stream-K: two partials and a 64-bit tag per slot
+    return (size_t)(kStreamGroups + 1) * (2 * kHeads * (kVal + 2) * sizeof(float) + sizeof(unsigned long long));
   const int s = choose_splits(R, k);
   if (s == 1) return 0;
   return (size_t)R * s * kHeads * (kVal + 2) * sizeof(float);
@@ -731,10 +740,11 @@ hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, con
     const int slots = kStreamGroups + 1;
     float* wo = (float*)ws;
     float* wml = wo + (size_t)slots * 2 * kHeads * kVal;
-    int* ctr = (int*)(wml + (size_t)slots * 2 * kHeads * 2);
-    hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(256), 0, s, ctr, slots);
+    unsigned long long* tag = (unsigned long long*)(wml + (size_t)slots * 2 * kHeads * 2);   // 8-B aligned
+    static std::atomic<unsigned long long> launches{0};
+    const unsigned long long launch = ++launches;      // >= 1, increasing
     hipLaunchKernelGGL(k_sparse_mla_stream, dim3(kStreamGroups), dim3(kThreads), 0, s, q, rows.req, rows.pos, g,
-                       cache, idx, k, R, sm_log2, out, lse, wo, wml, ctr);
+                       cache, idx, k, R, sm_log2, out, lse, wo, wml, tag, launch);
     return hipGetLastError();
   }
   const int nsplit = choose_splits(R, k);
