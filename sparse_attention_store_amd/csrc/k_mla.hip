@@ -253,9 +253,6 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
 // Partial results cross work-groups (and XCDs, each with its own L2): they are written and
 // read as relaxed agent-scope atomics, which the hardware keeps coherent across the L2s
 // without a device-wide cache write-back.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void store_coherent(DSA_GLOBAL float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

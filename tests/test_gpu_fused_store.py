@@ -137,3 +137,25 @@ def test_fused_store_full_size_prefill_chunk():
     _same(lat, "latent cache")
     _same(idx, "index-K cache")
     _same(qq, "q")
+
+
+def test_fused_store_empty_and_all_padded():
+    """No tokens: a successful no-op.  Every token padded: nothing written, q left as it was."""
+    print("\n[gpu] fused store, empty and all-padded batches", flush=True)
+    w = gi.config(0, "small")
+    kv, gamma, k_idx, q = _inputs(w.seed, 4)
+    pages = dsa.Pages(dev(w.page_table), w.num_pages)
+    lat = torch.full((w.num_pages, 41984), 0x5A, dtype=torch.uint8, device=DEV)
+    idx = torch.full((w.num_pages, 8448), 0x5A, dtype=torch.uint8, device=DEV)
+    dq = dev(q.view(np.int16))
+    q0 = dq.clone()
+    empty = dsa.Rows(torch.zeros(0, dtype=torch.int32, device=DEV), torch.zeros(0, dtype=torch.int32, device=DEV), 0, 1)
+    dsa.dsa_fused_norm_rope_store(dev(kv.view(np.int16))[:0, 2048:], empty, pages, lat, index_cache=idx,
+                                  k_idx=dev(k_idx.view(np.int16))[:0], gamma=dev(gamma.view(np.int16)))
+    padded = dsa.Rows(dev(np.zeros(4, np.int32)), dev(np.full(4, -1, np.int32)), 0, 1)
+    dsa.dsa_fused_norm_rope_store(dev(kv.view(np.int16))[:, 2048:], padded, pages, lat, index_cache=idx,
+                                  k_idx=dev(k_idx.view(np.int16)), gamma=dev(gamma.view(np.int16)),
+                                  q_pe=dq[:, :, 512:])
+    torch.cuda.synchronize()
+    assert bool((lat == 0x5A).all()) and bool((idx == 0x5A).all()) and torch.equal(dq, q0)
+    dsa.dsa_check_device_errors()

@@ -108,3 +108,31 @@ def test_mxfp4_fused_topk(cid):
     ref_lg = orc.indexer_logits_mxfp4(q8, qs, wt, w.row_req, w.row_pos, w.page_table, host(cache))
     ridx, kth = orc.topk(ref_lg, w.row_pos, 2048)
     topk_sets_match(fused, ridx, ref_lg, kth)
+
+
+def test_mxfp4_store_special_keys():
+    """Keys whose LayerNorm output is all zero (a constant raw key: scale byte 127, zero codes),
+    very large and very small raw keys, and exact powers of two: bit-exact against the oracle."""
+    _announce("mxfp4 store, special keys")
+    n = 64
+    rng = np.random.default_rng(61)
+    raw = rng.standard_normal((n, 128))
+    raw[0] = 3.0                                  # constant: LayerNorm gives zeros
+    raw[1] *= 1e30
+    raw[2] *= 1e-30
+    raw[3] = np.where(np.arange(128) % 2 == 0, 4.0, -4.0)
+    raw[4, :] = 0.0
+    raw[4, 7] = 1.0                               # one spike
+    k = orc.bf16_from_double(raw)
+    pos = np.arange(n, dtype=np.int32)
+    pt = np.array([[0]], np.int32)
+    ref = np.zeros((1, MX_PAGE), np.uint8)
+    orc.index_k_store_mxfp4(k, np.zeros(n, np.int32), pos, pt, ref, LN_EPS, THETA)
+    cache = torch.zeros((1, MX_PAGE), dtype=torch.uint8, device=DEV)
+    tok = dsa.Rows(dev(np.zeros(n, np.int32)), dev(pos), n - 1, 1)
+    dsa.dsa_index_k_store_mxfp4(dev(k.view(np.int16)), tok, dsa.Pages(dev(pt), 1), cache, LN_EPS, THETA)
+    torch.cuda.synchronize()
+    got = host(cache)
+    diff = np.argwhere(got != ref)
+    assert len(diff) == 0, f"{len(diff)} bytes differ, first at {diff[:5].tolist()}"
+    assert got[0, 4096] == 127 and not got[0, :64].any()     # the constant key
