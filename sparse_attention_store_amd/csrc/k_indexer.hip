@@ -48,9 +48,14 @@ template <int RG> constexpr int kStage = RG <= 6 ? 768 / RG : 104;
 // lanes reading chunk g of 16 consecutive rows hit distinct banks without padding
 __device__ __forceinline__ int qswz(int row, int c) { return row * kIdxDim + 16 * (c ^ (row & 7)); }
 
+// Plain loads: the nontemporal hint was slower here, also where a row group reads each page
+// once (and prefill chunks re-read pages from the last-level cache).
+__device__ __forceinline__ i32x4 ld16(const uint8_t* p) { return *reinterpret_cast<const i32x4*>(p); }
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
 __device__ inline i32x8 load_b_operand(const uint8_t* key_row, int g) {
-  i32x4 lo = *reinterpret_cast<const i32x4*>(key_row + 16 * g);
-  i32x4 hi = *reinterpret_cast<const i32x4*>(key_row + 64 + 16 * g);
+  i32x4 lo = ld16(key_row + 16 * g);
+  i32x4 hi = ld16(key_row + 64 + 16 * g);
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -79,15 +84,15 @@ __device__ inline void load_page(PageRegs<kIdxFp8>& P, const uint8_t* page, int 
   const int g = lane >> 4, k16 = lane & 15;
 #pragma unroll
   for (int t = 0; t < 4; t++) P.b[t] = load_b_operand(page + (16 * t + k16) * kIdxDim, g);
-  P.ks = *reinterpret_cast<const float*>(page + kIdxScaleOff + 4 * lane);
+  P.ks = __uint_as_float(ld4(page + kIdxScaleOff + 4 * lane));
 }
 __device__ inline void load_page(PageRegs<kIdxMxfp4>& P, const uint8_t* page, int lane) {
   const int g = lane >> 4, k16 = lane & 15;
   uint32_t sw[4];
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    P.b[t] = *reinterpret_cast<const i32x4*>(page + (16 * t + k16) * kMx4KeyBytes + 16 * g);
-    sw[t] = *reinterpret_cast<const uint32_t*>(page + kMx4ScaleOff + 4 * (16 * t + k16));
+    P.b[t] = ld16(page + (16 * t + k16) * kMx4KeyBytes + 16 * g);
+    sw[t] = ld4(page + kMx4ScaleOff + 4 * (16 * t + k16));
   }
   uint32_t sb = 0;
 #pragma unroll
@@ -136,7 +141,8 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
   __shared__ int st_pos[KIND == kLogitsFilter ? RG : 1][KIND == kLogitsFilter ? kStage : 1];
   __shared__ int st_n[RG];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, k16 = lane & 15;
   const int64_t row0 = (int64_t)blockIdx.y * RG;
   // only the sample and fallback passes of the fused top-k ask for row ranges
@@ -171,6 +177,12 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
   const int64_t pend = min(pg0 + chunk_pages, (vis_pages + step - 1) / step);
 
   if (pg0 < pend) {
+    // ids of this wave's pages pg0 + wave + kWaves * i, lane i holding the i-th (a chunk has
+    // at most 32 pages, so at most eight per wave); loaded once, ahead of the q staging, so the
+    // page loop has no dependent page-table load
+    const int nw = pend > pg0 + wave ? (int)((pend - pg0 - wave + kWaves - 1) / kWaves) : 0;
+    int my_id = -1;
+    if (lane < nw) my_id = (int)page_of(pg, rq, (pg0 + wave + (int64_t)kWaves * lane) * step * 64);
     // stage q (RG x 32 heads x 128 B, rows padded) and w*q_scale in LDS; the MFMA A operands
     // and head weights are re-read from LDS for every page, which keeps the register file
     // small enough for four waves per SIMD
@@ -256,21 +268,27 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         }
       }
     };
-    // two register buffers in ping-pong: the next page loads while this one is scored
+    // two register buffers in ping-pong: the next page loads while this one is scored.  The
+    // loop takes pages in pairs and leaves only at its end, with the same loads in flight on
+    // every path (past the last page the last one is loaded again; a bad id loads page 0 and
+    // scores as invisible), so the waits for a page's operands keep the next page in flight.
     PageRegs<FMT> pa, pb;
-    int64_t pi = pg0 + wave;
-    int64_t ida = pi < pend ? page_of(pg, rq, pi * step * 64) : -1;
-    if (pi < pend && ida >= 0) load_page(pa, cache + ida * kPageBytes<FMT>, lane);
-    for (; pi < pend; pi += 2 * kWaves) {
-      const int64_t pn = pi + kWaves;
-      const int64_t idb = pn < pend ? page_of(pg, rq, pn * step * 64) : -1;
-      if (pn < pend && idb >= 0) load_page(pb, cache + idb * kPageBytes<FMT>, lane);
-      process(pa, pi, ida);
-      if (pn >= pend) break;
-      const int64_t pn2 = pn + kWaves;
-      ida = pn2 < pend ? page_of(pg, rq, pn2 * step * 64) : -1;
-      if (pn2 < pend && ida >= 0) load_page(pa, cache + ida * kPageBytes<FMT>, lane);
-      process(pb, pn, idb);
+    auto page_addr = [&](int id) { return cache + (int64_t)(id < 0 ? 0 : id) * kPageBytes<FMT>; };
+    auto page_id = [&](int i) { return __builtin_amdgcn_readlane(my_id, min(i, nw - 1)); };
+    auto page_vi = [&](int i) { return pg0 + wave + (int64_t)kWaves * i; };
+    if (nw > 0) {
+      int ida = page_id(0);
+      load_page(pa, page_addr(ida), lane);
+      int i = 0;
+      for (; i + 1 < nw; i += 2) {
+        const int idb = page_id(i + 1);
+        load_page(pb, page_addr(idb), lane);
+        process(pa, page_vi(i), ida);
+        ida = page_id(i + 2);
+        load_page(pa, page_addr(ida), lane);
+        process(pb, page_vi(i + 1), idb);
+      }
+      if (i < nw) process(pa, page_vi(i), ida);     // an odd page count: the last page
     }
     if (kRange && md.range != nullptr) {
       __shared__ uint32_t red[kWaves][2];

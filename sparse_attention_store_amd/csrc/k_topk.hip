@@ -12,11 +12,10 @@
 //               The fused indexer+top-k entry gets the range from the logits kernel instead.
 //  2. k_hist:   grid (chunk, row): LDS histogram of d = (key - kmin) >> shift, 4096 bins,
 //               shift chosen from the range; merged into a per-row global histogram.
-//  3. k_thresh: one work-group per row finds the threshold bin T (the bin holding the k-th
-//               largest key) from the merged histogram.
-//     k_select: grid (chunk, row): keys with d > T are selected, keys with d == T become
-//               candidates.  Appends are gathered per work-group in LDS and reserved with
-//               one global atomic per list.
+//  3. k_select: grid (chunk, row): each work-group finds the threshold bin T (the bin
+//               holding the k-th largest key) from the row's merged histogram, then keys with
+//               d > T are selected and keys with d == T become candidates.  Appends are
+//               gathered per work-group in LDS and reserved with one global atomic per list.
 //  4. k_final:  one work-group per row resolves the low `shift` bits over the candidates in
 //               LDS (10-bit rounds), keeps the lowest positions among exact ties at the
 //               threshold, and writes the k positions in ascending order via an LDS bitmap of
@@ -234,21 +233,6 @@ __device__ inline int find_threshold(const int* h, int k, int* scan, int* result
   return result[0];
 }
 
-// Per row: the threshold bin T from the merged histogram (one work-group per row).
-__global__ void __launch_bounds__(256) k_thresh(const int32_t* __restrict__ pos, int64_t stride, int32_t k, Ws ws,
-                                                const int* __restrict__ gate) {
-  __shared__ int h[kBins];
-  __shared__ int scan[256 / 64];
-  __shared__ int res[2];
-  const int r = blockIdx.x;
-  if (gate != nullptr && !gate[r]) return;
-  if (row_len(pos, r, stride) <= k) return;
-  for (int i = threadIdx.x; i < kBins; i += 256) h[i] = ws.hist[(int64_t)r * kBins + i];
-  __syncthreads();
-  const int T = find_threshold<256, kBins>(h, k, scan, res);
-  if (threadIdx.x == 0) ws.cnt[(int64_t)r * 4 + 2] = T;
-}
-
 constexpr int kSelCap = 1024;    // candidates gathered per work-group before spilling to global appends
 
 __global__ void __launch_bounds__(256) k_select(const float* __restrict__ logits, int64_t stride,
@@ -258,6 +242,9 @@ __global__ void __launch_bounds__(256) k_select(const float* __restrict__ logits
   __shared__ uint32_t l_ckey[kSelCap];
   __shared__ int l_cpos[kSelCap];
   __shared__ int n_above, n_cand, base_above, base_cand;
+  __shared__ int h[kBins];
+  __shared__ int scan[256 / 64];
+  __shared__ int res[2];
   const int r = blockIdx.y;
   if (gate != nullptr && !gate[r]) return;
   const int64_t n = row_len(pos, r, stride);
@@ -265,12 +252,15 @@ __global__ void __launch_bounds__(256) k_select(const float* __restrict__ logits
   if (n <= k || c0 >= n) return;
   const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
   const int shift = range_shift(kmin, kmax);
-  const uint32_t T = (uint32_t)ws.cnt[(int64_t)r * 4 + 2];
   const int64_t c1 = min(c0 + kChunk, n);
   float4 v[kPerThread];
   load_chunk(logits + (int64_t)r * stride, c0, c1, v);
+  // the threshold bin from the row's merged histogram (every work-group of the row finds the
+  // same one; the chunk's logits load meanwhile)
+  for (int i = threadIdx.x; i < kBins; i += 256) h[i] = ws.hist[(int64_t)r * kBins + i];
   if (threadIdx.x == 0) { n_above = 0; n_cand = 0; }
   __syncthreads();
+  const uint32_t T = (uint32_t)find_threshold<256, kBins>(h, k, scan, res);
   uint32_t* ckey = ws.ckey + (int64_t)r * kCap;
   int* cpos = ws.cpos + (int64_t)r * kCap;
 #pragma unroll
@@ -676,7 +666,6 @@ static hipError_t launch_radix_passes(const float* logits, int64_t stride, RowsV
   if (visible > k) {
     const unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
     hipLaunchKernelGGL(k_hist, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
-    hipLaunchKernelGGL(k_thresh, dim3(R), dim3(256), 0, s, rows.pos, stride, k, w, gate);
     hipLaunchKernelGGL(k_select, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
   }
   hipLaunchKernelGGL(k_final, dim3(R), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k, idx, w, gate);
