@@ -11,7 +11,8 @@
 //  * Each tile's 32 records (656 B each: fp8 latent, 4 scales, bf16 rope) are copied from
 //    HBM straight into LDS with gfx950's global_load_lds_dwordx4, two tiles ahead of the
 //    compute (explicit vmcnt waits + raw s_barrier: a full __syncthreads() would drain the
-//    in-flight copies every tile).
+//    in-flight copies every tile).  The copies scatter the records' 16-B chunks so that every
+//    wave-wide LDS access of the tile reads one contiguous block (see the tile layout below).
 //  * Warp specialisation, one barrier per tile: waves 0-3 score tile t (S^T[32 keys x 16
 //    heads]; the 512 latent dims on the block-scaled FP8 MFMA v_mfma_scale_f32_16x16x128_
 //    f8f6f4 fed with the cached codes and their ue8m0 scales as E8M0 operands, against a
@@ -53,7 +54,6 @@ static_assert(kDmaWaves * kDmaPerWave >= kTileSlots, "copy slots must cover a ti
 constexpr int kMaxSplitKeys = 2048;
 static_assert(kDepth * kTile <= kMaxSplitKeys, "the first tiles' lookups stay inside phys");
 static_assert(kMaxSplitKeys % kThreads == 0, "whole index loads per thread");
-constexpr int kPRowB = kTile + 8;   // P row pitch in bf16 (80 B): 16-B reads of 8 head rows hit distinct banks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;      // log2 units the running max may lag behind
 
@@ -83,8 +83,40 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Global->LDS copies of one tile: LDS chunk c of the tile holds 16 B of key c/41, chunk
-// c%41 of its 656-B record (records land back to back).  Each QK wave issues exactly
+// Tile layout in LDS, in 16-B chunks (1312 per tile of 32 keys).  Every wave-wide access of
+// the scoring and accumulation steps reads one contiguous block: measured with the LDS
+// bank-conflict counter, 16-B reads of records stored back to back (a 656-B stride between
+// the lanes' keys) took twice the cycles of a contiguous 1-KiB read, and contiguous reads
+// took none extra.
+//  * chunks [0, 1024): latent.  Block (mt * 4 + b) * 2 + half of 64 chunks holds, at chunk
+//    16 gg + kk, bytes 128 b + 64 half + 16 gg .. +16 of key 16 mt + kk;
+//  * [1024, 1056): the 16 scale bytes of key c - 1024;
+//  * [1056, 1312): rope.  Block mt * 2 + ks holds, at chunk 16 gg + kk, rope bytes 64 ks +
+//    16 gg .. +16 of key 16 mt + kk.
+constexpr int kScaleChunk0 = 1024, kRopeChunk0 = 1056;
+static_assert(kRopeChunk0 + 4 * 64 == kTileChunks, "the layout covers the tile");
+// tile chunk of latent byte `byte` (a multiple of 8) of key `key`
+__device__ __forceinline__ int lat_chunk(int key, int byte) {
+  return (((key >> 4) * 4 + (byte >> 7)) * 2 + ((byte >> 6) & 1)) * 64 + 16 * ((byte >> 4) & 3) + (key & 15);
+}
+// key and 16-B record chunk held at tile chunk c (0 <= c < kTileChunks)
+__device__ __forceinline__ void chunk_src(int c, int& key, int& rc) {
+  if (c < kScaleChunk0) {
+    const int q = c >> 6, r = c & 63;
+    key = 16 * (q >> 3) + (r & 15);
+    rc = 8 * ((q >> 1) & 3) + 4 * (q & 1) + (r >> 4);
+  } else if (c < kRopeChunk0) {
+    key = c - kScaleChunk0;
+    rc = kRecScaleOff / 16;
+  } else {
+    const int q = (c - kRopeChunk0) >> 6, r = (c - kRopeChunk0) & 63;
+    key = 16 * (q >> 1) + (r & 15);
+    rc = kRecRopeOff / 16 + 4 * (q & 1) + (r >> 4);
+  }
+}
+
+// Global->LDS copies of one tile: lane l of copy u of a QK wave fills tile chunk
+// (wave * kDmaPerWave + u) * 64 + l with its record chunk.  Each QK wave issues exactly
 // kDmaPerWave copies so that per-tile vmcnt accounting is uniform; lanes past the tile or of
 // invalid keys copy from the first record of the pool into the buffer (the records of
 // invalid keys are zeroed before use).  The record lookups (read_tile_phys) are done a tile
@@ -94,7 +126,9 @@ __device__ __forceinline__ void read_tile_phys(const DSA_LDS int* __restrict__ p
 #pragma unroll
   for (int u = 0; u < kDmaPerWave; u++) {
     const int c = (wave * kDmaPerWave + u) * 64 + lane;
-    ph[u] = phys[tile_base + min(c / kChunks, kTile - 1)];   // < ntiles * kTile <= kMaxSplitKeys
+    int key, rc;
+    chunk_src(min(c, kTileChunks - 1), key, rc);
+    ph[u] = phys[tile_base + key];   // < ntiles * kTile <= kMaxSplitKeys
   }
 }
 __device__ __forceinline__ void issue_tile_ph(const uint8_t* cache, const int (&ph)[kDmaPerWave], DSA_LDS uint8_t* buf,
@@ -102,9 +136,10 @@ __device__ __forceinline__ void issue_tile_ph(const uint8_t* cache, const int (&
 #pragma unroll
   for (int u = 0; u < kDmaPerWave; u++) {
     const int c = (wave * kDmaPerWave + u) * 64 + lane;
-    const int key = min(c / kChunks, kTile - 1);
+    int key, rc;
+    chunk_src(min(c, kTileChunks - 1), key, rc);
     const bool ok = c < kTileChunks && ph[u] >= 0;
-    const uint8_t* src = ok ? cache + (int64_t)ph[u] * kRecBytes + 16 * (c - key * kChunks) : cache;
+    const uint8_t* src = ok ? cache + (int64_t)ph[u] * kRecBytes + 16 * rc : cache;
     const int slot = min(wave * kDmaPerWave + u, kTileSlots);   // surplus copies share the sink
     __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(buf + slot * 1024), 16, 0, 0);
   }
@@ -112,8 +147,9 @@ __device__ __forceinline__ void issue_tile_ph(const uint8_t* cache, const int (&
 // Zeroes the records of the invalid keys of a tile (all threads of the work-group).
 __device__ __forceinline__ void zero_bad_records(DSA_LDS uint8_t* __restrict__ T, const DSA_LDS int* phys, int tile_base,
                                                  int tid) {
-  for (int i = tid; i < kTile * kChunks; i += kThreads) {
-    const int key = i / kChunks;
+  for (int i = tid; i < kTileChunks; i += kThreads) {
+    int key, rc;
+    chunk_src(i, key, rc);
     if (phys[tile_base + key] < 0) *reinterpret_cast<DSA_LDS i32x4*>(T + 16 * i) = i32x4{0, 0, 0, 0};
   }
 }
@@ -168,21 +204,21 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
   i32x8 a[2][4];
   bf16x8 ar[2][2];
   int sa[2][4];
+  // lane (g, c16) reads chunk `lane` of a 64-chunk block: bytes 16g.. of key 16mt + c16
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
-    const DSA_LDS uint8_t* rec = T + (16 * mt + c16) * kRecBytes;
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-      const i32x4 lo4 = *reinterpret_cast<const DSA_LDS i32x4*>(rec + 128 * b + 16 * g);
-      const i32x4 hi4 = *reinterpret_cast<const DSA_LDS i32x4*>(rec + 128 * b + 64 + 16 * g);
+      const i32x4 lo4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * (((mt * 4 + b) * 2 + 0) * 64 + lane));
+      const i32x4 hi4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * (((mt * 4 + b) * 2 + 1) * 64 + lane));
       a[mt][b] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     }
-    const i32x4 ksc = *reinterpret_cast<const DSA_LDS i32x4*>(rec + kRecScaleOff);
+    const i32x4 ksc = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * (kScaleChunk0 + 16 * mt + c16));
 #pragma unroll
     for (int b = 0; b < 4; b++) sa[mt][b] = (ksc[b] >> 23) & 0xFF;   // E8M0 = the fp32 exponent of 2^e
 #pragma unroll
     for (int ks = 0; ks < 2; ks++)
-      ar[mt][ks] = *reinterpret_cast<const DSA_LDS bf16x8*>(rec + kRecRopeOff + 2 * (32 * ks + 8 * g));
+      ar[mt][ks] = *reinterpret_cast<const DSA_LDS bf16x8*>(T + 16 * (kRopeChunk0 + (mt * 2 + ks) * 64 + lane));
   }
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -243,11 +279,12 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
   const bool any_resc = __any(alpha != 1.f);     // wave-uniform: tells the PV waves to rescale
   if (lane == 0) resc_p[qw] = any_resc;
   // P as bf16, unscaled: the PV waves multiply in each key's value-block scale (a power of
-  // two, so the product is the bf16 rounding of P times the scale)
-#pragma unroll
-  for (int mt = 0; mt < 2; mt++)
-    *reinterpret_cast<DSA_LDS i32x2*>(plp + hh * kPRowB + 16 * mt + 4 * g) =
-        i32x2{pack2_bf16(p[mt][0], p[mt][1]), pack2_bf16(p[mt][2], p[mt][3])};
+  // two, so the product is the bf16 rounding of P times the scale).  A lane's 16 B, its
+  // head's keys 4g..4g+3 and 16+4g..16+4g+3, land at chunk 64 qw + lane: the PV waves read
+  // them as their MFMA operand's K = 8g..8g+7 in that key order.
+  *reinterpret_cast<DSA_LDS i32x4*>(plp + 8 * (64 * qw + lane)) =
+      i32x4{pack2_bf16(p[0][0], p[0][1]), pack2_bf16(p[0][2], p[0][3]), pack2_bf16(p[1][0], p[1][1]),
+            pack2_bf16(p[1][2], p[1][3])};
 }
 
 // Partial results cross work-groups (and XCDs, each with its own L2): they are written and
@@ -291,7 +328,7 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
   const int64_t pt_stride = pg.pt_stride, num_pages = pg.num_pages;
   const int32_t num_reqs = pg.num_reqs;
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[kBufs][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t pl[2][kHeads * kPRowB];     // P of a tile, bf16
+  __shared__ __attribute__((aligned(16))) uint16_t pl[2][kHeads * kTile];     // P of a tile, bf16
   __shared__ __attribute__((aligned(16))) float alpha_s[2][kHeads];
   __shared__ __attribute__((aligned(16))) int resc_s[2][4];     // per QK wave: some alpha != 1
   __shared__ float m_s[kHeads], l_s[kHeads];
@@ -510,19 +547,19 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
 #pragma unroll
             for (int i = 0; i < 4; i++) O[ht][dt][i] *= al[ht][i];
       }
-      // A operands: P of heads 16ht + c16 for keys 8g..8g+7, times those keys' scale of
-      // value block qw (a power of two: exact), rounded to bf16
+      // A operands: P of heads 16ht + c16 for K = 8g..8g+7, i.e. keys 4g..4g+3 and
+      // 16+4g..16+4g+3 (the order the QK waves wrote), times those keys' scale of value block
+      // qw (a power of two: exact), rounded to bf16
       f32x4 ks[2];
 #pragma unroll
       for (int h = 0; h < 2; h++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) ks[h][i] = *reinterpret_cast<const DSA_LDS float*>(T + (8 * g + 4 * h + i) * kRecBytes +
-                                                                                kRecScaleOff + 4 * qw);
+        for (int i = 0; i < 4; i++)
+          ks[h][i] = *reinterpret_cast<const DSA_LDS float*>(T + 16 * (kScaleChunk0 + 16 * h + 4 * g + i) + 4 * qw);
       bf16x8 pa[4];
 #pragma unroll
       for (int ht = 0; ht < 4; ht++) {
-        const i32x4 pw = *reinterpret_cast<const DSA_LDS i32x4*>((const DSA_LDS uint16_t*)pl[par] +
-                                                                 (16 * ht + c16) * kPRowB + 8 * g);
+        const i32x4 pw = *reinterpret_cast<const DSA_LDS i32x4*>((const DSA_LDS uint16_t*)pl[par] + 8 * (64 * ht + lane));
         int w[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {            // keys 8g + 2j, 8g + 2j + 1
@@ -532,11 +569,12 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
         }
         pa[ht] = __builtin_bit_cast(bf16x8, i32x4{w[0], w[1], w[2], w[3]});
       }
-      // tr8: lane i of a 16-lane group points at key 8g + i/2, dims +8*(i%2); gets 8 keys of dim c16
+      // tr8: lane i of a 16-lane group points at the key of K = 8g + i/2 (key 16(i/8) + 4g +
+      // (i/2)%4), dims +8*(i%2); gets those 8 keys of dim c16
+      const int vkey = 16 * (c16 >> 3) + 4 * g + ((c16 >> 1) & 3);
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
-        const int dim0 = 128 * qw + 16 * dt;
-        DSA_LDS i32x2* src = (DSA_LDS i32x2*)(T + (8 * g + (c16 >> 1)) * kRecBytes + dim0 + 8 * (c16 & 1));
+        DSA_LDS i32x2* src = (DSA_LDS i32x2*)(T + 16 * lat_chunk(vkey, 128 * qw + 16 * dt) + 8 * (c16 & 1));
         const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(src);
         const bf16x8 vv = fp8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1], 1.0f);
 #pragma unroll
