@@ -12,7 +12,7 @@ One step = one pass of that 4-layer group.  value = query tokens x layers / s (t
 which query tokens pass through DSA layers); per-kernel times come from HIP events on the
 stream the kernels run on, over the whole timed region.
 
-Prints one JSON line.  --gpus N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus N > 1 exits: the library has no multi-GPU path.
 """
 from __future__ import annotations
 
@@ -209,7 +209,7 @@ def main():
         print(json.dumps(write_traffic(*a.write_traffic), indent=1))
         return
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 

@@ -13,7 +13,7 @@
 //    compute (explicit vmcnt waits + raw s_barrier: a full __syncthreads() would drain the
 //    in-flight copies every tile).  The copies scatter the records' 16-B chunks so that every
 //    wave-wide LDS access of the tile reads one contiguous block (see the tile layout below).
-//  * Warp specialisation, one barrier per tile: waves 0-3 score tile t (S^T[32 keys x 16
+//  * Wave specialisation, one barrier per tile: waves 0-3 score tile t (S^T[32 keys x 16
 //    heads]; the 512 latent dims on the block-scaled FP8 MFMA v_mfma_scale_f32_16x16x128_
 //    f8f6f4 fed with the cached codes and their ue8m0 scales as E8M0 operands, against a
 //    two-term FP8 expansion of q that keeps bf16's precision; the 64 rope dims on the bf16
