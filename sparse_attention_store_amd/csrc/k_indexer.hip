@@ -183,9 +183,9 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     const int nw = pend > pg0 + wave ? (int)((pend - pg0 - wave + kWaves - 1) / kWaves) : 0;
     int my_id = -1;
     if (lane < nw) my_id = (int)page_of(pg, rq, (pg0 + wave + (int64_t)kWaves * lane) * step * 64);
-    // stage q (RG x 32 heads x 128 B, rows padded) and w*q_scale in LDS; the MFMA A operands
-    // and head weights are re-read from LDS for every page, which keeps the register file
-    // small enough for four waves per SIMD
+    // stage q (RG x 32 heads x 128 B, 16-B chunks swizzled by row) and w*q_scale in LDS; the
+    // MFMA A operands and head weights are re-read from LDS for every page, which keeps the
+    // register file small enough for four waves per SIMD
     for (int i = tid; i < RG * kIdxHeads * kIdxDim / 16; i += 256) {
       const int row = i >> 3, c = i & 7;
       *reinterpret_cast<i32x4*>(q_lds + qswz(row, c)) =
