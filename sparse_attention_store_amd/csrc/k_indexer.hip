@@ -165,10 +165,18 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
   // no score (the fused indexer + top-k passes k here; nothing of the group is written)
   if (pmax + 1 <= md.skip_upto) return;
   if (KIND == kLogitsFallback && !flagged) return;     // no row of the group needs the full scores
-  uint32_t thr[RG];
+  // the rows' thresholds as floats: for a finite score v, key(v) >= thr exactly when
+  // v >= thr_f, except that -0.0 also passes a threshold of +0.0 (a superset of the candidates;
+  // the exact selection over them is unchanged).  Thresholds at or below key(-inf) pass every
+  // score; those above key(+inf) decode to NaN, which no score reaches.
+  float thr_f[RG];
   if (KIND == kLogitsFilter) {
 #pragma unroll
-    for (int r = 0; r < RG; r++) thr[r] = md.thr[row0 + r];
+    for (int r = 0; r < RG; r++) {
+      const uint32_t t = md.thr[row0 + r];
+      const uint32_t f = t <= 0x007FFFFFu ? 0xFF800000u : ((t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t);
+      thr_f[r] = __int_as_float(__builtin_amdgcn_readfirstlane((int)f));     // wave-uniform: scalar
+    }
     if (tid < RG) st_n[tid] = 0;
   }
   const int32_t rq = req[row0];
@@ -241,11 +249,14 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         const float mine = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
         const bool vis = pid >= 0 && s <= prow[r];        // pid < 0: a bad page id (flagged)
         const float v = vis ? mine * key_scale(P) : -INFINITY;
-        const uint32_t u = __float_as_uint(v);
-        const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        auto key_of = [](float x) {
+          const uint32_t u = __float_as_uint(x);
+          return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        };
         if (KIND == kLogitsFilter) {
           // keep the scores at or above the row's threshold (rare: a few per cent)
-          if (vis && key >= thr[r]) {
+          if (vis && v >= thr_f[r]) {
+            const uint32_t key = key_of(v);
             const int sl = atomicAdd(&st_n[r], 1);
             if (sl < kStage) {
               st_key[r][sl] = key;
@@ -262,6 +273,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         } else {
           logits[(row0 + r) * stride + s] = v;
           if (kRange && md.range != nullptr && s <= prow[r]) {
+            const uint32_t key = key_of(v);
             kmn = min(kmn, key);
             kmx = max(kmx, key);
           }
