@@ -186,7 +186,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
 
   if (pg0 < pend) {
     // ids of this wave's pages pg0 + wave + kWaves * i, lane i holding the i-th (a chunk has
-    // at most 64 pages, so at most 16 per wave); loaded once, ahead of the q staging, so the
+    // at most 128 pages, so at most 32 per wave); loaded once, ahead of the q staging, so the
     // page loop has no dependent page-table load
     const int nw = pend > pg0 + wave ? (int)((pend - pg0 - wave + kWaves - 1) / kWaves) : 0;
     int my_id = -1;
@@ -361,15 +361,15 @@ hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsVie
   // enough work-groups to cover the chip (each page is one wave-iteration); the sampling pass
   // reads few pages, so it stops at one round of resident work-groups to amortise the q staging
   const int64_t want = KIND == kLogitsSample ? 1024 : 2048;
-  // 32 pages per work-group; the filter pass, which writes no logits, takes up to 64 (fewer
-  // work-groups amortise the q staging: 3% off the c2 filter pass, while the logits-writing
-  // pass was 1% slower with 64)
+  // 32 pages per work-group; the filter pass, which writes no logits, takes up to 128 as its
+  // stage allows (fewer work-groups amortise the q staging: 64 took 3% off the c2 filter pass
+  // and 128 1.6% off the 1M prefill indexer, while the logits-writing pass was 1% slower with 64)
   int chunk = 32;
   if (KIND == kLogitsFilter) {
     // a row keeps up to fcap of its visible keys: a work-group's share, chunk * 64 * fcap /
     // visible, should fit its per-row stage
     const int64_t lim = (int64_t)kStage<RG> * ((int64_t)rows.max_pos + 1) / ((int64_t)md.fcap * 64);
-    chunk = lim >= 64 ? 64 : lim >= 32 ? 32 : lim >= 16 ? 16 : lim >= 8 ? 8 : 4;
+    chunk = lim >= 128 ? 128 : lim >= 64 ? 64 : lim >= 32 ? 32 : lim >= 16 ? 16 : lim >= 8 ? 8 : 4;
   }
   while (chunk > 4 && n_groups * ((total_pages + chunk - 1) / chunk) < want) chunk >>= 1;
   const int64_t nchunks = (total_pages + chunk - 1) / chunk;
