@@ -64,6 +64,9 @@ struct LogitsMode {
   uint32_t* fkey = nullptr;
   int* fpos = nullptr;
   int fcap = 0;
+  // filter: pages p with p % sampled_step == 0 already hold their scores in `logits` (the sample
+  // pass wrote them); when it is > 1 and divides the chunk, those pages are not scored again
+  int sampled_step = 0;
   // fallback: plain scores for the row groups with a flagged row only
   const int* flag = nullptr;
 };

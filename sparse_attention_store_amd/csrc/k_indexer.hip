@@ -188,9 +188,18 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     // ids of this wave's pages pg0 + wave + kWaves * i, lane i holding the i-th (a chunk has
     // at most 128 pages, so at most 32 per wave); loaded once, ahead of the q staging, so the
     // page loop has no dependent page-table load
-    const int nw = pend > pg0 + wave ? (int)((pend - pg0 - wave + kWaves - 1) / kWaves) : 0;
+    // The filter pass skips the pages the sample pass scored (one in S, their scores are in
+    // `logits`, bit-identical to a rescoring) when S divides the chunk: page j of the scored
+    // sequence is then the j-th page of [pg0, pend) that is not a multiple of S.
+    constexpr int S = kTopkSampleStep;
+    const bool skip = KIND == kLogitsFilter && md.sampled_step == S && chunk_pages % S == 0;
+    const int nchunk = (int)(pend - pg0);                                  // <= chunk_pages <= 128
+    const int nsamp = skip ? (nchunk + S - 1) / S : 0;
+    auto scored_page = [&](int j) -> int64_t { return pg0 + (skip ? (j / (S - 1)) * S + 1 + j % (S - 1) : j); };
+    const int nscored = nchunk - nsamp;
+    const int nw = nscored > wave ? (nscored - wave + kWaves - 1) / kWaves : 0;
     int my_id = -1;
-    if (lane < nw) my_id = (int)page_of(pg, rq, (pg0 + wave + (int64_t)kWaves * lane) * step * 64);
+    if (lane < nw) my_id = (int)page_of(pg, rq, scored_page(wave + kWaves * lane) * step * 64);
     // stage q (RG x 32 heads x 128 B, 16-B chunks swizzled by row) and w*q_scale in LDS; the
     // MFMA A operands and head weights are re-read from LDS for every page, which keeps the
     // register file small enough for four waves per SIMD
@@ -206,6 +215,25 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     // group's rows (only kept when the fused top-k asked for row ranges; a range covering a
     // row's keys is all the radix select needs, so the group's union serves each of its rows)
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    auto key_of = [](float x) {
+      const uint32_t u = __float_as_uint(x);
+      return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    };
+    // filter mode: one kept (key, position) of row r into the work-group's stage
+    auto stage = [&](int r, int s, uint32_t key) {
+      const int sl = atomicAdd(&st_n[r], 1);
+      if (sl < kStage) {
+        st_key[r][sl] = key;
+        st_pos[r][sl] = s;
+      } else {
+        // stage full: straight to the row's list (a count past fcap still flags the row)
+        const int gi = atomicAdd(&md.fcnt[row0 + r], 1);
+        if (gi < md.fcap) {
+          md.fkey[(row0 + r) * md.fcap + gi] = key;
+          md.fpos[(row0 + r) * md.fcap + gi] = s;
+        }
+      }
+    };
     // score one page (held in registers) for all RG rows
     auto process = [&](const PageRegs<FMT>& P, int64_t vi, int64_t pid) {
       // keep the per-page LDS reads of q / w inside the loop (hoisting them would pin all
@@ -249,27 +277,9 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         const float mine = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
         const bool vis = pid >= 0 && s <= prow[r];        // pid < 0: a bad page id (flagged)
         const float v = vis ? mine * key_scale(P) : -INFINITY;
-        auto key_of = [](float x) {
-          const uint32_t u = __float_as_uint(x);
-          return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-        };
         if (KIND == kLogitsFilter) {
           // keep the scores at or above the row's threshold (rare: a few per cent)
-          if (vis && v >= thr_f[r]) {
-            const uint32_t key = key_of(v);
-            const int sl = atomicAdd(&st_n[r], 1);
-            if (sl < kStage) {
-              st_key[r][sl] = key;
-              st_pos[r][sl] = s;
-            } else {
-              // stage full: straight to the row's list (a count past fcap still flags the row)
-              const int gi = atomicAdd(&md.fcnt[row0 + r], 1);
-              if (gi < md.fcap) {
-                md.fkey[(row0 + r) * md.fcap + gi] = key;
-                md.fpos[(row0 + r) * md.fcap + gi] = s;
-              }
-            }
-          }
+          if (vis && v >= thr_f[r]) stage(r, s, key_of(v));
         } else {
           // nontemporal: 5% off the c2 logits pass, and the top-k that reads them back is no slower
           __builtin_nontemporal_store(v, &logits[(row0 + r) * stride + s]);
@@ -288,7 +298,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     PageRegs<FMT> pa, pb;
     auto page_addr = [&](int id) { return cache + (int64_t)(id < 0 ? 0 : id) * kPageBytes<FMT>; };
     auto page_id = [&](int i) { return __builtin_amdgcn_readlane(my_id, min(i, nw - 1)); };
-    auto page_vi = [&](int i) { return pg0 + wave + (int64_t)kWaves * i; };
+    auto page_vi = [&](int i) { return scored_page(wave + kWaves * i); };
     if (nw > 0) {
       int ida = page_id(0);
       load_page(pa, page_addr(ida), lane);
@@ -302,6 +312,16 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         process(pb, page_vi(i + 1), idb);
       }
       if (i < nw) process(pa, page_vi(i), ida);     // an odd page count: the last page
+    }
+    // the sampled pages of the chunk: their stored scores against the threshold (a page of a
+    // bad id holds -inf)
+    for (int m = wave; m < nsamp; m += kWaves) {
+      const int s = (int)((pg0 + (int64_t)m * S) * 64) + lane;
+#pragma unroll
+      for (int r = 0; r < RG; r++) {
+        const float v = logits[(row0 + r) * stride + s];
+        if (s <= prow[r] && v >= thr_f[r]) stage(r, s, key_of(v));
+      }
     }
     if (kRange && md.range != nullptr) {
       __shared__ uint32_t red[kWaves][2];

@@ -713,6 +713,7 @@ LogitsMode topk_filter_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto) {
   m.fkey = w.ckey;
   m.fpos = w.cpos;
   m.fcap = kCap;
+  m.sampled_step = kTopkSampleStep;
   return m;
 }
 
