@@ -206,6 +206,27 @@ def test_context_sweep_single_request(ctx):
     _release(L)
 
 
+@pytest.mark.parametrize("ctx,rows", [(16384, 6), (131072, 6), (131072, 1), (50000, 3)])
+def test_fused_equals_separate_where_sampled_pages_are_reused(ctx, rows):
+    """Filter chunks of 16 pages or more: the filter pass takes the sampled pages' scores from the
+    sample pass instead of scoring them again.  The selection must be exactly that of the
+    separate logits + top-k calls (three requests of different lengths, `rows` rows each)."""
+    _announce(f"fused == separate with sampled pages reused: ctx {ctx}, {rows} rows per request")
+    w = gi.make_decode(f"reuse_{ctx}_{rows}", gi.SEED_BASE + 51, [ctx, ctx - 777, 3 * ctx // 4],
+                       rows_per_req=rows)
+    L = DeviceLayer(w)
+    dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
+    L.indexer_topk(0)
+    torch.cuda.synchronize()
+    fused = host(L.idx).copy()
+    dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
+    dsa.dsa_topk(L.logits, L.rows, 2048, L.idx, L.ws_topk)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(L.idx), fused)
+    dsa.dsa_check_device_errors()
+    _release(L)
+
+
 SAMPLE_STEP = 16    # the fused path scores one page in SAMPLE_STEP to set its filter threshold
 
 
