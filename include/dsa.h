@@ -273,7 +273,11 @@ dsa_status dsa_indexer_topk_mxfp4(const uint8_t* q_fp8, const float* q_scale, co
 /* ---------------------------------------------------------------- sparse MLA */
 
 /* Workspace for dsa_sparse_mla_decode / _prefill, in bytes (may be 0).  Its contents need no
- * initialisation; calls that share one workspace must not overlap. */
+ * initialisation: with 256 rows or more, rows split between two work-groups are merged through
+ * per-slot tag words that each call sets to a random 64-bit value and clears again before it
+ * ends, so a workspace can be reused by any number of calls, also from a captured graph
+ * replayed many times.  Calls that share one workspace must not overlap (on one stream, or
+ * ordered by events). */
 size_t dsa_sparse_mla_workspace_size(int32_t R, int32_t k);
 
 /* Sparse MLA in absorbed (MQA) form ([VLLM] §Sparse MLA Attention; [REQ]

@@ -116,6 +116,17 @@ __device__ inline f32x4 mfma_tile(const i32x8& a, const PageRegs<kIdxMxfp4>& P) 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, T, P.sb);
 }
 
+// The VALU reads the two results of a tile right after their MFMAs.  For the block-scaled
+// FP8 x FP4 product a probe on this device read a scaled result too early after the 10-11 wait
+// states the compiler puts in for an 8-pass MFMA, so there the wait is explicit: 20 wait states
+// after the second MFMA (what a 16-pass MFMA needs), tied to both results' registers so that
+// every read of them comes after it.  The unscaled FP8 product needs no more than the
+// compiler's wait.
+template <int FMT>
+__device__ inline void mfma_results_ready(f32x4& c0, f32x4& c1) {
+  if (FMT == kIdxMxfp4) __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(c0), "+v"(c1));
+}
+
 // tile index as a run-time value; the unrolled callers make it a constant
 template <int FMT>
 __device__ inline f32x4 mfma_tile_at(int t, const i32x8& a, const PageRegs<FMT>& P) {
@@ -162,8 +173,9 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     if (KIND == kLogitsFallback) flagged |= md.flag[row0 + r] != 0;
   }
   // every row of the group sees at most skip_upto keys: its top-k is all of them and needs
-  // no score (the fused indexer + top-k passes k here; nothing of the group is written)
-  if (pmax + 1 <= md.skip_upto) return;
+  // no score (the fused indexer + top-k passes k here; nothing of the group is written).  In
+  // the plain pass (skip_upto 0) a group of padded rows (pos < 0) goes on to the -inf fill.
+  if (md.skip_upto > 0 && pmax + 1 <= md.skip_upto) return;
   if (KIND == kLogitsFallback && !flagged) return;     // no row of the group needs the full scores
   // the rows' thresholds as floats: for a finite score v, key(v) >= thr exactly when
   // v >= thr_f, except that -0.0 also passes a threshold of +0.0 (a superset of the candidates;
@@ -255,8 +267,9 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         float part[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-          const f32x4 c0 = mfma_tile_at(t, A[0], P);
-          const f32x4 c1 = mfma_tile_at(t, A[1], P);
+          f32x4 c0 = mfma_tile_at(t, A[0], P);
+          f32x4 c1 = mfma_tile_at(t, A[1], P);
+          mfma_results_ready<FMT>(c0, c1);
           float acc = wr[0].x * relu(c0[0]);
           acc = fmaf(wr[0].y, relu(c0[1]), acc);
           acc = fmaf(wr[0].z, relu(c0[2]), acc);
@@ -320,7 +333,9 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
 #pragma unroll
       for (int r = 0; r < RG; r++) {
         const float v = logits[(row0 + r) * stride + s];
-        if (s <= prow[r] && v >= thr_f[r]) stage(r, s, key_of(v));
+        // -inf: a page whose id failed the range check (a visible key's score is finite); the
+        // scored path never stages those, whatever the threshold
+        if (s <= prow[r] && v > -INFINITY && v >= thr_f[r]) stage(r, s, key_of(v));
       }
     }
     if (kRange && md.range != nullptr) {

@@ -27,7 +27,10 @@
 //    and a combine kernel merges the splits; with one split the kernel normalises and writes
 //    bf16.  Many rows: a stream-K schedule, one persistent work-group per CU over equal
 //    ranges of all rows' tiles; a row cut between two work-groups is merged by the second.
+#include <unistd.h>
+
 #include <atomic>
+#include <chrono>
 
 #include "dsa_device.hpp"
 #include "dsa_internal.h"
@@ -671,10 +674,12 @@ __device__ __attribute__((noinline)) void mla_segment_call(const uint16_t* q, co
 // gridDim.x equal consecutive ranges, one per work-group, each covering at least one full
 // row; a work-group runs its range as row segments.  A row cut between work-groups g-1 and
 // g (never more than two parts) leaves one partial from each in slot g; each writer waits
-// for its coherent partial stores to complete, then tags the slot with this launch's number,
-// and the writer that finds the tag already there merges both parts (no work-group ever waits
-// for another).  Tags replace clearing the slots before each launch: 0 is never a tag, and a
-// slot left by an earlier launch holds that launch's (smaller) tag.
+// for its coherent partial stores to complete, then swaps the launch's tag into the slot's
+// tag word, and the writer that gets the tag back is the second: it merges both parts (no
+// work-group ever waits for another) and clears the word again.  Every launch so leaves its
+// slots cleared, which keeps a captured graph correct on every replay (its tag is fixed at
+// capture), and the tag is a random 64-bit value, never 0, so a word left in recycled memory
+// matches it only with probability 2^-64: the workspace needs no initialisation.
 __global__ void __launch_bounds__(kThreads)
 k_sparse_mla_stream(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, const int32_t* __restrict__ pos,
                     DevPages pg, const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx, int32_t k,
@@ -701,18 +706,17 @@ k_sparse_mla_stream(const uint16_t* __restrict__ q, const int32_t* __restrict__ 
       wait_vmcnt<0>();                          // this thread's part of the partial is stored ...
       __syncthreads();
       if (threadIdx.x == 0) {                   // ... before the part is tagged
-        // exactly two parts per cut row and launch: the writer that swaps this launch's tag
-        // in is the first; the other finds it there and is the second
-        const unsigned long long old = __hip_atomic_load(&tag[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        unsigned long long seen = old;
-        if (old != launch)
-          seen = __hip_atomic_compare_exchange_strong(&tag[slot], &seen, launch, __ATOMIC_RELAXED,
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                     ? old : seen;
-        s_old = seen == launch;
+        // exactly two parts per cut row and launch: the first writer swaps the tag in and gets
+        // the slot's old word back; the second gets the tag
+        const unsigned long long old =
+            __hip_atomic_exchange(&tag[slot], launch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_old = old == launch;
       }
       __syncthreads();
-      if (s_old) merge_two_parts(po, pml, r, out, lse);   // both parts are in: merge them
+      if (s_old) {                              // both parts are in: merge them, clear the slot
+        merge_two_parts(po, pml, r, out, lse);
+        if (threadIdx.x == 0) __hip_atomic_store(&tag[slot], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       __syncthreads();
     }
     u += t1 - t0;
@@ -753,6 +757,25 @@ int choose_splits(int32_t R, int32_t k) {
 
 constexpr int kStreamGroups = 256;              // one persistent work-group per CU (LDS-bound)
 
+// SplitMix64 finaliser (Steele, Lea and Flood 2014): spreads a counter over 64 bits.
+uint64_t mix64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+// Merge tag of one stream-K launch: a per-process random salt (clock, process id, address
+// layout) mixed with a launch counter; never 0, the cleared state of a slot.
+unsigned long long stream_merge_tag() {
+  static const uint64_t salt =
+      mix64((uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count() ^
+            ((uint64_t)getpid() << 32) ^ (uint64_t)(uintptr_t)&kStreamGroups);
+  static std::atomic<uint64_t> launches{0};
+  const uint64_t t = mix64(salt + launches.fetch_add(1));
+  return t ? t : 1;
+}
+
 }  // namespace
 
 size_t mla_workspace_bytes(int32_t R, int32_t k) {
@@ -776,8 +799,7 @@ hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, con
     float* wo = (float*)ws;
     float* wml = wo + (size_t)slots * 2 * kHeads * kVal;
     unsigned long long* tag = (unsigned long long*)(wml + (size_t)slots * 2 * kHeads * 2);   // 8-B aligned
-    static std::atomic<unsigned long long> launches{0};
-    const unsigned long long launch = ++launches;      // >= 1, increasing
+    const unsigned long long launch = stream_merge_tag();
     hipLaunchKernelGGL(k_sparse_mla_stream, dim3(kStreamGroups), dim3(kThreads), 0, s, q, rows.req, rows.pos, g,
                        cache, idx, k, R, sm_log2, out, lse, wo, wml, tag, launch);
     return hipGetLastError();

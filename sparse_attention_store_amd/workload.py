@@ -120,6 +120,16 @@ class DeviceLayer:
                     out[i] = torch.from_numpy(self.k_overrides[int(pos[i])].view(np.int16)).to(self.device)
         return out
 
+    def _raw_keys(self, b: int, p0: int, p1: int) -> torch.Tensor:
+        """Raw index keys of positions p0..p1-1 of request b, with the planted overrides."""
+        n = p1 - p0
+        k = self._gen(gi.T_RAW_K, (int(self.token_base[b]) + p0) * 128, n * 128).view(n, 128)
+        if b == 0 and self.k_overrides:
+            for p, v in self.k_overrides.items():
+                if p0 <= p < p1:
+                    k[p - p0] = torch.from_numpy(v.view(np.int16)).to(self.device)
+        return k
+
     def populate(self):
         """Store every context position of every request into all caches."""
         w = self.w
@@ -132,11 +142,7 @@ class DeviceLayer:
                 pos = torch.arange(p0, p1, dtype=torch.int32, device=self.device)
                 rows = dsa.Rows(req, pos, p1 - 1)
                 for l in w.full_layers:
-                    k = self._gen(gi.T_RAW_K, (int(self.token_base[b]) + p0) * 128, n * 128).view(n, 128)
-                    if b == 0 and self.k_overrides:
-                        for p, v in self.k_overrides.items():
-                            if p0 <= p < p1:
-                                k[p - p0] = torch.from_numpy(v.view(np.int16)).to(self.device)
+                    k = self._raw_keys(b, p0, p1)
                     dsa.dsa_index_k_store(k, rows, self.pages, self.index_cache[l], LN_EPS, ROPE_THETA)
                 for l in self.layers:
                     kv = self._gen(gi.T_LATENT0 + l, (int(self.token_base[b]) + p0) * 576, n * 576).view(n, 576)
@@ -154,7 +160,7 @@ class DeviceLayer:
                 n = p1 - p0
                 req = torch.full((n,), b, dtype=torch.int32, device=self.device)
                 pos = torch.arange(p0, p1, dtype=torch.int32, device=self.device)
-                k = self._gen(gi.T_RAW_K, (int(self.token_base[b]) + p0) * 128, n * 128).view(n, 128)
+                k = self._raw_keys(b, p0, p1)
                 dsa.dsa_index_k_store_mxfp4(k, dsa.Rows(req, pos, p1 - 1), self.pages, cache, LN_EPS, ROPE_THETA)
         torch.cuda.synchronize()
         return cache

@@ -206,14 +206,41 @@ def test_context_sweep_single_request(ctx):
     _release(L)
 
 
-@pytest.mark.parametrize("ctx,rows", [(16384, 6), (131072, 6), (131072, 1), (50000, 3)])
-def test_fused_equals_separate_where_sampled_pages_are_reused(ctx, rows):
-    """Filter chunks of 16 pages or more: the filter pass takes the sampled pages' scores from the
-    sample pass instead of scoring them again.  The selection must be exactly that of the
-    separate logits + top-k calls (three requests of different lengths, `rows` rows each)."""
-    _announce(f"fused == separate with sampled pages reused: ctx {ctx}, {rows} rows per request")
-    w = gi.make_decode(f"reuse_{ctx}_{rows}", gi.SEED_BASE + 51, [ctx, ctx - 777, 3 * ctx // 4],
-                       rows_per_req=rows)
+def filter_pass_chunk(rows_per_group, max_pos, n_groups, fcap=4096, want=2048):
+    """Pages per work-group of the fused call's filter pass, as libdsa's launcher picks them: the
+    stage of a row group (768 / RG candidates per row up to six rows, 104 for the eight-row
+    sub-groups of a long group) bounds the chunk to what a row's share of fcap candidates fits,
+    then the chunk halves while fewer than `want` work-groups would run."""
+    stage = 768 // rows_per_group if rows_per_group <= 6 else 104
+    lim = stage * (max_pos + 1) // (fcap * 64)
+    chunk = next((c for c in (128, 64, 32, 16, 8) if lim >= c), 4)
+    total_pages = dsa.dsa_logits_stride(max_pos) // 64
+    while chunk > 4 and n_groups * -(-total_pages // chunk) < want:
+        chunk //= 2
+    return chunk
+
+
+# decode / verify batches whose filter chunks are multiples of 16, and a prefill chunk whose long
+# group runs in eight-row sub-groups
+REUSE_CASES = [("verify_16x6_128k", [131072] * 16, 6), ("verify_64x6_32k", [32768] * 64, 6),
+               ("decode_32x1_128k", [131072 - 5000 * (b % 3) for b in range(32)], 1),
+               ("verify_48x3_64k", [65536 - 64 * b for b in range(48)], 3), ("prefill_45000_512", None, 512)]
+
+
+@pytest.mark.parametrize("name,ctx,rows", REUSE_CASES, ids=[c[0] for c in REUSE_CASES])
+def test_fused_equals_separate_where_sampled_pages_are_reused(name, ctx, rows):
+    """Filter chunks of 16 pages or more (a multiple of the sampling step): the filter pass takes
+    the sampled pages' scores from the sample pass instead of scoring them again.  The selection
+    must be exactly that of the separate logits + top-k calls."""
+    _announce(f"fused == separate with sampled pages reused: {name}")
+    if ctx is None:
+        w = gi.make_prefill(name, gi.SEED_BASE + 51, 45000, rows)
+        rg, n_groups = 8, rows // 8
+    else:
+        w = gi.make_decode(name, gi.SEED_BASE + 51, ctx, rows_per_req=rows)
+        rg, n_groups = rows, len(ctx)
+    chunk = filter_pass_chunk(rg, w.max_pos, n_groups)
+    assert chunk >= 16 and chunk % 16 == 0, f"filter chunk {chunk}: the sampled-page reuse would not run"
     L = DeviceLayer(w)
     dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
     L.indexer_topk(0)

@@ -136,3 +136,74 @@ def test_mxfp4_store_special_keys():
     diff = np.argwhere(got != ref)
     assert len(diff) == 0, f"{len(diff)} bytes differ, first at {diff[:5].tolist()}"
     assert got[0, 4096] == 127 and not got[0, :64].any()     # the constant key
+
+
+# ----------------------------------------------------------------------------- full size
+def oracle_mx_cache_of(w, b, overrides=None):
+    """Request b's MXFP4 index-K cache alone, in a compact pool (page i of the request is pool
+    page i; scores do not depend on page placement)."""
+    L = int(w.ctx[b])
+    npg = (L + 63) // 64
+    pt = np.arange(npg, dtype=np.int32)[None, :]
+    k = gi.normal_bf16(w.seed, gi.T_RAW_K, int(w.token_base[b]) * 128, L * 128).reshape(L, 128)
+    for p, v in (overrides or {}).items() if b == 0 else ():
+        k[p] = v
+    cache = np.zeros((npg, MX_PAGE), np.uint8)
+    orc.index_k_store_mxfp4(k, np.zeros(L, np.int32), np.arange(L, dtype=np.int32), pt, cache, LN_EPS, THETA)
+    return cache, pt
+
+
+def _full_size_mx(w, sample_reqs, overrides=None):
+    """The benchmark's launch configuration on the whole batch (every request stored, scored and
+    selected on the GPU), checked against the oracle on the sampled requests' rows: logits
+    element-wise, the fused and the separate selections against the oracle's sets."""
+    from parity import row_queries
+    from sparse_attention_store_amd.workload import DeviceLayer
+    L = DeviceLayer(w, latent_layers=[], k_overrides=overrides)
+    cache = L.build_mxfp4_index(0)
+    dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
+    dsa.dsa_indexer_topk_mxfp4(L.q8, L.qs, L.w_head, L.rows, L.pages, cache, L.logits, 2048, L.idx, L.ws_topk)
+    torch.cuda.synchronize()
+    fused = host(L.idx).copy()
+    dsa.dsa_indexer_logits_mxfp4(L.q8, L.qs, L.w_head, L.rows, L.pages, cache, L.logits)
+    torch.cuda.synchronize()
+    n_same = n_rows = 0
+    for b in sample_reqs:
+        rs = np.where(w.row_req == b)[0]
+        mx, pt = oracle_mx_cache_of(w, b, overrides)
+        q, wt, _ = row_queries(w, rs, [])
+        q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+        pos = w.row_pos[rs]
+        ref = orc.indexer_logits_mxfp4(q8.reshape(-1, 32, 128), qs.reshape(-1, 32), wt, np.zeros(len(rs), np.int32),
+                                       pos, pt, mx)
+        got = host(L.logits[torch.as_tensor(rs, device=DEV)])
+        ow = ref.shape[1]
+        assert_logits_close(got[:, :ow], ref)
+        assert np.all(np.isneginf(got[:, ow:]))
+        ridx, kth = orc.topk(ref, pos, 2048)
+        topk_sets_match(fused[rs], ridx, ref, kth)
+        n_same += sum(set(fused[r]) == set(ridx[i]) for i, r in enumerate(rs))
+        n_rows += len(rs)
+    # the separate radix top-k over the same GPU scores selects exactly what the fused call did
+    dsa.dsa_topk(L.logits, L.rows, 2048, L.idx, L.ws_topk)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(L.idx), fused)
+    dsa.dsa_check_device_errors()
+    del L, cache
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return n_same, n_rows
+
+
+def test_mxfp4_full_c2_verify_128k_sampled_requests():
+    _announce("mxfp4 full size c2: 64 x 6 rows at 128K, 6 sampled requests")
+    w = gi.config(2, "full")
+    n_same, n = _full_size_mx(w, [0, 1, 31, 32, 62, 63])
+    assert n_same >= 0.9 * n, f"only {n_same}/{n} rows have the oracle's exact set"
+
+
+def test_mxfp4_full_c3_long_1m():
+    _announce("mxfp4 full size c3: 1 request at 1M context (needle keys stored as MXFP4)")
+    from parity import needle_overrides
+    w = gi.config(3, "full")
+    _full_size_mx(w, [0], needle_overrides(w))          # the set differs only at near-ties
