@@ -300,6 +300,23 @@ dsa_status dsa_sparse_mla_prefill(const uint16_t* q_bf16, const dsa_rows* rows, 
                                   float sm_scale, uint16_t* out_bf16, float* lse,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* dsa_sparse_mla_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It computes the same function as dsa_sparse_mla_decode, within the same
+ * tolerance (fewer than 256 rows may run in fewer splits).  Its scratch is a fixed array of
+ * 67,636,232 B (64.5 MiB) in device memory, one per GPU, that the library holds from the first
+ * call on that GPU until the process ends; the call itself allocates nothing (no hipMalloc or
+ * allocating library routine).  The array serves any row count: 256 rows or more take the
+ * stream-K schedule, whose need is exactly its size; fewer rows take at most as many splits as
+ * it holds.  A need beyond the array returns DSA_ERR_WORKSPACE before any launch.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (on different streams, or from
+ * different threads, without ordering) race and give wrong results; calls ordered on one stream
+ * do not.  The array keeps the last call's contents; no call needs it cleared.  The current
+ * device must be the GPU of `stream`.  Arguments and other errors as dsa_sparse_mla_decode. */
+dsa_status dsa_sparse_mla_decode_noalloc(const uint16_t* q_bf16, const dsa_rows* rows, const dsa_pages* pt,
+                                         const uint8_t* latent_cache, const int32_t* idx, int32_t k,
+                                         float sm_scale, uint16_t* out_bf16, float* lse, void* stream);
+
 /* ---------------------------------------------------------------- diagnostics */
 
 /* Synchronises the current device and reports (then clears) the device error flag

@@ -320,6 +320,33 @@ dsa_status dsa_sparse_mla_prefill(const uint16_t* q, const dsa_rows* rows, const
                     "dsa_sparse_mla_prefill");
 }
 
+dsa_status dsa_sparse_mla_decode_noalloc(const uint16_t* q, const dsa_rows* rows, const dsa_pages* pt,
+                                         const uint8_t* cache, const int32_t* idx, int32_t k, float sm_scale,
+                                         uint16_t* out, float* lse, void* stream) {
+  const char* what = "dsa_sparse_mla_decode_noalloc";
+  dsa_status st = check_rows(rows, what, false);
+  if (st) return st;
+  if (k < 1 || k > DSA_TOPK_MAX) return fail(DSA_ERR_ARG, "%s: k = %d not in [1, %d]", what, k, DSA_TOPK_MAX);
+  if (rows->n == 0) return DSA_OK;
+  if ((st = check_pages(pt, rows->max_pos, what))) return st;
+  if (!q || !cache || !idx || !out) return fail(DSA_ERR_ARG, "%s: NULL pointer", what);
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(idx, 4) || (lse && !aligned(lse, 4)))
+    return fail(DSA_ERR_ARG, "%s: misaligned pointer", what);
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return fail(DSA_ERR_ARG, "%s: sm_scale must be > 0", what);
+  // the fixed array serves the stream-K schedule (256 rows or more) in full; fewer rows take
+  // as many splits as it holds.  A need beyond it is refused before anything runs.
+  const size_t cap = dsa::mla_static_scratch_bytes();
+  if (rows->n >= 256 && dsa::mla_workspace_bytes(rows->n, k) > cap)
+    return fail(DSA_ERR_WORKSPACE, "%s: %d rows need %zu B of scratch, the fixed array holds %zu B", what, rows->n,
+                dsa::mla_workspace_bytes(rows->n, k), cap);
+  void* ws = nullptr;
+  hipError_t e = dsa::mla_static_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "dsa_sparse_mla_decode_noalloc: scratch address");
+  return hip_status(dsa::launch_sparse_mla(q, view(rows), view(pt), cache, idx, k, sm_scale, out, lse, ws, cap, false,
+                                           (hipStream_t)stream),
+                    what);
+}
+
 dsa_status dsa_check_device_errors(void) {
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_status(e, "dsa_check_device_errors");

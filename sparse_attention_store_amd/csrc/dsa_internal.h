@@ -95,6 +95,10 @@ hipError_t launch_topk_fallback(const float* logits, int64_t stride, RowsView ro
                                 void* ws, hipStream_t s);
 
 size_t mla_workspace_bytes(int32_t R, int32_t k);
+// The allocation-free entry point's fixed scratch: its size, and its device address on the
+// current device (looked up once per device).
+size_t mla_static_scratch_bytes();
+hipError_t mla_static_scratch(void** ptr);
 hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, const uint8_t* cache,
                              const int32_t* idx, int32_t k, float sm_scale, uint16_t* out, float* lse,
                              void* ws, size_t ws_bytes, bool prefill, hipStream_t s);

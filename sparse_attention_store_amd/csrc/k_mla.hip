@@ -31,6 +31,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 
 #include "dsa_device.hpp"
 #include "dsa_internal.h"
@@ -748,10 +749,14 @@ __global__ void __launch_bounds__(128) k_mla_combine(const float* __restrict__ w
     lse[(int64_t)r * kHeads + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-int choose_splits(int32_t R, int32_t k) {
-  // enough work-groups to cover 256 CUs a few times over; at least 64 keys per split
+constexpr size_t kSplitPartBytes = (size_t)kHeads * (kVal + 2) * sizeof(float);   // O, m, l of one split
+
+int choose_splits(int32_t R, int32_t k, size_t ws_cap = SIZE_MAX) {
+  // enough work-groups to cover 256 CUs a few times over; at least 64 keys per split; no more
+  // splits than a workspace of ws_cap bytes holds
   int s = 1;
-  while (s < 32 && (int64_t)R * s < 512 && k / (2 * s) >= 64) s <<= 1;
+  while (s < 32 && (int64_t)R * s < 512 && k / (2 * s) >= 64 && (size_t)R * (2 * s) * kSplitPartBytes <= ws_cap)
+    s <<= 1;
   return s;
 }
 
@@ -783,7 +788,7 @@ size_t mla_workspace_bytes(int32_t R, int32_t k) {
     return (size_t)(kStreamGroups + 1) * (2 * kHeads * (kVal + 2) * sizeof(float) + sizeof(unsigned long long));
   const int s = choose_splits(R, k);
   if (s == 1) return 0;
-  return (size_t)R * s * kHeads * (kVal + 2) * sizeof(float);
+  return (size_t)R * s * kSplitPartBytes;
 }
 
 hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, const uint8_t* cache,
@@ -804,14 +809,16 @@ hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, con
                        cache, idx, k, R, sm_log2, out, lse, wo, wml, tag, launch);
     return hipGetLastError();
   }
-  const int nsplit = choose_splits(R, k);
+  // a workspace of at least mla_workspace_bytes(R, k) gives the full split count; a smaller one
+  // (the allocation-free entry point's fixed array) caps it
+  const int nsplit = choose_splits(R, k, ws == nullptr ? 0 : ws_bytes);
   const int kps = (k + nsplit - 1) / nsplit;
   if (nsplit == 1) {
     hipLaunchKernelGGL(k_sparse_mla, dim3(1, R), dim3(kThreads), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
                        kps, sm_log2, out, lse, nullptr, nullptr);
     return hipGetLastError();
   }
-  if (ws == nullptr || ws_bytes < mla_workspace_bytes(R, k)) return hipErrorInvalidValue;
+  if (ws == nullptr || ws_bytes < (size_t)R * nsplit * kSplitPartBytes) return hipErrorInvalidValue;
   float* wo = (float*)ws;
   float* wml = wo + (size_t)R * nsplit * kHeads * kVal;
   hipLaunchKernelGGL(k_sparse_mla, dim3(nsplit, R), dim3(kThreads), 0, s, q, rows.req, rows.pos, g, cache, idx, k,
@@ -820,6 +827,41 @@ hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, con
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_mla_combine, dim3(kHeads, R), dim3(128), 0, s, wo, wml, nsplit, out, lse);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// Scratch of dsa_sparse_mla_decode_noalloc: a fixed array in device memory, one per GPU the
+// library runs on, held until the process ends.  Its size is the stream-K schedule's need
+// (two partials and a tag word for each of the 257 slots), which serves every row count of 256
+// or more; fewer rows take at most as many splits as it holds.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol): kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes =
+    (size_t)(kStreamGroups + 1) * (2 * kSplitPartBytes + sizeof(unsigned long long));
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];          // device address of `scratch` per device, once looked up
+}  // namespace
+
+size_t mla_static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t mla_static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));     // with device `dev` current
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 DSA_DEFINE_ERROR_ACCESSOR(take_device_errors_mla)

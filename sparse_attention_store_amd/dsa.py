@@ -78,6 +78,7 @@ def _load():
         "dsa_sparse_mla_workspace_size": ([i32, i32], sz),
         "dsa_sparse_mla_decode": ([p, R, P, p, p, i32, f32, p, p, p, sz, p], ctypes.c_int),
         "dsa_sparse_mla_prefill": ([p, R, P, p, p, i32, f32, p, p, p, sz, p], ctypes.c_int),
+        "dsa_sparse_mla_decode_noalloc": ([p, R, P, p, p, i32, f32, p, p, p], ctypes.c_int),
         "dsa_check_device_errors": ([], ctypes.c_int),
     }
     for name, (args, ret) in sigs.items():
@@ -93,7 +94,8 @@ EXPORTED = ("dsa_abi_version", "dsa_last_error", "dsa_layer_is_shared", "dsa_mtp
             "dsa_index_k_store", "dsa_index_k_store_mxfp4", "dsa_latent_store", "dsa_fused_norm_rope_store", "dsa_logits_stride",
             "dsa_logits_rows_per_chunk", "dsa_indexer_logits", "dsa_indexer_logits_mxfp4", "dsa_topk_workspace_size",
             "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_mxfp4", "dsa_sparse_mla_workspace_size",
-            "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_check_device_errors")
+            "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_sparse_mla_decode_noalloc",
+            "dsa_check_device_errors")
 
 
 def _check(st: int):
@@ -261,6 +263,13 @@ def dsa_sparse_mla_decode(q, rows: Rows, pages: Pages, latent_cache, idx, out, l
 def dsa_sparse_mla_prefill(q, rows: Rows, pages: Pages, latent_cache, idx, out, lse=None, ws=None,
                            sm_scale=1.0 / 16.0, stream=None):
     _mla(_lib.dsa_sparse_mla_prefill, q, rows, pages, latent_cache, idx, sm_scale, out, lse, ws, stream)
+
+
+def dsa_sparse_mla_decode_noalloc(q, rows: Rows, pages: Pages, latent_cache, idx, out, lse=None, sm_scale=1.0 / 16.0,
+                                  stream=None):
+    r, p = rows.c(), pages.c()
+    _check(_lib.dsa_sparse_mla_decode_noalloc(_ptr(q), ctypes.byref(r), ctypes.byref(p), _ptr(latent_cache), _ptr(idx),
+                                              idx.shape[-1], sm_scale, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def dsa_check_device_errors():
