@@ -255,7 +255,9 @@ dsa_status dsa_topk(const float* logits, int64_t stride, const dsa_rows* rows, i
  * depends on the sample.  `logits` is scratch: on return it holds the sampled pages'
  * scores and the full scores of rows that fell back; other entries are unspecified.  A
  * row group (rows->group consecutive rows) whose rows all have pos + 1 <= k is not scored
- * ([IDXC] §优化二:短上下文直接跳过打分).  Arguments as for the two calls; ws sized by
+ * ([IDXC] §优化二:短上下文直接跳过打分).  A call whose R x stride is at most 4096 scores
+ * writes every score and takes the radix top-k directly (the filter's extra steps cost more
+ * than they save there); the result is the same.  Arguments as for the two calls; ws sized by
  * dsa_topk_workspace_size(R, stride, k).  index_cache must not be NULL (a shared layer
  * reuses the full layer's idx instead). */
 dsa_status dsa_indexer_topk(const uint8_t* q_fp8, const float* q_scale, const float* w,

@@ -205,6 +205,13 @@ dsa_status dsa_indexer_logits_mxfp4(const uint8_t* q8, const float* qs, const fl
                              "dsa_indexer_logits_mxfp4");
 }
 
+// Score-array size (rows x stride) up to which the fused indexer + top-k writes every score and
+// takes the radix passes directly instead of the sampled-threshold filter.
+#ifndef DSA_INDEXER_TOPK_DIRECT
+#define DSA_INDEXER_TOPK_DIRECT 4096
+#endif
+constexpr int64_t kIndexerTopkDirect = DSA_INDEXER_TOPK_DIRECT;
+
 static dsa_status indexer_topk_impl(const uint8_t* q8, const float* qs, const float* w, const dsa_rows* rows,
                                     const dsa_pages* pt, const uint8_t* cache, float* logits, int64_t stride,
                                     int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream, int fmt,
@@ -233,7 +240,19 @@ static dsa_status indexer_topk_impl(const uint8_t* q8, const float* qs, const fl
   const dsa::RowsView rv = view(rows);
   const dsa::PagesView pv = view(pt);
   const int R = rows->n;
-  hipError_t e = dsa::launch_topk_init(R, k, ws, s);
+  if ((int64_t)R * stride <= kIndexerTopkDirect) {
+    // few scores: writing them all and selecting with the radix passes costs less than the
+    // filtered path's extra launches and single-work-group steps.  Every row is flagged, so the
+    // exact path's kernels (full scores with the row ranges, histogram, select, final) take it;
+    // row groups whose rows are all short are still not scored.
+    hipError_t e = dsa::launch_topk_init(R, k, ws, s, true);
+    if (e == hipSuccess)
+      e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_fallback_mode(ws, R, k, k), fmt,
+                                     s);
+    if (e == hipSuccess) e = dsa::launch_topk_fallback(logits, stride, rv, k, idx, ws, s);
+    return hip_status(e, name);
+  }
+  hipError_t e = dsa::launch_topk_init(R, k, ws, s, false);
   if (e == hipSuccess)
     e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_sample_mode(ws, R, k, k), fmt, s);
   if (e == hipSuccess) e = dsa::launch_topk_threshold(logits, stride, rv, k, ws, s);

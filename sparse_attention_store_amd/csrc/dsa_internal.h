@@ -83,14 +83,15 @@ hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32
 //  flagging rows whose candidate list is short or overflowed; for the flagged rows only,
 //  full scores (logits kernel, fallback mode) and the radix top-k passes.
 constexpr int kTopkSampleStep = 16;        // one page in sixteen is sampled
-hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s);
+// flag_all: every row is flagged for the radix passes (the fused call's small-array path)
+hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s, bool flag_all);
 LogitsMode topk_sample_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto);
 hipError_t launch_topk_threshold(const float* logits, int64_t stride, RowsView rows, int32_t k, void* ws,
                                  hipStream_t s);
 LogitsMode topk_filter_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto);
 hipError_t launch_topk_filtered_final(RowsView rows, int64_t stride, int32_t k, int32_t* idx, void* ws,
                                       hipStream_t s);
-LogitsMode topk_fallback_mode(void* ws, int32_t R, int32_t k);
+LogitsMode topk_fallback_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto = 0);
 hipError_t launch_topk_fallback(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
                                 void* ws, hipStream_t s);
 

@@ -53,7 +53,7 @@ constexpr int kTileBytes = (kTileSlots + 1) * 1024;      // + one sink for the s
 #endif
 constexpr int kDepth = DSA_MLA_DEPTH;                     // tiles in flight ahead of the QK tile
 constexpr int kBufs = kDepth + 2;                        // + the QK tile + the PV tile
-static_assert(kDepth >= 1 && kDepth <= 3, "the tile wait handles up to two tiles ahead");
+static_assert(kDepth >= 1 && kDepth <= 4, "the tile wait handles up to three tiles ahead");
 static_assert(kDmaWaves * kDmaPerWave >= kTileSlots, "copy slots must cover a tile");
 constexpr int kMaxSplitKeys = 2048;
 static_assert(kDepth * kTile <= kMaxSplitKeys, "the first tiles' lookups stay inside phys");
@@ -102,6 +102,13 @@ static_assert(kRopeChunk0 + 4 * 64 == kTileChunks, "the layout covers the tile")
 // tile chunk of latent byte `byte` (a multiple of 8) of key `key`
 __device__ __forceinline__ int lat_chunk(int key, int byte) {
   return (((key >> 4) * 4 + (byte >> 7)) * 2 + ((byte >> 6) & 1)) * 64 + 16 * ((byte >> 4) & 3) + (key & 15);
+}
+// tile chunk of record chunk rc of key `key`
+__device__ __forceinline__ int rec_chunk(int key, int rc) {
+  if (rc < kRecScaleOff / 16) return lat_chunk(key, 16 * rc);
+  if (rc == kRecScaleOff / 16) return kScaleChunk0 + key;
+  const int r = rc - kRecRopeOff / 16;          // rope chunk 0..7
+  return kRopeChunk0 + ((key >> 4) * 2 + (r >> 2)) * 64 + 16 * (r & 3) + (key & 15);
 }
 // key and 16-B record chunk held at tile chunk c (0 <= c < kTileChunks)
 __device__ __forceinline__ void chunk_src(int c, int& key, int& rc) {
@@ -213,16 +220,16 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
   for (int mt = 0; mt < 2; mt++) {
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-      const i32x4 lo4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * (((mt * 4 + b) * 2 + 0) * 64 + lane));
-      const i32x4 hi4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * (((mt * 4 + b) * 2 + 1) * 64 + lane));
+      const i32x4 lo4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * rec_chunk(16 * mt + c16, 8 * b + g));
+      const i32x4 hi4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * rec_chunk(16 * mt + c16, 8 * b + 4 + g));
       a[mt][b] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     }
-    const i32x4 ksc = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * (kScaleChunk0 + 16 * mt + c16));
+    const i32x4 ksc = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * rec_chunk(16 * mt + c16, kRecScaleOff / 16));
 #pragma unroll
     for (int b = 0; b < 4; b++) sa[mt][b] = (ksc[b] >> 23) & 0xFF;   // E8M0 = the fp32 exponent of 2^e
 #pragma unroll
     for (int ks = 0; ks < 2; ks++)
-      ar[mt][ks] = *reinterpret_cast<const DSA_LDS bf16x8*>(T + 16 * (kRopeChunk0 + (mt * 2 + ks) * 64 + lane));
+      ar[mt][ks] = *reinterpret_cast<const DSA_LDS bf16x8*>(T + 16 * rec_chunk(16 * mt + c16, kRecRopeOff / 16 + 4 * ks + g));
   }
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -435,7 +442,8 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
     if (is_qk && it < ntiles) {
       // tiles it+1 .. it+kDepth-1 (those that exist) may stay in flight
       const int ahead = min(kDepth - 1, ntiles - 1 - it);
-      if (ahead >= 2) wait_vmcnt<2 * kDmaPerWave>();
+      if (ahead >= 3) wait_vmcnt<3 * kDmaPerWave>();
+      else if (ahead >= 2) wait_vmcnt<2 * kDmaPerWave>();
       else if (ahead == 1) wait_vmcnt<kDmaPerWave>();
       else wait_vmcnt<0>();
     }
@@ -551,38 +559,45 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
 #pragma unroll
             for (int i = 0; i < 4; i++) O[ht][dt][i] *= al[ht][i];
       }
+      // B operands: V of value block qw, read transposed (tr8: lane i of a 16-lane group
+      // points at the key of K = 8g + i/2, i.e. key 16(i/8) + 4g + (i/2)%4, dims +8*(i%2), and
+      // gets those 8 keys of dim c16), all eight dim tiles converted to bf16 up front
+      const int vkey = 16 * (c16 >> 3) + 4 * g + ((c16 >> 1) & 3);
+      i32x2 vraw[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++)
+        vraw[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (DSA_LDS i32x2*)(T + 16 * lat_chunk(vkey, 128 * qw + 16 * dt) + 8 * (c16 & 1)));
       // A operands: P of heads 16ht + c16 for K = 8g..8g+7, i.e. keys 4g..4g+3 and
       // 16+4g..16+4g+3 (the order the QK waves wrote), times those keys' scale of value block
       // qw (a power of two: exact), rounded to bf16
+      i32x4 praw[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ht++)
+        praw[ht] = *reinterpret_cast<const DSA_LDS i32x4*>((const DSA_LDS uint16_t*)pl[par] + 8 * (64 * ht + lane));
       f32x4 ks[2];
 #pragma unroll
       for (int h = 0; h < 2; h++)
 #pragma unroll
         for (int i = 0; i < 4; i++)
-          ks[h][i] = *reinterpret_cast<const DSA_LDS float*>(T + 16 * (kScaleChunk0 + 16 * h + 4 * g + i) + 4 * qw);
-      bf16x8 pa[4];
+          ks[h][i] = *reinterpret_cast<const DSA_LDS float*>(T + 16 * rec_chunk(16 * h + 4 * g + i, kRecScaleOff / 16) + 4 * qw);
+      bf16x8 vv[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) vv[dt] = fp8x8_to_bf16((uint32_t)vraw[dt][0], (uint32_t)vraw[dt][1], 1.0f);
+      // head tile by head tile: the scaling of the next tile's P is independent of this tile's
+      // eight MFMAs, so it issues while they run
 #pragma unroll
       for (int ht = 0; ht < 4; ht++) {
-        const i32x4 pw = *reinterpret_cast<const DSA_LDS i32x4*>((const DSA_LDS uint16_t*)pl[par] + 8 * (64 * ht + lane));
         int w[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {            // keys 8g + 2j, 8g + 2j + 1
-          const uint32_t x = (uint32_t)pw[j];
+          const uint32_t x = (uint32_t)praw[ht][j];
           w[j] = pack2_bf16(__uint_as_float(x << 16) * ks[j >> 1][2 * (j & 1)],
                             __uint_as_float(x & 0xFFFF0000u) * ks[j >> 1][2 * (j & 1) + 1]);
         }
-        pa[ht] = __builtin_bit_cast(bf16x8, i32x4{w[0], w[1], w[2], w[3]});
-      }
-      // tr8: lane i of a 16-lane group points at the key of K = 8g + i/2 (key 16(i/8) + 4g +
-      // (i/2)%4), dims +8*(i%2); gets those 8 keys of dim c16
-      const int vkey = 16 * (c16 >> 3) + 4 * g + ((c16 >> 1) & 3);
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, i32x4{w[0], w[1], w[2], w[3]});
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) {
-        DSA_LDS i32x2* src = (DSA_LDS i32x2*)(T + 16 * lat_chunk(vkey, 128 * qw + 16 * dt) + 8 * (c16 & 1));
-        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(src);
-        const bf16x8 vv = fp8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1], 1.0f);
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) O[ht][dt] = mfma_bf16(pa[ht], vv, O[ht][dt]);
+        for (int dt = 0; dt < 8; dt++) O[ht][dt] = mfma_bf16(pa, vv[dt], O[ht][dt]);
       }
     }
     __syncthreads();                            // m_s / l_s written by the QK waves
@@ -724,20 +739,35 @@ k_sparse_mla_stream(const uint16_t* __restrict__ q, const int32_t* __restrict__ 
   }
 }
 
-// Merges the splits of one row: block = (row, head), 128 threads x 4 dims.
+// Merges the splits of one row: block = (row, head), 128 threads x 4 dims.  Every split's (m, l)
+// and partial O are loaded before any is used (a split count of at most kMaxSplits, predicated),
+// so the loads are in flight together instead of one memory round trip per split.
+constexpr int kMaxSplits = 32;
 __global__ void __launch_bounds__(128) k_mla_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                                                      int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int r = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+  f32x2 ml[kMaxSplits];
+  float4 o[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; s++) {
+    if (s < nsplit) {
+      ml[s] = *reinterpret_cast<const f32x2*>(ws_ml + (((int64_t)r * nsplit + s) * kHeads + h) * 2);
+      o[s] = *reinterpret_cast<const float4*>(ws_o + (((int64_t)r * nsplit + s) * kHeads + h) * kVal + 4 * tid);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; s++) M = fmaxf(M, ws_ml[(((int64_t)r * nsplit + s) * kHeads + h) * 2]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; s++)
+    if (s < nsplit) M = fmaxf(M, ml[s][0]);
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < nsplit; s++) {
-    const float* ml = ws_ml + (((int64_t)r * nsplit + s) * kHeads + h) * 2;
-    const float f = (ml[0] == -INFINITY) ? 0.f : exp2f(ml[0] - M);
-    L += ml[1] * f;
-    const float4 o = *reinterpret_cast<const float4*>(ws_o + (((int64_t)r * nsplit + s) * kHeads + h) * kVal + 4 * tid);
-    acc.x += o.x * f; acc.y += o.y * f; acc.z += o.z * f; acc.w += o.w * f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; s++) {
+    if (s < nsplit) {
+      const float f = (ml[s][0] == -INFINITY) ? 0.f : exp2f(ml[s][0] - M);
+      L += ml[s][1] * f;
+      acc.x += o[s].x * f; acc.y += o[s].y * f; acc.z += o[s].z * f; acc.w += o[s].w * f;
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = out + ((int64_t)r * kHeads + h) * kVal + 4 * tid;
@@ -755,7 +785,7 @@ int choose_splits(int32_t R, int32_t k, size_t ws_cap = SIZE_MAX) {
   // enough work-groups to cover 256 CUs a few times over; at least 64 keys per split; no more
   // splits than a workspace of ws_cap bytes holds
   int s = 1;
-  while (s < 32 && (int64_t)R * s < 512 && k / (2 * s) >= 64 && (size_t)R * (2 * s) * kSplitPartBytes <= ws_cap)
+  while (s < kMaxSplits && (int64_t)R * s < 512 && k / (2 * s) >= 64 && (size_t)R * (2 * s) * kSplitPartBytes <= ws_cap)
     s <<= 1;
   return s;
 }

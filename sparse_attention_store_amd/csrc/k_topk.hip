@@ -94,13 +94,14 @@ __device__ inline int64_t row_len(const int32_t* pos, int r, int64_t stride) {
   return min((int64_t)pos[r] + 1, stride);
 }
 
-// Workspace initialisation: ranges to (max, 0), histograms and counters to 0.
-__global__ void k_init(Ws w, int32_t R) {
+// Workspace initialisation: ranges to (max, 0), histograms and counters to 0, every row's
+// exact-path flag to `flag` (1: the rows go straight to the radix passes).
+__global__ void k_init(Ws w, int32_t R, int flag) {
   const int64_t n_hist = (int64_t)R * kBins;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_hist; i += (int64_t)gridDim.x * blockDim.x) {
     w.hist[i] = 0;
     if (i < (int64_t)R * 4) w.cnt[i] = 0;
-    if (i < R) { w.range[2 * i] = 0xFFFFFFFFu; w.range[2 * i + 1] = 0u; w.flag[i] = 0; w.fcnt[i] = 0; }
+    if (i < R) { w.range[2 * i] = 0xFFFFFFFFu; w.range[2 * i + 1] = 0u; w.flag[i] = flag; w.fcnt[i] = 0; }
   }
 }
 
@@ -521,10 +522,23 @@ __global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt
       for (int j = 0; j < kPer; j++)
         if (j < jn && (low >= 32 || (v[j] >> low) == prefix)) atomicAdd(&h[(v[j] >> sh) & (kBins - 1)], 1);
     } else {
-      for (int64_t i = tid; i < ns; i += kFinalThreads) {
-        const int64_t s = (i >> 6) * step * 64 + (i & 63);
-        const uint32_t u = min(max(ord_key(row[s]), kmin), kmax) - kmin;
-        if (low >= 32 || (u >> low) == prefix) atomicAdd(&h[(u >> sh) & (kBins - 1)], 1);
+      // more samples than the registers hold: batches of kThrSamples, every load of a batch
+      // issued before any is used (one dependent load per sample would be a memory round trip
+      // per iteration)
+      for (int64_t i0 = 0; i0 < ns; i0 += kThrSamples) {
+        float x[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; j++) {
+          const int64_t i = i0 + tid + (int64_t)j * kFinalThreads;
+          const int64_t s = (min(i, ns - 1) >> 6) * step * 64 + (min(i, ns - 1) & 63);
+          x[j] = row[s];
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; j++) {
+          const int64_t i = i0 + tid + (int64_t)j * kFinalThreads;
+          const uint32_t u = min(max(ord_key(x[j]), kmin), kmax) - kmin;
+          if (i < ns && (low >= 32 || (u >> low) == prefix)) atomicAdd(&h[(u >> sh) & (kBins - 1)], 1);
+        }
       }
     }
     __syncthreads();
@@ -650,11 +664,11 @@ __global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt
 
 size_t topk_workspace_bytes(int32_t R, int64_t /*stride*/, int32_t k) { return ws_bytes(R, k); }
 
-hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s) {
+hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s, bool flag_all) {
   Ws w = carve(ws, R, k);
   const int64_t n = (int64_t)R * kBins;
   const int64_t grid = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-  hipLaunchKernelGGL(k_init, dim3((unsigned)grid), dim3(256), 0, s, w, R);
+  hipLaunchKernelGGL(k_init, dim3((unsigned)grid), dim3(256), 0, s, w, R, flag_all ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -676,7 +690,7 @@ hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32
                        hipStream_t s) {
   const int R = rows.n;
   if (R <= 0) return hipSuccess;
-  hipError_t e = launch_topk_init(R, k, ws, s);
+  hipError_t e = launch_topk_init(R, k, ws, s, false);
   if (e != hipSuccess) return e;
   Ws w = carve(ws, R, k);
   const int64_t visible = (int64_t)rows.max_pos + 1;
@@ -724,10 +738,11 @@ hipError_t launch_topk_filtered_final(RowsView rows, int64_t stride, int32_t k, 
   return hipGetLastError();
 }
 
-LogitsMode topk_fallback_mode(void* ws, int32_t R, int32_t k) {
+LogitsMode topk_fallback_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto) {
   const Ws w = carve(ws, R, k);
   LogitsMode m;
   m.kind = kLogitsFallback;
+  m.skip_upto = skip_upto;
   m.flag = w.flag;
   m.range = w.range;      // the full scores widen the sample's range to the row's
   return m;

@@ -313,7 +313,8 @@ def test_fused_topk_fallback_when_candidates_overflow():
 
 def test_fused_topk_ties_inside_candidate_list():
     _announce("fused top-k: all scores equal, 3000 candidates -> exact within the list")
-    w = gi.make_decode("fb_ties", gi.SEED_BASE + 72, [3000])
+    # two rows: R x stride above the size up to which the fused call takes the radix path directly
+    w = gi.make_decode("fb_ties", gi.SEED_BASE + 72, [3000], rows_per_req=2)
     key = _equal_score_key()
     gidx, ridx = _fused_topk_case(w, {p: key for p in range(3000)}, expect_fallback=False)
     assert np.array_equal(gidx[0], np.arange(2048))
