@@ -41,19 +41,26 @@ namespace {
 
 constexpr int kThreads = 512;             // 4 QK waves + 4 PV waves
 static_assert(kThreads == kVal, "the two-part merge maps one thread to each value dim");
-constexpr int kTile = 32;                  // keys per tile
+#ifndef DSA_MLA_TILE
+#define DSA_MLA_TILE 64
+#endif
+constexpr int kTile = DSA_MLA_TILE;        // keys per tile
+static_assert(kTile == 32 || kTile == 64, "tiles of 32 or 64 keys");
+constexpr int kMT = kTile / 16;            // 16-key blocks of the QK MFMAs
+constexpr int kKS = kTile / 32;            // 32-key K steps of the PV MFMAs
 constexpr int kChunks = kRecBytes / 16;    // 41 x 16 B per record
-constexpr int kTileChunks = kTile * kChunks;            // 1312 chunks of 16 B
+constexpr int kTileChunks = kTile * kChunks;            // 1312 / 2624 chunks of 16 B
 constexpr int kDmaWaves = 4;                             // the QK waves issue every copy
-constexpr int kDmaPerWave = 6;                           // 4 waves x 6 x 64 lanes >= 1312
-constexpr int kTileSlots = (kTileChunks + 63) / 64;     // 21 wave-wide 1-KiB copies hold a tile
+constexpr int kTileSlots = (kTileChunks + 63) / 64;     // 21 / 41 wave-wide 1-KiB copies hold a tile
+constexpr int kDmaPerWave = (kTileSlots + kDmaWaves - 1) / kDmaWaves;   // 6 / 11 per QK wave
 constexpr int kTileBytes = (kTileSlots + 1) * 1024;      // + one sink for the surplus copies
 #ifndef DSA_MLA_DEPTH
-#define DSA_MLA_DEPTH 2
+#define DSA_MLA_DEPTH (kTile == 32 ? 2 : 1)
 #endif
 constexpr int kDepth = DSA_MLA_DEPTH;                     // tiles in flight ahead of the QK tile
 constexpr int kBufs = kDepth + 2;                        // + the QK tile + the PV tile
 static_assert(kDepth >= 1 && kDepth <= 4, "the tile wait handles up to three tiles ahead");
+static_assert(3 * kDmaPerWave < 64, "vmcnt counts the copies in flight");
 static_assert(kDmaWaves * kDmaPerWave >= kTileSlots, "copy slots must cover a tile");
 constexpr int kMaxSplitKeys = 2048;
 static_assert(kDepth * kTile <= kMaxSplitKeys, "the first tiles' lookups stay inside phys");
@@ -87,18 +94,17 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Tile layout in LDS, in 16-B chunks (1312 per tile of 32 keys).  Every wave-wide access of
-// the scoring and accumulation steps reads one contiguous block: measured with the LDS
-// bank-conflict counter, 16-B reads of records stored back to back (a 656-B stride between
-// the lanes' keys) took twice the cycles of a contiguous 1-KiB read, and contiguous reads
-// took none extra.
-//  * chunks [0, 1024): latent.  Block (mt * 4 + b) * 2 + half of 64 chunks holds, at chunk
-//    16 gg + kk, bytes 128 b + 64 half + 16 gg .. +16 of key 16 mt + kk;
-//  * [1024, 1056): the 16 scale bytes of key c - 1024;
-//  * [1056, 1312): rope.  Block mt * 2 + ks holds, at chunk 16 gg + kk, rope bytes 64 ks +
-//    16 gg .. +16 of key 16 mt + kk.
-constexpr int kScaleChunk0 = 1024, kRopeChunk0 = 1056;
-static_assert(kRopeChunk0 + 4 * 64 == kTileChunks, "the layout covers the tile");
+// Tile layout in LDS, in 16-B chunks (41 per key).  Every wave-wide access of the scoring and
+// accumulation steps reads one contiguous block: measured with the LDS bank-conflict counter,
+// 16-B reads of records stored back to back (a 656-B stride between the lanes' keys) took
+// twice the cycles of a contiguous 1-KiB read, and contiguous reads took none extra.
+//  * chunks [0, kScaleChunk0): latent.  Block (mt * 4 + b) * 2 + half of 64 chunks holds, at
+//    chunk 16 gg + kk, bytes 128 b + 64 half + 16 gg .. +16 of key 16 mt + kk;
+//  * [kScaleChunk0, kRopeChunk0): the 16 scale bytes of key c - kScaleChunk0;
+//  * [kRopeChunk0, kTileChunks): rope.  Block mt * 2 + ks holds, at chunk 16 gg + kk, rope
+//    bytes 64 ks + 16 gg .. +16 of key 16 mt + kk.
+constexpr int kScaleChunk0 = kMT * 8 * 64, kRopeChunk0 = kScaleChunk0 + kTile;
+static_assert(kRopeChunk0 + kMT * 2 * 64 == kTileChunks, "the layout covers the tile");
 // tile chunk of latent byte `byte` (a multiple of 8) of key `key`
 __device__ __forceinline__ int lat_chunk(int key, int byte) {
   return (((key >> 4) * 4 + (byte >> 7)) * 2 + ((byte >> 6) & 1)) * 64 + 16 * ((byte >> 4) & 3) + (key & 15);
@@ -210,60 +216,67 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
     zero_bad_records(T, phys, it * kTile, tid);
     lds_barrier();
   }
-  // S^T (32 keys x 16 heads): lane holds keys 4g+i (+16 mt), head c16.  All operands of
-  // the tile are read first; the two 16-key accumulator chains are interleaved.
-  i32x8 a[2][4];
-  bf16x8 ar[2][2];
-  int sa[2][4];
-  // lane (g, c16) reads chunk `lane` of a 64-chunk block: bytes 16g.. of key 16mt + c16
+  // S^T (kTile keys x 16 heads): lane holds keys 16 mt + 4g + i, head c16.  The operands of
+  // two 16-key blocks are read, then their MFMAs issued (two interleaved accumulator chains).
+  f32x4 acc[kMT];
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++) {
+  for (int m0 = 0; m0 < kMT; m0 += 2) {
+    i32x8 a[2][4];
+    bf16x8 ar[2][2];
+    int sa[2][4];
+    // lane (g, c16) reads chunk `lane` of a 64-chunk block: bytes 16g.. of key 16mt + c16
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int mt = m0 + u;
+#pragma unroll
+      for (int b = 0; b < 4; b++) {
+        const i32x4 lo4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * rec_chunk(16 * mt + c16, 8 * b + g));
+        const i32x4 hi4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * rec_chunk(16 * mt + c16, 8 * b + 4 + g));
+        a[u][b] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      }
+      const i32x4 ksc = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * rec_chunk(16 * mt + c16, kRecScaleOff / 16));
+#pragma unroll
+      for (int b = 0; b < 4; b++) sa[u][b] = (ksc[b] >> 23) & 0xFF;   // E8M0 = the fp32 exponent of 2^e
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++)
+        ar[u][ks] = *reinterpret_cast<const DSA_LDS bf16x8*>(T + 16 * rec_chunk(16 * mt + c16, kRecRopeOff / 16 + 4 * ks + g));
+    }
+    f32x4 c2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-      const i32x4 lo4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * rec_chunk(16 * mt + c16, 8 * b + g));
-      const i32x4 hi4 = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * rec_chunk(16 * mt + c16, 8 * b + 4 + g));
-      a[mt][b] = i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-    }
-    const i32x4 ksc = *reinterpret_cast<const DSA_LDS i32x4*>(T + 16 * rec_chunk(16 * mt + c16, kRecScaleOff / 16));
 #pragma unroll
-    for (int b = 0; b < 4; b++) sa[mt][b] = (ksc[b] >> 23) & 0xFF;   // E8M0 = the fp32 exponent of 2^e
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++)
-      ar[mt][ks] = *reinterpret_cast<const DSA_LDS bf16x8*>(T + 16 * rec_chunk(16 * mt + c16, kRecRopeOff / 16 + 4 * ks + g));
-  }
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int b = 0; b < 4; b++) {
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++)
-      acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mt][b], Q.qhi[b], acc[mt], 0, 0, 0, sa[mt][b], 0,
+      for (int u = 0; u < 2; u++)
+        c2[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[u][b], Q.qhi[b], c2[u], 0, 0, 0, sa[u][b], 0,
                                                                  Q.sbhi[b]);
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
-      acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mt][b], Q.qlo[b], acc[mt], 0, 0, 0, sa[mt][b], 0,
+      for (int u = 0; u < 2; u++)
+        c2[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[u][b], Q.qlo[b], c2[u], 0, 0, 0, sa[u][b], 0,
                                                                  Q.sblo[b]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+      for (int u = 0; u < 2; u++) c2[u] = mfma_bf16(ar[u][ks], Q.qr[ks], c2[u]);
+    acc[m0] = c2[0];
+    acc[m0 + 1] = c2[1];
   }
-#pragma unroll
-  for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++) acc[mt] = mfma_bf16(ar[mt][ks], Q.qr[ks], acc[mt]);
 
-  float sv[2][4];
+  float sv[kMT][4];
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++)
+  for (int mt = 0; mt < kMT; mt++)
 #pragma unroll
     for (int i = 0; i < 4; i++) sv[mt][i] = acc[mt][i] * sm_log2;
-  if (bad) {     // invalid keys of the tile (two runs of four consecutive entries of phys) score -inf
-    const i32x4 vk[2] = {*reinterpret_cast<const DSA_LDS i32x4*>(phys + it * kTile + 4 * g),
-                         *reinterpret_cast<const DSA_LDS i32x4*>(phys + it * kTile + 16 + 4 * g)};
+  if (bad) {     // invalid keys of the tile (runs of four consecutive entries of phys) score -inf
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
+    for (int mt = 0; mt < kMT; mt++) {
+      const i32x4 vk = *reinterpret_cast<const DSA_LDS i32x4*>(phys + it * kTile + 16 * mt + 4 * g);
 #pragma unroll
-      for (int i = 0; i < 4; i++) sv[mt][i] = vk[mt][i] >= 0 ? sv[mt][i] : -INFINITY;
+      for (int i = 0; i < 4; i++) sv[mt][i] = vk[i] >= 0 ? sv[mt][i] : -INFINITY;
+    }
   }
   float tmax = -INFINITY;
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++)
+  for (int mt = 0; mt < kMT; mt++)
 #pragma unroll
     for (int i = 0; i < 4; i++) tmax = fmaxf(tmax, sv[mt][i]);
   tmax = rows_max(tmax);
@@ -276,9 +289,9 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
   }
   const bool live = m_run != -INFINITY;
   float psum = 0.f;
-  float p[2][4];
+  float p[kMT][4];
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++)
+  for (int mt = 0; mt < kMT; mt++)
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       p[mt][i] = live ? __builtin_amdgcn_exp2f(sv[mt][i] - m_run) : 0.f;
@@ -290,12 +303,15 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
   const bool any_resc = __any(alpha != 1.f);     // wave-uniform: tells the PV waves to rescale
   if (lane == 0) resc_p[qw] = any_resc;
   // P as bf16, unscaled: the PV waves multiply in each key's value-block scale (a power of
-  // two, so the product is the bf16 rounding of P times the scale).  A lane's 16 B, its
-  // head's keys 4g..4g+3 and 16+4g..16+4g+3, land at chunk 64 qw + lane: the PV waves read
-  // them as their MFMA operand's K = 8g..8g+7 in that key order.
-  *reinterpret_cast<DSA_LDS i32x4*>(plp + 8 * (64 * qw + lane)) =
-      i32x4{pack2_bf16(p[0][0], p[0][1]), pack2_bf16(p[0][2], p[0][3]), pack2_bf16(p[1][0], p[1][1]),
-            pack2_bf16(p[1][2], p[1][3])};
+  // two, so the product is the bf16 rounding of P times the scale).  Per 32-key block ks (its
+  // 64 heads x 32 keys at plp + ks * 2048), a lane's 16 B, its head's keys 32ks + 4g..4g+3 and
+  // 32ks + 16+4g..16+4g+3, land at chunk 64 qw + lane: the PV waves read them as their MFMA
+  // operand's K = 8g..8g+7 in that key order.
+#pragma unroll
+  for (int ks = 0; ks < kKS; ks++)
+    *reinterpret_cast<DSA_LDS i32x4*>(plp + ks * kHeads * 32 + 8 * (64 * qw + lane)) =
+        i32x4{pack2_bf16(p[2 * ks][0], p[2 * ks][1]), pack2_bf16(p[2 * ks][2], p[2 * ks][3]),
+              pack2_bf16(p[2 * ks + 1][0], p[2 * ks + 1][1]), pack2_bf16(p[2 * ks + 1][2], p[2 * ks + 1][3])};
 }
 
 // Partial results cross work-groups (and XCDs, each with its own L2): they are written and
@@ -559,45 +575,51 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
 #pragma unroll
             for (int i = 0; i < 4; i++) O[ht][dt][i] *= al[ht][i];
       }
-      // B operands: V of value block qw, read transposed (tr8: lane i of a 16-lane group
-      // points at the key of K = 8g + i/2, i.e. key 16(i/8) + 4g + (i/2)%4, dims +8*(i%2), and
-      // gets those 8 keys of dim c16), all eight dim tiles converted to bf16 up front
-      const int vkey = 16 * (c16 >> 3) + 4 * g + ((c16 >> 1) & 3);
-      i32x2 vraw[8];
+      // per 32-key step ks of the tile:
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++)
-        vraw[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (DSA_LDS i32x2*)(T + 16 * lat_chunk(vkey, 128 * qw + 16 * dt) + 8 * (c16 & 1)));
-      // A operands: P of heads 16ht + c16 for K = 8g..8g+7, i.e. keys 4g..4g+3 and
-      // 16+4g..16+4g+3 (the order the QK waves wrote), times those keys' scale of value block
-      // qw (a power of two: exact), rounded to bf16
-      i32x4 praw[4];
+      for (int kst = 0; kst < kKS; kst++) {
+        // B operands: V of value block qw, read transposed (tr8: lane i of a 16-lane group
+        // points at the key of K = 8g + i/2, i.e. key 32kst + 16(i/8) + 4g + (i/2)%4, dims
+        // +8*(i%2), and gets those 8 keys of dim c16), all eight dim tiles converted up front
+        const int vkey = 32 * kst + 16 * (c16 >> 3) + 4 * g + ((c16 >> 1) & 3);
+        i32x2 vraw[8];
 #pragma unroll
-      for (int ht = 0; ht < 4; ht++)
-        praw[ht] = *reinterpret_cast<const DSA_LDS i32x4*>((const DSA_LDS uint16_t*)pl[par] + 8 * (64 * ht + lane));
-      f32x4 ks[2];
+        for (int dt = 0; dt < 8; dt++)
+          vraw[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (DSA_LDS i32x2*)(T + 16 * lat_chunk(vkey, 128 * qw + 16 * dt) + 8 * (c16 & 1)));
+        // A operands: P of heads 16ht + c16 for K = 8g..8g+7, i.e. keys 32kst + 4g..4g+3 and
+        // 32kst + 16+4g..16+4g+3 (the order the QK waves wrote), times those keys' scale of value
+        // block qw (a power of two: exact), rounded to bf16
+        i32x4 praw[4];
 #pragma unroll
-      for (int h = 0; h < 2; h++)
+        for (int ht = 0; ht < 4; ht++)
+          praw[ht] = *reinterpret_cast<const DSA_LDS i32x4*>((const DSA_LDS uint16_t*)pl[par] + kst * kHeads * 32 +
+                                                             8 * (64 * ht + lane));
+        f32x4 ks[2];
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-          ks[h][i] = *reinterpret_cast<const DSA_LDS float*>(T + 16 * rec_chunk(16 * h + 4 * g + i, kRecScaleOff / 16) + 4 * qw);
-      bf16x8 vv[8];
+        for (int h = 0; h < 2; h++)
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) vv[dt] = fp8x8_to_bf16((uint32_t)vraw[dt][0], (uint32_t)vraw[dt][1], 1.0f);
-      // head tile by head tile: the scaling of the next tile's P is independent of this tile's
-      // eight MFMAs, so it issues while they run
+          for (int i = 0; i < 4; i++)
+            ks[h][i] = *reinterpret_cast<const DSA_LDS float*>(
+                T + 16 * rec_chunk(32 * kst + 16 * h + 4 * g + i, kRecScaleOff / 16) + 4 * qw);
+        bf16x8 vv[8];
 #pragma unroll
-      for (int ht = 0; ht < 4; ht++) {
-        int w[4];
+        for (int dt = 0; dt < 8; dt++) vv[dt] = fp8x8_to_bf16((uint32_t)vraw[dt][0], (uint32_t)vraw[dt][1], 1.0f);
+        // head tile by head tile: the scaling of the next tile's P is independent of this tile's
+        // eight MFMAs, so it issues while they run
 #pragma unroll
-        for (int j = 0; j < 4; j++) {            // keys 8g + 2j, 8g + 2j + 1
-          const uint32_t x = (uint32_t)praw[ht][j];
-          w[j] = pack2_bf16(__uint_as_float(x << 16) * ks[j >> 1][2 * (j & 1)],
-                            __uint_as_float(x & 0xFFFF0000u) * ks[j >> 1][2 * (j & 1) + 1]);
+        for (int ht = 0; ht < 4; ht++) {
+          int w[4];
+#pragma unroll
+          for (int j = 0; j < 4; j++) {            // keys 8g + 2j, 8g + 2j + 1
+            const uint32_t x = (uint32_t)praw[ht][j];
+            w[j] = pack2_bf16(__uint_as_float(x << 16) * ks[j >> 1][2 * (j & 1)],
+                              __uint_as_float(x & 0xFFFF0000u) * ks[j >> 1][2 * (j & 1) + 1]);
+          }
+          const bf16x8 pa = __builtin_bit_cast(bf16x8, i32x4{w[0], w[1], w[2], w[3]});
+#pragma unroll
+          for (int dt = 0; dt < 8; dt++) O[ht][dt] = mfma_bf16(pa, vv[dt], O[ht][dt]);
         }
-        const bf16x8 pa = __builtin_bit_cast(bf16x8, i32x4{w[0], w[1], w[2], w[3]});
-#pragma unroll
-        for (int dt = 0; dt < 8; dt++) O[ht][dt] = mfma_bf16(pa, vv[dt], O[ht][dt]);
       }
     }
     __syncthreads();                            // m_s / l_s written by the QK waves
@@ -781,11 +803,14 @@ __global__ void __launch_bounds__(128) k_mla_combine(const float* __restrict__ w
 
 constexpr size_t kSplitPartBytes = (size_t)kHeads * (kVal + 2) * sizeof(float);   // O, m, l of one split
 
+constexpr int kSplitGroups = 256;           // one round of work-groups: one fits a CU (LDS)
 int choose_splits(int32_t R, int32_t k, size_t ws_cap = SIZE_MAX) {
-  // enough work-groups to cover 256 CUs a few times over; at least 64 keys per split; no more
-  // splits than a workspace of ws_cap bytes holds
+  // up to one round of work-groups over the chip (a second round took c1's 32 rows from 37 to
+  // 57 us, and every split adds a 128-KiB partial); at least one tile of keys per split; no
+  // more splits than a workspace of ws_cap bytes holds
   int s = 1;
-  while (s < kMaxSplits && (int64_t)R * s < 512 && k / (2 * s) >= 64 && (size_t)R * (2 * s) * kSplitPartBytes <= ws_cap)
+  while (s < kMaxSplits && (int64_t)R * 2 * s <= kSplitGroups && k / (2 * s) >= kTile &&
+         (size_t)R * (2 * s) * kSplitPartBytes <= ws_cap)
     s <<= 1;
   return s;
 }
