@@ -351,9 +351,12 @@ def mtp_carry_saved_fraction(draft_steps: int = 5, n_full: int = 21) -> float:
 def chunked_prefill_indexer_read_bytes(L: int = 1 << 20, rows_per_read: int = 32, n_full: int = 21) -> int:
     """Index-K bytes the prefill of an L-token prompt reads when each block of `rows_per_read`
     consecutive query rows reads the keys visible to its last row once, 132 B per token, per
-    full layer.  The page's 1M prefill figure ([IDXC], the cross-layer section: about 47 TB,
-    a simplified per-layer whole-segment accounting) is this sum with 32-row blocks; a kernel
-    that reads the cache once per 32K-row chunk reads `rows_per_read` = 32768's worth."""
+    full layer.  A kernel that reads the cache once per 32K-row chunk reads `rows_per_read` =
+    32768's worth.  Parity unpinned for the default: the page's 1M prefill figure ([IDXC], the
+    cross-layer section: about 47 TB, an accounting the page calls simplified) does not say
+    how often a key is read; 32-row blocks is the granularity that reproduces it, a fitted
+    reading, so that figure pins nothing.  The formula itself is pinned by its two limits
+    (one row per block: every row reads its own prefix; one block: one read of the prompt)."""
     n = (L + rows_per_read - 1) // rows_per_read
     return n_full * index_k_bytes_per_token() * sum(min(L, (b + 1) * rows_per_read) for b in range(n))
 
