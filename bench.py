@@ -49,6 +49,11 @@ PREFILL_LOGITS_BUDGET = 4 << 30   # logits scratch per indexer launch in the 1M 
 # parts read and written (64 x 64 bf16 each way), the 656-B record, the 132-B index entry, req + pos
 FUSED_STORE_BYTES_PER_TOKEN = 576 * 2 + 128 * 2 + 2 * 64 * 64 * 2 + 656 + 132 + 8
 SECTIONS = ("c2", "c0", "c1", "c3", "sweep", "c4", "mxfp4", "mtp", "fused_store", "prefill1m", "copy")
+# file stem of each section's summaries under profiles/: the workload it covers
+PROFILE_STEMS = {"c2": "c2_verify_128k", "c0": "c0_tiny_decode_4k", "c1": "c1_decode_batch_8k_32k",
+                 "c3": "c3_long_context_1m", "c4": "c4_chunked_prefill_8192_on_64k", "sweep": "decode_ctx_sweep_1k_1m",
+                 "mxfp4": "c2_verify_128k_mxfp4_index", "mtp": "c2_mtp_draft_round",
+                 "fused_store": "fused_norm_rope_store_8192", "prefill1m": "chunked_prefill_1m"}
 
 _IDX_SRC = ["sparse_attention_store_amd/csrc/k_indexer.hip", "sparse_attention_store_amd/csrc/dsa_device.hpp",
             "sparse_attention_store_amd/csrc/dsa_internal.h"]
@@ -133,6 +138,13 @@ def profiled_us(section, kernel):
 
 
 # ----------------------------------------------------------------------------- counter summaries
+def _kname(raw):
+    """A kernel's name as rocprofv3 prints it, without return type, namespaces and arguments."""
+    for junk in ("(anonymous namespace)::", "void ", "dsa::"):
+        raw = raw.replace(junk, "")
+    return raw.split("(")[0].strip()
+
+
 def _read_csv(path):
     import csv
     with open(path) as fh:
@@ -148,7 +160,7 @@ def write_traffic(section, fetch_csv, write_csv, command):
     def per_kernel(path):
         vals = {}
         for r in _read_csv(path):
-            vals.setdefault(r["Kernel_Name"].split("(")[0].replace("dsa::", ""), []).append(float(r["Counter_Value"]))
+            vals.setdefault(_kname(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
         return vals
 
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
@@ -170,6 +182,17 @@ def write_traffic(section, fetch_csv, write_csv, command):
     out["sections"][section] = sec
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
+    lines = [f"HBM traffic per dispatch, section {section} of bench.py (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)",
+             "", "Command (one run per counter):"] + ["  " + c for c in command.split(" ;; ")] + [
+             "", f"Calibration: a 1 GiB device copy reads {copy_f:.0f} KiB (factor {gib_kib / copy_f:.4f}) and writes "
+                 f"{copy_w:.0f} KiB (factor {gib_kib / copy_w:.4f}); the MB below are scaled by these factors.", "",
+             f"{'kernel':<56} {'dispatches':>10} {'fetch MB':>10} {'write MB':>10}"]
+    for k, v in sorted(sec.items(), key=lambda kv: -kv[1]["fetch_kib"] if isinstance(kv[1], dict) else 0):
+        if isinstance(v, dict):
+            lines.append(f"{k[:56]:<56} {v['dispatches']:>10} {v['fetch_kib'] * 1024 * gib_kib / copy_f / 1e6:>10.2f} "
+                         f"{v['write_kib'] * 1024 * gib_kib / copy_w / 1e6:>10.2f}")
+    with open(os.path.join(ROOT, "profiles", f"{PROFILE_STEMS.get(section, section)}_hbm_traffic.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
     return sec
 
 
@@ -182,7 +205,7 @@ def write_stats(section, stats_csv, command, title):
     lines = [title, "", "Command:", "  " + command, "",
              f"{'kernel':<64} {'calls':>7} {'avg us':>9} {'min us':>9} {'max us':>9}"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"].split("(")[0].replace("dsa::", "")
+        name = _kname(r["Name"])
         avg, mn, mx = float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3
         lines.append(f"{name[:64]:<64} {int(r['Calls']):>7} {avg:>9.2f} {mn:>9.2f} {mx:>9.2f}")
         src = kernel_sources(name)
@@ -192,9 +215,68 @@ def write_stats(section, stats_csv, command, title):
     out["sections"][section] = sec
     with open(STATS_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
-    with open(os.path.join(ROOT, "profiles", f"{section}_kernel_stats.txt"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"{PROFILE_STEMS.get(section, section)}_kernel_stats.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     return sec
+
+
+def write_counters(section, csvs, command, title):
+    """Summarises rocprofv3 --pmc runs of one section (comma-separated counter_collection.csv
+    files, one per pass, each with GRBM_GUI_ACTIVE) into profiles/<stem>_counters.txt: per
+    kernel, over all its dispatches, the busy fractions of the MFMA and VALU units, LDS activity
+    and bank conflicts, wave wait fractions and instruction counts.  Chip constants: 8 XCDs of
+    32 CUs, 4 SIMDs per CU; GRBM_GUI_ACTIVE is summed over the XCDs."""
+    import collections
+    xcd, cus, simds = 8, 256, 1024
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for path in csvs.split(","):
+        seen = collections.defaultdict(lambda: collections.defaultdict(float))
+        for r in _read_csv(path):
+            name = _kname(r["Kernel_Name"])
+            seen[name][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[(name, path)].add(r["Dispatch_Id"])
+        for name, cs in seen.items():
+            gui = cs.pop("GRBM_GUI_ACTIVE", 0.0)
+            for c, v in cs.items():
+                tot[name][c] += v
+                tot[name]["gui:" + c] += gui      # the pass's own cycles, for its counters' ratios
+    lines = [title, "", "Command (one run per pass, counters as listed):"] + ["  " + c for c in command.split(" ;; ")]
+    lines += ["", "Per kernel, summed over its dispatches; busy fractions are of all SIMDs (MFMA, VALU) or CUs (LDS)",
+              "over the kernel's active cycles (GRBM_GUI_ACTIVE / 8 XCDs).  conflict/access = bank-conflict cycles",
+              "per conflict-free LDS cycle.  wait/active = share of wave-cycles waiting / issuing.", ""]
+
+    def ratio(m, c, scale):
+        g = m.get("gui:" + c, 0.0) / xcd
+        return m[c] / (g * scale) if c in m and g else None
+
+    for name, m in sorted(tot.items(), key=lambda kv: -max(v for c, v in kv[1].items() if c.startswith("gui:"))):
+        n = max(len(d) for (k, _), d in disp.items() if k == name)
+        cyc = max(v for c, v in m.items() if c.startswith("gui:")) / xcd
+        parts = [f"{name}", f"  dispatches {n}, active {cyc / 2.4e3 / n:.1f} us per dispatch at 2.4 GHz"]
+        mf, va = ratio(m, "SQ_VALU_MFMA_BUSY_CYCLES", simds), ratio(m, "SQ_ACTIVE_INST_VALU", simds / 4)
+        ld = ratio(m, "SQ_LDS_IDX_ACTIVE", cus)
+        f = []
+        if mf is not None:
+            f.append(f"MFMA busy {100 * mf:.1f}%")
+        if va is not None:
+            f.append(f"VALU {100 * va:.1f}% (SQ_ACTIVE_INST_VALU x 4 cycles / SIMD-cycles)")
+        if ld is not None:
+            conf = m.get("SQ_LDS_BANK_CONFLICT", 0.0)
+            f.append(f"LDS active {100 * ld:.1f}%, conflict/access {conf / max(1.0, m['SQ_LDS_IDX_ACTIVE'] - conf):.3f}")
+        if "SQ_WAVE_CYCLES" in m:
+            wc = m["SQ_WAVE_CYCLES"]
+            f.append(f"wave-cycles: wait {100 * m.get('SQ_WAIT_ANY', 0) / wc:.0f}%, wait on dependency "
+                     f"{100 * m.get('SQ_WAIT_INST_ANY', 0) / wc:.0f}%, issuing {100 * m.get('SQ_ACTIVE_INST_ANY', 0) / wc:.0f}%")
+        if "SQ_INSTS_VALU" in m:
+            f.append("instructions per dispatch: " + ", ".join(
+                f"{c[9:].lower()} {m[c] / n:.3g}" for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+                                                           "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD") if c in m))
+        lines += parts + ["  " + x for x in f] + [""]
+    path = os.path.join(ROOT, "profiles", f"{PROFILE_STEMS.get(section, section)}_counters.txt")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    return path
 
 
 # ----------------------------------------------------------------------------- GPU timing helpers
@@ -718,7 +800,12 @@ def main():
                     help="merge two rocprofv3 --pmc counter files of one section into the traffic summary")
     ap.add_argument("--write-stats", nargs=4, metavar=("SECTION", "STATS_CSV", "COMMAND", "TITLE"),
                     help="merge a rocprofv3 --stats kernel summary of one section into the stats summary")
+    ap.add_argument("--write-counters", nargs=4, metavar=("SECTION", "CSVS", "COMMANDS", "TITLE"),
+                    help="summarise rocprofv3 --pmc passes (comma-separated counter csv files) of one section")
     a = ap.parse_args()
+    if a.write_counters:
+        print(write_counters(*a.write_counters))
+        return
     if a.write_traffic:
         print(json.dumps(write_traffic(*a.write_traffic), indent=1))
         return
