@@ -245,14 +245,14 @@ static dsa_status indexer_topk_impl(const uint8_t* q8, const float* qs, const fl
     // filtered path's extra launches and single-work-group steps.  Every row is flagged, so the
     // exact path's kernels (full scores with the row ranges, histogram, select, final) take it;
     // row groups whose rows are all short are still not scored.
-    hipError_t e = dsa::launch_topk_init(R, k, ws, s, true);
+    hipError_t e = dsa::launch_topk_init(R, k, ws, s, true, true);
     if (e == hipSuccess)
       e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_fallback_mode(ws, R, k, k), fmt,
                                      s);
     if (e == hipSuccess) e = dsa::launch_topk_fallback(logits, stride, rv, k, idx, ws, s);
     return hip_status(e, name);
   }
-  hipError_t e = dsa::launch_topk_init(R, k, ws, s, false);
+  hipError_t e = dsa::launch_topk_init(R, k, ws, s, false, false);
   if (e == hipSuccess)
     e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_sample_mode(ws, R, k, k), fmt, s);
   if (e == hipSuccess) e = dsa::launch_topk_threshold(logits, stride, rv, k, ws, s);

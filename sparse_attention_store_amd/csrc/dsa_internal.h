@@ -83,8 +83,9 @@ hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32
 //  flagging rows whose candidate list is short or overflowed; for the flagged rows only,
 //  full scores (logits kernel, fallback mode) and the radix top-k passes.
 constexpr int kTopkSampleStep = 16;        // one page in sixteen is sampled
-// flag_all: every row is flagged for the radix passes (the fused call's small-array path)
-hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s, bool flag_all);
+// flag_all: every row is flagged for the radix passes (the fused call's small-array path);
+// zero_hist: clear the radix histograms (the filtered path clears only those of flagged rows)
+hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s, bool flag_all, bool zero_hist);
 LogitsMode topk_sample_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto);
 hipError_t launch_topk_threshold(const float* logits, int64_t stride, RowsView rows, int32_t k, void* ws,
                                  hipStream_t s);

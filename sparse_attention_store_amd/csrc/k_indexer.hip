@@ -394,12 +394,13 @@ hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsVie
   const int step = KIND == kLogitsSample ? md.page_step : 1;
   const int64_t total_pages = (stride / 64 + step - 1) / step;      // in units of `step` pages
   // enough work-groups to cover the chip (each page is one wave-iteration); the sampling pass
-  // reads few pages, so it stops at one round of resident work-groups to amortise the q staging
-  const int64_t want = KIND == kLogitsSample ? 1024 : 2048;
+  // reads few pages, so it stops at one round of resident work-groups to amortise the q staging,
+  // and so does the fused call's fallback, whose work-groups mostly find no flagged row and exit
+  const int64_t want = KIND == kLogitsSample || KIND == kLogitsFallback ? 1024 : 2048;
   // 32 pages per work-group; the filter pass, which writes no logits, takes up to 128 as its
   // stage allows (fewer work-groups amortise the q staging: 64 took 3% off the c2 filter pass
   // and 128 1.6% off the 1M prefill indexer, while the logits-writing pass was 1% slower with 64)
-  int chunk = 32;
+  int chunk = KIND == kLogitsFallback ? 128 : 32;
   if (KIND == kLogitsFilter) {
     // a row keeps up to fcap of its visible keys: a work-group's share, chunk * 64 * fcap /
     // visible, should fit its per-row stage

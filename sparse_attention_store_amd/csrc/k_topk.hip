@@ -32,12 +32,13 @@ constexpr int kBins = 4096;          // first digit: 12 bits over the row's key 
 constexpr int kCap = 4096;           // candidates kept per row
 constexpr int kChunk = 8192;         // logits per work-group in passes 1-3
 constexpr int kFinalThreads = 1024;
-// Two 1024-thread work-groups per CU need 8 waves per SIMD, and measured on the device a SIMD
-// holds 8 waves only when each uses at most about 60 scalar registers (a kernel of 76 runs one
-// work-group per CU, whatever its LDS and vector registers), so such kernels cap them.
-#define DSA_TWO_GROUPS_PER_CU __attribute__((amdgpu_num_sgpr(56)))
+// Two 1024-thread work-groups per CU need 8 waves per SIMD: at most 64 vector registers per
+// wave (the second argument of __launch_bounds__ is a minimum of waves per SIMD, not of
+// work-groups per CU), and, measured on the device, at most about 60 scalar registers (a
+// kernel of 76 runs one work-group per CU, whatever its LDS and vector registers).
+#define DSA_TWO_GROUPS_PER_CU __launch_bounds__(kFinalThreads, 8) __attribute__((amdgpu_num_sgpr(56)))
 constexpr int kBufferWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit raw reads
-constexpr int kThrSamples = 16384;  // sampled keys a threshold work-group holds in registers
+constexpr int kThrSamples = 8192;   // sampled keys a threshold work-group holds in registers
 static_assert(kThrSamples % kFinalThreads == 0 && kCap % kFinalThreads == 0, "whole loads per thread");
 constexpr int kBitmapMaxN = 1 << 18; // rows up to 256K positions use the LDS bitmap (32 KiB)
 // fused path: the filter keeps about kMarginNum / kMarginDen times k candidates per row
@@ -94,12 +95,13 @@ __device__ inline int64_t row_len(const int32_t* pos, int r, int64_t stride) {
   return min((int64_t)pos[r] + 1, stride);
 }
 
-// Workspace initialisation: ranges to (max, 0), histograms and counters to 0, every row's
-// exact-path flag to `flag` (1: the rows go straight to the radix passes).
-__global__ void k_init(Ws w, int32_t R, int flag) {
-  const int64_t n_hist = (int64_t)R * kBins;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_hist; i += (int64_t)gridDim.x * blockDim.x) {
-    w.hist[i] = 0;
+// Workspace initialisation: ranges to (max, 0), counters to 0, every row's exact-path flag to
+// `flag` (1: the rows go straight to the radix passes), and, with zero_hist, the histograms to
+// 0 (the fused call's filtered path leaves them: it clears the histogram of each row it flags).
+__global__ void k_init(Ws w, int32_t R, int flag, int zero_hist) {
+  const int64_t n = zero_hist ? (int64_t)R * kBins : (int64_t)R * 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    if (zero_hist) w.hist[i] = 0;
     if (i < (int64_t)R * 4) w.cnt[i] = 0;
     if (i < R) { w.range[2 * i] = 0xFFFFFFFFu; w.range[2 * i + 1] = 0u; w.flag[i] = flag; w.fcnt[i] = 0; }
   }
@@ -155,6 +157,9 @@ __device__ inline void load_chunk(const float* row, int64_t c0, int64_t c1, floa
   }
 }
 
+// Passes 2 and 3 take chunks blockIdx.x, blockIdx.x + gridDim.x, ... of their row: one chunk
+// per work-group for the plain top-k, a few work-groups per row for the fused call's fallback,
+// whose grid is mostly rows that are not flagged and exit at once.
 __global__ void __launch_bounds__(256) k_hist(const float* __restrict__ logits, int64_t stride,
                                               const int32_t* __restrict__ pos, int32_t k, Ws ws,
                                               const int* __restrict__ gate) {
@@ -162,31 +167,33 @@ __global__ void __launch_bounds__(256) k_hist(const float* __restrict__ logits, 
   const int r = blockIdx.y;
   if (gate != nullptr && !gate[r]) return;
   const int64_t n = row_len(pos, r, stride);
-  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-  if (n <= k || c0 >= n) return;
+  if (n <= k) return;
   const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
   const int shift = range_shift(kmin, kmax);
-  const int64_t c1 = min(c0 + kChunk, n);
-  float4 v[kPerThread];
-  load_chunk(logits + (int64_t)r * stride, c0, c1, v);
-  for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < kPerThread; u++) {
-    const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
-    const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-      if (i + j < c1) {
-        // keys outside [kmin, kmax] cannot occur when the range covers the row; clamp anyway
-        const uint32_t key = min(max(ord_key(e[j]), kmin), kmax);
-        atomicAdd(&h[(key - kmin) >> shift], 1);
-      }
-  }
-  __syncthreads();
   int* gh = ws.hist + (int64_t)r * kBins;
-  for (int i = threadIdx.x; i < kBins; i += 256)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
+  for (int64_t c0 = (int64_t)blockIdx.x * kChunk; c0 < n; c0 += (int64_t)gridDim.x * kChunk) {
+    const int64_t c1 = min(c0 + kChunk, n);
+    float4 v[kPerThread];
+    load_chunk(logits + (int64_t)r * stride, c0, c1, v);
+    for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPerThread; u++) {
+      const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (i + j < c1) {
+          // keys outside [kmin, kmax] cannot occur when the range covers the row; clamp anyway
+          const uint32_t key = min(max(ord_key(e[j]), kmin), kmax);
+          atomicAdd(&h[(key - kmin) >> shift], 1);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kBins; i += 256)
+      if (h[i]) atomicAdd(&gh[i], h[i]);
+    __syncthreads();                  // h is cleared again for the next chunk
+  }
 }
 
 // Inclusive prefix sum of v over the NT threads of the work-group in thread order (a wave
@@ -249,57 +256,64 @@ __global__ void __launch_bounds__(256) k_select(const float* __restrict__ logits
   const int r = blockIdx.y;
   if (gate != nullptr && !gate[r]) return;
   const int64_t n = row_len(pos, r, stride);
-  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+  int64_t c0 = (int64_t)blockIdx.x * kChunk;
   if (n <= k || c0 >= n) return;
   const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
   const int shift = range_shift(kmin, kmax);
-  const int64_t c1 = min(c0 + kChunk, n);
   float4 v[kPerThread];
-  load_chunk(logits + (int64_t)r * stride, c0, c1, v);
+  load_chunk(logits + (int64_t)r * stride, c0, min(c0 + kChunk, n), v);
   // the threshold bin from the row's merged histogram (every work-group of the row finds the
-  // same one; the chunk's logits load meanwhile)
+  // same one; the first chunk's logits load meanwhile)
   for (int i = threadIdx.x; i < kBins; i += 256) h[i] = ws.hist[(int64_t)r * kBins + i];
-  if (threadIdx.x == 0) { n_above = 0; n_cand = 0; }
   __syncthreads();
   const uint32_t T = (uint32_t)find_threshold<256, kBins>(h, k, scan, res);
   uint32_t* ckey = ws.ckey + (int64_t)r * kCap;
   int* cpos = ws.cpos + (int64_t)r * kCap;
+  for (;;) {
+    const int64_t c1 = min(c0 + kChunk, n);
+    if (threadIdx.x == 0) { n_above = 0; n_cand = 0; }
+    __syncthreads();
 #pragma unroll
-  for (int u = 0; u < kPerThread; u++) {
-    const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
-    const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    for (int u = 0; u < kPerThread; u++) {
+      const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      if (i + j >= c1) continue;
-      const uint32_t key = min(max(ord_key(e[j]), kmin), kmax);
-      const uint32_t d = (key - kmin) >> shift;
-      if (d > T) {
-        const int sl = atomicAdd(&n_above, 1);
-        if (sl < kTopkMax) l_above[sl] = (int)(i + j);
-      } else if (d == T) {
-        const int sl = atomicAdd(&n_cand, 1);
-        if (sl < kSelCap) {
-          l_ckey[sl] = key; l_cpos[sl] = (int)(i + j);
-        } else {                                  // rare: many ties in this chunk
-          const int gsl = atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], 1);
-          if (gsl < kCap) { ckey[gsl] = key; cpos[gsl] = (int)(i + j); }
+      for (int j = 0; j < 4; j++) {
+        if (i + j >= c1) continue;
+        const uint32_t key = min(max(ord_key(e[j]), kmin), kmax);
+        const uint32_t d = (key - kmin) >> shift;
+        if (d > T) {
+          const int sl = atomicAdd(&n_above, 1);
+          if (sl < kTopkMax) l_above[sl] = (int)(i + j);
+        } else if (d == T) {
+          const int sl = atomicAdd(&n_cand, 1);
+          if (sl < kSelCap) {
+            l_ckey[sl] = key; l_cpos[sl] = (int)(i + j);
+          } else {                                  // rare: many ties in this chunk
+            const int gsl = atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], 1);
+            if (gsl < kCap) { ckey[gsl] = key; cpos[gsl] = (int)(i + j); }
+          }
         }
       }
     }
+    __syncthreads();
+    // fewer than k keys of the whole row lie above T, so n_above < k here
+    const int nc_local = min(n_cand, kSelCap);
+    if (threadIdx.x == 0) {
+      base_above = n_above ? atomicAdd(&ws.cnt[(int64_t)r * 4], n_above) : 0;
+      base_cand = nc_local ? atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], nc_local) : 0;
+    }
+    __syncthreads();
+    int* above = ws.above + (int64_t)r * k;
+    for (int i = threadIdx.x; i < min(n_above, kTopkMax); i += 256)
+      if (base_above + i < k) above[base_above + i] = l_above[i];
+    for (int i = threadIdx.x; i < nc_local; i += 256)
+      if (base_cand + i < kCap) { ckey[base_cand + i] = l_ckey[i]; cpos[base_cand + i] = l_cpos[i]; }
+    c0 += (int64_t)gridDim.x * kChunk;
+    if (c0 >= n) break;
+    load_chunk(logits + (int64_t)r * stride, c0, min(c0 + kChunk, n), v);
+    __syncthreads();                    // the stage and its counters are reused for the next chunk
   }
-  __syncthreads();
-  // fewer than k keys of the whole row lie above T, so n_above < k here
-  const int nc_local = min(n_cand, kSelCap);
-  if (threadIdx.x == 0) {
-    base_above = n_above ? atomicAdd(&ws.cnt[(int64_t)r * 4], n_above) : 0;
-    base_cand = nc_local ? atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], nc_local) : 0;
-  }
-  __syncthreads();
-  int* above = ws.above + (int64_t)r * k;
-  for (int i = threadIdx.x; i < min(n_above, kTopkMax); i += 256)
-    if (base_above + i < k) above[base_above + i] = l_above[i];
-  for (int i = threadIdx.x; i < nc_local; i += 256)
-    if (base_cand + i < kCap) { ckey[base_cand + i] = l_ckey[i]; cpos[base_cand + i] = l_cpos[i]; }
 }
 
 __device__ inline void push(int* sel, int* n, int v) {
@@ -464,7 +478,7 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
 // m-th largest sample, so at least m samples, and about margin * k of the row's scores,
 // lie at or above it.  Short rows (n <= k) get a threshold nothing reaches; rows with too
 // few samples get 0 (every score passes).
-__global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt_thresh(const float* __restrict__ logits, int64_t stride,
+__global__ void DSA_TWO_GROUPS_PER_CU k_filt_thresh(const float* __restrict__ logits, int64_t stride,
                                                                   const int32_t* __restrict__ pos, int32_t k, Ws ws) {
   constexpr int step = kTopkSampleStep;
   __shared__ int h[kBins];
@@ -552,10 +566,10 @@ __global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt
 }
 
 // The need-th largest (1 <= need <= cnt) of keys[0..cnt) in LDS, all in [base, base + 2^width),
-// in radix rounds of at most 11 bits over (key - base) from bit `width` down.  need_eq receives
+// in radix rounds of at most 12 bits over (key - base) from bit `width` down.  need_eq receives
 // how many keys equal to it belong to the need largest.  All kFinalThreads threads call it;
 // h holds kFinalBins ints.
-constexpr int kFinalBits = 11;
+constexpr int kFinalBits = 12;
 constexpr int kFinalBins = 1 << kFinalBits;
 __device__ inline uint32_t kth_largest(const uint32_t* keys, int cnt, int need, uint32_t base, int width, int* h,
                                        int* scan, int* res, int& need_eq) {
@@ -587,7 +601,7 @@ __device__ inline uint32_t kth_largest(const uint32_t* keys, int cnt, int need, 
 // fallback instead.  Among exactly equal scores at the k-th the lower positions are kept:
 // the tied positions go to their own list, and when it holds more than are needed a second
 // selection over the complemented positions picks the lowest.
-__global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ pos, int64_t stride,
+__global__ void DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ pos, int64_t stride,
                                                               int32_t k, int32_t* __restrict__ idx, Ws ws) {
   // Under 64 KiB of LDS, so two work-groups share a CU.  The candidates (keys, then positions)
   // and, once they are selected, the output bitmap share one buffer; the radix histogram lives
@@ -612,7 +626,8 @@ __global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt
     return;
   }
   const int c = ws.fcnt[r];
-  if (c < k || c > kCap) {            // the filter kept too few (or too many): exact fallback
+  if (c < k || c > kCap) {            // the filter kept too few (or too many): exact fallback,
+    for (int i = tid; i < kBins; i += kFinalThreads) ws.hist[(int64_t)r * kBins + i] = 0;   // from a clear histogram
     if (tid == 0) ws.flag[r] = 1;
     return;
   }
@@ -635,7 +650,8 @@ __global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt
       if (i < c) { skey[i] = key[j]; spos[i] = p[j]; mx = max(mx, key[j]); }
     }
   }
-  atomicMax(&cmax, mx);
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  if ((tid & 63) == 0) atomicMax(&cmax, mx);     // one LDS atomic per wave, not per thread
   __syncthreads();
   // every candidate lies in [filter threshold, cmax]: the rounds start at that span's width
   const uint32_t base = ws.thr[r];
@@ -664,21 +680,24 @@ __global__ void __launch_bounds__(kFinalThreads, 2) DSA_TWO_GROUPS_PER_CU k_filt
 
 size_t topk_workspace_bytes(int32_t R, int64_t /*stride*/, int32_t k) { return ws_bytes(R, k); }
 
-hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s, bool flag_all) {
+hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s, bool flag_all, bool zero_hist) {
   Ws w = carve(ws, R, k);
-  const int64_t n = (int64_t)R * kBins;
+  const int64_t n = zero_hist ? (int64_t)R * kBins : (int64_t)R * 4;
   const int64_t grid = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-  hipLaunchKernelGGL(k_init, dim3((unsigned)grid), dim3(256), 0, s, w, R, flag_all ? 1 : 0);
+  hipLaunchKernelGGL(k_init, dim3((unsigned)grid), dim3(256), 0, s, w, R, flag_all ? 1 : 0, zero_hist ? 1 : 0);
   return hipGetLastError();
 }
 
-// Passes 2-4 (the row ranges are already in the workspace); gate: only flagged rows.
+// Passes 2-4 (the row ranges are already in the workspace); gate: only flagged rows, which
+// then take kGatedChunkGroups work-groups each for passes 2 and 3.
+constexpr unsigned kGatedChunkGroups = 4;
 static hipError_t launch_radix_passes(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
                                       Ws w, const int* gate, hipStream_t s) {
   const int R = rows.n;
   const int64_t visible = (int64_t)rows.max_pos + 1;
   if (visible > k) {
-    const unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
+    unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
+    if (gate != nullptr && nchunk > kGatedChunkGroups) nchunk = kGatedChunkGroups;
     hipLaunchKernelGGL(k_hist, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
     hipLaunchKernelGGL(k_select, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
   }
@@ -690,7 +709,7 @@ hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32
                        hipStream_t s) {
   const int R = rows.n;
   if (R <= 0) return hipSuccess;
-  hipError_t e = launch_topk_init(R, k, ws, s, false);
+  hipError_t e = launch_topk_init(R, k, ws, s, false, true);
   if (e != hipSuccess) return e;
   Ws w = carve(ws, R, k);
   const int64_t visible = (int64_t)rows.max_pos + 1;

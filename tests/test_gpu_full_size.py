@@ -280,7 +280,22 @@ def _fused_topk_case(w, overrides, expect_fallback):
     dsa.dsa_topk(L.logits, L.rows, 2048, L.idx, L.ws_topk)
     torch.cuda.synchronize()
     assert np.array_equal(host(L.idx), gidx)
+    # the fused call again, on the workspace the radix top-k just filled (its histograms are
+    # not cleared for the filtered path: a flagged row clears its own)
+    L.idx.fill_(-7)
+    L.indexer_topk(0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(L.idx), gidx)
     return gidx, ridx
+
+
+def _too_few_needles(w, n, seed):
+    """1000 needles of request 0, 600 of them on sampled pages: the sample sets the threshold
+    among the needles, so fewer than k scores pass the filter and the row is flagged."""
+    rng = np.random.default_rng(seed)
+    sampled = np.array([s for s in range(n - 1) if (s // 64) % SAMPLE_STEP == 0])
+    others = np.array([s for s in range(n - 1) if (s // 64) % SAMPLE_STEP != 0])
+    return np.sort(np.concatenate([rng.choice(sampled, 600, replace=False), rng.choice(others, 400, replace=False)]))
 
 
 def _equal_score_key():
@@ -295,10 +310,18 @@ def test_fused_topk_fallback_when_filter_keeps_too_few():
     _announce("fused top-k: filter keeps fewer than k -> exact fallback")
     n = 30000
     w = gi.make_decode("fb_few", gi.SEED_BASE + 70, [n])
-    rng = np.random.default_rng(70)
-    sampled = np.array([s for s in range(n - 1) if (s // 64) % SAMPLE_STEP == 0])
-    others = np.array([s for s in range(n - 1) if (s // 64) % SAMPLE_STEP != 0])
-    w.needles = np.sort(np.concatenate([rng.choice(sampled, 600, replace=False), rng.choice(others, 400, replace=False)]))
+    w.needles = _too_few_needles(w, n, 70)
+    gidx, ridx = _fused_topk_case(w, needle_overrides(w), expect_fallback=True)
+    assert set(w.needles.tolist()) <= set(gidx[0].tolist())
+
+
+def test_fused_topk_fallback_long_row_beside_a_filtered_row():
+    """A flagged row of 100,000 positions (13 score chunks: each of the fallback's work-groups
+    of the row takes several) beside a row of 60,000 that stays on the filtered path."""
+    _announce("fused top-k: long flagged row + filtered row")
+    n = 100000
+    w = gi.make_decode("fb_long", gi.SEED_BASE + 73, [n, 60000])
+    w.needles = _too_few_needles(w, n, 73)
     gidx, ridx = _fused_topk_case(w, needle_overrides(w), expect_fallback=True)
     assert set(w.needles.tolist()) <= set(gidx[0].tolist())
 
