@@ -255,15 +255,24 @@ dsa_status dsa_topk(const float* logits, int64_t stride, const dsa_rows* rows, i
  * depends on the sample.  `logits` is scratch: on return it holds the sampled pages'
  * scores and the full scores of rows that fell back; other entries are unspecified.  A
  * row group (rows->group consecutive rows) whose rows all have pos + 1 <= k is not scored
- * ([IDXC] §优化二:短上下文直接跳过打分).  A call whose R x stride is at most 4096 scores
- * writes every score and takes the radix top-k directly (the filter's extra steps cost more
- * than they save there); the result is the same.  Arguments as for the two calls; ws sized by
+ * ([IDXC] §优化二:短上下文直接跳过打分).  A call whose R x stride is at most the direct
+ * limit (dsa_set_topk_direct_limit; 4,194,304 scores by default) writes every score and takes
+ * the radix top-k directly (the filter's extra steps cost more than they save there); the
+ * result is the same.  Arguments as for the two calls; ws sized by
  * dsa_topk_workspace_size(R, stride, k).  index_cache must not be NULL (a shared layer
  * reuses the full layer's idx instead). */
 dsa_status dsa_indexer_topk(const uint8_t* q_fp8, const float* q_scale, const float* w,
                             const dsa_rows* rows, const dsa_pages* pt, const uint8_t* index_cache,
                             float* logits, int64_t stride, int32_t k, int32_t* idx,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* Tuning: the score-array size (R x stride) up to which dsa_indexer_topk and
+ * dsa_indexer_topk_mxfp4 write every score and take the radix top-k directly instead of the
+ * sampled-threshold filter (both give the same idx; which is faster depends on the shape).
+ * Sets the limit for the process and returns the previous one; a negative argument only
+ * returns the current limit.  0 sends every call with a row longer than k through the filter.
+ * Takes effect for calls issued after it returns. */
+int64_t dsa_set_topk_direct_limit(int64_t max_scores);
 
 /* The fused indexer + top-k against an MXFP4 index-K cache: the same idx as
  * dsa_indexer_logits_mxfp4 followed by dsa_topk.  Arguments and errors as dsa_indexer_topk. */

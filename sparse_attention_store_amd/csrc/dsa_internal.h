@@ -93,8 +93,9 @@ LogitsMode topk_filter_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto);
 hipError_t launch_topk_filtered_final(RowsView rows, int64_t stride, int32_t k, int32_t* idx, void* ws,
                                       hipStream_t s);
 LogitsMode topk_fallback_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto = 0);
+// all_flagged: every row takes the radix passes (the direct path), so they get full grids
 hipError_t launch_topk_fallback(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
-                                void* ws, hipStream_t s);
+                                void* ws, bool all_flagged, hipStream_t s);
 
 size_t mla_workspace_bytes(int32_t R, int32_t k);
 // The allocation-free entry point's fixed scratch: its size, and its device address on the

@@ -19,7 +19,7 @@
 //  4. k_final:  one work-group per row resolves the low `shift` bits over the candidates in
 //               LDS (10-bit rounds), keeps the lowest positions among exact ties at the
 //               threshold, and writes the k positions in ascending order via an LDS bitmap of
-//               the row (or an LDS bitonic sort for rows too long for the bitmap).  If more
+//               the row (or a bitonic sort for rows too long for the bitmap).  If more
 //               candidates than fit in LDS share the threshold bin (massive exact ties), the
 //               rounds and the tie walk run over the row in global memory instead.
 #include "dsa_device.hpp"
@@ -38,8 +38,11 @@ constexpr int kFinalThreads = 1024;
 // kernel of 76 runs one work-group per CU, whatever its LDS and vector registers).
 #define DSA_TWO_GROUPS_PER_CU __launch_bounds__(kFinalThreads, 8) __attribute__((amdgpu_num_sgpr(56)))
 constexpr int kBufferWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit raw reads
-constexpr int kThrSamples = 8192;   // sampled keys a threshold work-group holds in registers
-static_assert(kThrSamples % kFinalThreads == 0 && kCap % kFinalThreads == 0, "whole loads per thread");
+// sampled keys a threshold work-group holds in registers: 8 per thread in the kernel two
+// work-groups of which share a CU, 32 per thread (a row of up to 512K positions) in the one for
+// launches with longer rows
+constexpr int kThrPer = 8, kThrPerLong = 32;
+static_assert(kCap % kFinalThreads == 0, "whole loads per thread");
 constexpr int kBitmapMaxN = 1 << 18; // rows up to 256K positions use the LDS bitmap (32 KiB)
 // fused path: the filter keeps about kMarginNum / kMarginDen times k candidates per row
 constexpr int kMarginNum = 3, kMarginDen = 2;
@@ -321,24 +324,10 @@ __device__ inline void push(int* sel, int* n, int v) {
   if (s < kTopkMax) sel[s] = v;
 }
 
-// In-LDS bitonic sort of n (power of two) ints ascending.
-__device__ inline void bitonic_sort(int* a, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int st = size >> 1; st > 0; st >>= 1) {
-      for (int i = threadIdx.x; i < n / 2; i += kFinalThreads) {
-        const int lo = 2 * i - (i & (st - 1)), hi = lo + st;
-        const bool up = ((lo & size) == 0);
-        const int x = a[lo], y = a[hi];
-        if ((x > y) == up) { a[lo] = y; a[hi] = x; }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 // Writes the ns <= k selected positions sel[] of a row of n positions to out[0..k) in
 // ascending order, -1 after them: an LDS bitmap of the row and a prefix count of set bits
-// (rows up to kBitmapMaxN), else an LDS bitonic sort.  All kFinalThreads threads call it.
+// (rows up to kBitmapMaxN), else a bitonic sort in registers and LDS.  All kFinalThreads
+// threads call it.
 __device__ inline void write_ascending(int* sel, int ns, int64_t n, int k, int32_t* out, uint32_t* bitmap,
                                        int* scan) {
   const int tid = threadIdx.x;
@@ -365,12 +354,41 @@ __device__ inline void write_ascending(int* sel, int ns, int64_t n, int k, int32
     }
     for (int j = ns + tid; j < k; j += kFinalThreads) out[j] = -1;
   } else {
-    for (int i = ns + tid; i < kTopkMax; i += kFinalThreads) sel[i] = 0x7FFFFFFF;
-    __syncthreads();
+    // a bitonic sort of the selection padded to m (a power of two <= 2 * kFinalThreads): thread
+    // t holds elements 2t and 2t + 1; the partner of a compare-exchange at stride st is thread
+    // t ^ (st / 2), in the same wave up to st = 64 (a lane shuffle) and through LDS above
+    static_assert(kTopkMax <= 2 * kFinalThreads, "two elements per thread");
     int m = 1;
     while (m < k) m <<= 1;
-    bitonic_sort(sel, m);
-    for (int j = tid; j < k; j += kFinalThreads) out[j] = j < ns ? sel[j] : -1;
+    int e0 = 2 * tid < ns ? sel[2 * tid] : 0x7FFFFFFF;
+    int e1 = 2 * tid + 1 < ns ? sel[2 * tid + 1] : 0x7FFFFFFF;
+    __syncthreads();                  // sel is the exchange buffer from here on
+    for (int size = 2; size <= m; size <<= 1) {
+      const bool asc = ((2 * tid) & size) == 0;
+      for (int st = size >> 1; st > 1; st >>= 1) {
+        const int pl = st >> 1;
+        int p0, p1;
+        if (pl < 64) {
+          p0 = __shfl_xor(e0, pl, 64);
+          p1 = __shfl_xor(e1, pl, 64);
+        } else {
+          sel[2 * tid] = e0;
+          sel[2 * tid + 1] = e1;
+          __syncthreads();
+          p0 = sel[2 * (tid ^ pl)];
+          p1 = sel[2 * (tid ^ pl) + 1];
+          __syncthreads();
+        }
+        const bool keep_min = ((tid & pl) == 0) == asc;   // the lower index keeps the min when ascending
+        e0 = keep_min ? min(e0, p0) : max(e0, p0);
+        e1 = keep_min ? min(e1, p1) : max(e1, p1);
+      }
+      const int lo = min(e0, e1), hi = max(e0, e1);      // stride 1: the thread's own pair
+      e0 = asc ? lo : hi;
+      e1 = asc ? hi : lo;
+    }
+    if (2 * tid < k) out[2 * tid] = 2 * tid < ns ? e0 : -1;
+    if (2 * tid + 1 < k) out[2 * tid + 1] = 2 * tid + 1 < ns ? e1 : -1;
   }
 }
 
@@ -478,9 +496,11 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
 // m-th largest sample, so at least m samples, and about margin * k of the row's scores,
 // lie at or above it.  Short rows (n <= k) get a threshold nothing reaches; rows with too
 // few samples get 0 (every score passes).
-__global__ void DSA_TWO_GROUPS_PER_CU k_filt_thresh(const float* __restrict__ logits, int64_t stride,
-                                                                  const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+template <int kPer>
+__device__ inline void filt_thresh(const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ pos,
+                                   int32_t k, Ws ws) {
   constexpr int step = kTopkSampleStep;
+  constexpr int kThrSamples = kPer * kFinalThreads;
   __shared__ int h[kBins];
   __shared__ int scan[kFinalThreads / 64];
   __shared__ int res[2];
@@ -502,7 +522,6 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_thresh(const float* __restrict__ lo
   const float* row = logits + (int64_t)r * stride;
   // rows with few enough samples keep theirs in registers for both rounds, all requested
   // before any is used (the pass is latency-bound, not bandwidth-bound)
-  constexpr int kPer = kThrSamples / kFinalThreads;
   const bool held = ns <= kThrSamples;
   uint32_t v[kPer];
   if (held) {
@@ -513,11 +532,10 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_thresh(const float* __restrict__ lo
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, (int)(n * 4), kBufferWord3);
     const int o0 = ((tid >> 6) * (step * 64) + (tid & 63)) * 4;
     constexpr int kJump = (kFinalThreads / 64) * step * 64 * 4;
-    float x[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; j++) x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o0, j * kJump, 0));
+    for (int j = 0; j < kPer; j++) v[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, o0 + j * kJump, 0, 0);
 #pragma unroll
-    for (int j = 0; j < kPer; j++) v[j] = min(max(ord_key(x[j]), kmin), kmax) - kmin;
+    for (int j = 0; j < kPer; j++) v[j] = min(max(ord_key(__uint_as_float(v[j])), kmin), kmax) - kmin;
   }
   // this thread's samples are v[0 .. jn): sample tid + j * kFinalThreads exists for j < jn
   const int jn = held ? (int)min((int64_t)kPer, (ns - tid + kFinalThreads - 1) / kFinalThreads) : 0;
@@ -536,19 +554,20 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_thresh(const float* __restrict__ lo
       for (int j = 0; j < kPer; j++)
         if (j < jn && (low >= 32 || (v[j] >> low) == prefix)) atomicAdd(&h[(v[j] >> sh) & (kBins - 1)], 1);
     } else {
-      // more samples than the registers hold: batches of kThrSamples, every load of a batch
-      // issued before any is used (one dependent load per sample would be a memory round trip
-      // per iteration)
-      for (int64_t i0 = 0; i0 < ns; i0 += kThrSamples) {
-        float x[kPer];
+      // more samples than the registers hold: batches of kBatch per thread, every load of a
+      // batch issued before any is used (one dependent load per sample would be a memory round
+      // trip per iteration)
+      constexpr int kBatch = kPer < 16 ? kPer : 16;
+      for (int64_t i0 = 0; i0 < ns; i0 += kBatch * kFinalThreads) {
+        float x[kBatch];
 #pragma unroll
-        for (int j = 0; j < kPer; j++) {
+        for (int j = 0; j < kBatch; j++) {
           const int64_t i = i0 + tid + (int64_t)j * kFinalThreads;
           const int64_t s = (min(i, ns - 1) >> 6) * step * 64 + (min(i, ns - 1) & 63);
           x[j] = row[s];
         }
 #pragma unroll
-        for (int j = 0; j < kPer; j++) {
+        for (int j = 0; j < kBatch; j++) {
           const int64_t i = i0 + tid + (int64_t)j * kFinalThreads;
           const uint32_t u = min(max(ord_key(x[j]), kmin), kmax) - kmin;
           if (i < ns && (low >= 32 || (u >> low) == prefix)) atomicAdd(&h[(u >> sh) & (kBins - 1)], 1);
@@ -563,6 +582,15 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_thresh(const float* __restrict__ lo
     __syncthreads();
   }
   if (tid == 0) ws.thr[r] = kmin + (prefix << low);   // lower edge of the final bin
+}
+
+__global__ void DSA_TWO_GROUPS_PER_CU k_filt_thresh(const float* __restrict__ logits, int64_t stride,
+                                                    const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+  filt_thresh<kThrPer>(logits, stride, pos, k, ws);
+}
+__global__ void __launch_bounds__(kFinalThreads) k_filt_thresh_long(const float* __restrict__ logits, int64_t stride,
+                                                                     const int32_t* __restrict__ pos, int32_t k, Ws ws) {
+  filt_thresh<kThrPerLong>(logits, stride, pos, k, ws);
 }
 
 // The need-th largest (1 <= need <= cnt) of keys[0..cnt) in LDS, all in [base, base + 2^width),
@@ -688,16 +716,17 @@ hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s, bool 
   return hipGetLastError();
 }
 
-// Passes 2-4 (the row ranges are already in the workspace); gate: only flagged rows, which
-// then take kGatedChunkGroups work-groups each for passes 2 and 3.
+// Passes 2-4 (the row ranges are already in the workspace); gate: only flagged rows.  With
+// few_flagged (the fused call's fallback, where most rows are not flagged and their
+// work-groups exit at once), a row takes kGatedChunkGroups work-groups for passes 2 and 3.
 constexpr unsigned kGatedChunkGroups = 4;
 static hipError_t launch_radix_passes(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
-                                      Ws w, const int* gate, hipStream_t s) {
+                                      Ws w, const int* gate, bool few_flagged, hipStream_t s) {
   const int R = rows.n;
   const int64_t visible = (int64_t)rows.max_pos + 1;
   if (visible > k) {
     unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
-    if (gate != nullptr && nchunk > kGatedChunkGroups) nchunk = kGatedChunkGroups;
+    if (few_flagged && nchunk > kGatedChunkGroups) nchunk = kGatedChunkGroups;
     hipLaunchKernelGGL(k_hist, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
     hipLaunchKernelGGL(k_select, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
   }
@@ -717,7 +746,7 @@ hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32
     const unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
     hipLaunchKernelGGL(k_range, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, nullptr);
   }
-  return launch_radix_passes(logits, stride, rows, k, idx, w, nullptr, s);
+  return launch_radix_passes(logits, stride, rows, k, idx, w, nullptr, false, s);
 }
 
 LogitsMode topk_sample_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto) {
@@ -731,8 +760,14 @@ LogitsMode topk_sample_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto) {
 
 hipError_t launch_topk_threshold(const float* logits, int64_t stride, RowsView rows, int32_t k, void* ws,
                                  hipStream_t s) {
-  hipLaunchKernelGGL(k_filt_thresh, dim3(rows.n), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k,
-                     carve(ws, rows.n, k));
+  // samples of the longest row: one page in kTopkSampleStep, 64 positions each
+  const int64_t max_samples = (((int64_t)rows.max_pos + 64) / 64 + kTopkSampleStep - 1) / kTopkSampleStep * 64;
+  if (max_samples <= (int64_t)kThrPer * kFinalThreads)
+    hipLaunchKernelGGL(k_filt_thresh, dim3(rows.n), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k,
+                       carve(ws, rows.n, k));
+  else
+    hipLaunchKernelGGL(k_filt_thresh_long, dim3(rows.n), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k,
+                       carve(ws, rows.n, k));
   return hipGetLastError();
 }
 
@@ -768,9 +803,9 @@ LogitsMode topk_fallback_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto)
 }
 
 hipError_t launch_topk_fallback(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
-                                void* ws, hipStream_t s) {
+                                void* ws, bool all_flagged, hipStream_t s) {
   const Ws w = carve(ws, rows.n, k);
-  return launch_radix_passes(logits, stride, rows, k, idx, w, w.flag, s);
+  return launch_radix_passes(logits, stride, rows, k, idx, w, w.flag, !all_flagged, s);
 }
 
 DSA_DEFINE_ERROR_ACCESSOR(take_device_errors_topk)

@@ -69,6 +69,7 @@ def _load():
         "dsa_fused_norm_rope_store": ([p, i64, p, p, R, P, p, p, p, i64, i64, f64, f64, f64, f64, p], ctypes.c_int),
         "dsa_logits_stride": ([i32], i64),
         "dsa_logits_rows_per_chunk": ([i64, i64, i64], i64),
+        "dsa_set_topk_direct_limit": ([i64], i64),
         "dsa_indexer_logits": ([p, p, p, R, P, p, p, i64, p], ctypes.c_int),
         "dsa_indexer_logits_mxfp4": ([p, p, p, R, P, p, p, i64, p], ctypes.c_int),
         "dsa_topk_workspace_size": ([i32, i64, i32], sz),
@@ -93,7 +94,8 @@ EXPORTED = ("dsa_abi_version", "dsa_last_error", "dsa_layer_is_shared", "dsa_mtp
             "dsa_quant_fp8",
             "dsa_index_k_store", "dsa_index_k_store_mxfp4", "dsa_latent_store", "dsa_fused_norm_rope_store", "dsa_logits_stride",
             "dsa_logits_rows_per_chunk", "dsa_indexer_logits", "dsa_indexer_logits_mxfp4", "dsa_topk_workspace_size",
-            "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_mxfp4", "dsa_sparse_mla_workspace_size",
+            "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_mxfp4", "dsa_set_topk_direct_limit",
+            "dsa_sparse_mla_workspace_size",
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_sparse_mla_decode_noalloc",
             "dsa_check_device_errors")
 
@@ -217,6 +219,12 @@ def dsa_indexer_logits_mxfp4(q8, q_scale, w, rows: Rows, pages: Pages, index_cac
     r, p = rows.c(), pages.c()
     _check(_lib.dsa_indexer_logits_mxfp4(_ptr(q8), _ptr(q_scale), _ptr(w), ctypes.byref(r), ctypes.byref(p),
                                          _ptr(index_cache), _ptr(logits), logits.shape[-1], _stream(stream)))
+
+
+def dsa_set_topk_direct_limit(max_scores: int) -> int:
+    """Sets the score-array size up to which the fused indexer + top-k takes the radix path
+    directly; returns the previous limit (a negative argument only reads it)."""
+    return int(_lib.dsa_set_topk_direct_limit(max_scores))
 
 
 def dsa_topk_workspace_size(R: int, stride: int, k: int) -> int:

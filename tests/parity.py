@@ -12,6 +12,8 @@ Tolerances (the stated parity bar):
 """
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 
 import dsa_inputs as gi
@@ -162,3 +164,19 @@ def row_queries(w: gi.Workload, rows, layers):
     qm = {l: np.stack([gi.normal_bf16(w.seed, gi.T_MLA_Q, (l * w.rows_total + r) * 64 * 576, 64 * 576)
                        for r in rows]).reshape(-1, 64, 576) for l in layers}
     return q, wt, qm
+
+
+@contextlib.contextmanager
+def topk_path(path):
+    """Which path the fused indexer + top-k takes inside the block: "filtered" (sampled
+    threshold, filter pass, exact selection over the candidates) for every call, "direct"
+    (every score written, radix top-k) for every call, None the library's size rule."""
+    from sparse_attention_store_amd import dsa
+    if path is None:
+        yield
+        return
+    prev = dsa.dsa_set_topk_direct_limit({"filtered": 0, "direct": 1 << 62}[path])
+    try:
+        yield
+    finally:
+        dsa.dsa_set_topk_direct_limit(prev)

@@ -51,6 +51,15 @@ def test_layer_rule_matches_oracle(lib, orc):
             assert lib.dsa_layer_is_shared(l, **kw) == orc.layer_is_shared(l, **okw), (kw, l)
 
 
+def test_topk_direct_limit_setter(lib):
+    default = lib.dsa_set_topk_direct_limit(-1)
+    assert default == 1 << 22
+    assert lib.dsa_set_topk_direct_limit(0) == default
+    assert lib.dsa_set_topk_direct_limit(-5) == 0
+    assert lib.dsa_set_topk_direct_limit(default) == 0
+    assert lib.dsa_set_topk_direct_limit(-1) == default
+
+
 def test_stride_and_chunking(lib, orc):
     for p in [0, 1, 254, 255, 256, 4095, 131071, 1048575]:
         assert lib.dsa_logits_stride(p) == orc.logits_stride(p)

@@ -13,7 +13,7 @@ import dsa_inputs as gi
 import oracle as orc
 from parity import (SM, assert_attention_close, assert_logits_close, needle_overrides, oracle_index_cache,
                     oracle_index_cache_of, oracle_latent_cache, oracle_latent_cache_of, queries, row_queries,
-                    topk_sets_match)
+                    topk_path, topk_sets_match)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,12 +105,14 @@ def test_full_c2_verify_128k_sampled_requests():
     _release(L)
 
 
-def test_full_c3_long_1m_needles():
-    _announce("full size c3: 1 request at 1M context, 2048 needles")
+@pytest.mark.parametrize("path", ["direct", "filtered"])
+def test_full_c3_long_1m_needles(path):
+    _announce(f"full size c3: 1 request at 1M context, 2048 needles, {path} top-k")
     w = gi.config(3, "full")
     ov = needle_overrides(w)
     L = DeviceLayer(w, k_overrides=ov)
-    L.group_step()
+    with topk_path(path):
+        L.group_step()
     torch.cuda.synchronize()
     gidx = host(L.idx)[0]
     assert np.array_equal(gidx, np.sort(w.needles)), "top-k must be exactly the needle set, ascending"
@@ -243,7 +245,8 @@ def test_fused_equals_separate_where_sampled_pages_are_reused(name, ctx, rows):
     assert chunk >= 16 and chunk % 16 == 0, f"filter chunk {chunk}: the sampled-page reuse would not run"
     L = DeviceLayer(w)
     dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
-    L.indexer_topk(0)
+    with topk_path("filtered"):
+        L.indexer_topk(0)
     torch.cuda.synchronize()
     fused = host(L.idx).copy()
     dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
@@ -258,10 +261,13 @@ SAMPLE_STEP = 16    # the fused path scores one page in SAMPLE_STEP to set its f
 
 
 def _fused_topk_case(w, overrides, expect_fallback):
+    """The filtered path of the fused call on one workload: whether row 0 fell back, its
+    selection against the oracle and against the separate calls."""
     L = DeviceLayer(w, k_overrides=overrides)
     L.logits.fill_(float("nan"))
     dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
-    L.indexer_topk(0)
+    with topk_path("filtered"):
+        L.indexer_topk(0)
     torch.cuda.synchronize()
     gidx, glg = host(L.idx), host(L.logits)
     # which path the row took: the exact fallback scores every page, the filtered path
@@ -283,7 +289,8 @@ def _fused_topk_case(w, overrides, expect_fallback):
     # the fused call again, on the workspace the radix top-k just filled (its histograms are
     # not cleared for the filtered path: a flagged row clears its own)
     L.idx.fill_(-7)
-    L.indexer_topk(0)
+    with topk_path("filtered"):
+        L.indexer_topk(0)
     torch.cuda.synchronize()
     assert np.array_equal(host(L.idx), gidx)
     return gidx, ridx
@@ -336,8 +343,43 @@ def test_fused_topk_fallback_when_candidates_overflow():
 
 def test_fused_topk_ties_inside_candidate_list():
     _announce("fused top-k: all scores equal, 3000 candidates -> exact within the list")
-    # two rows: R x stride above the size up to which the fused call takes the radix path directly
     w = gi.make_decode("fb_ties", gi.SEED_BASE + 72, [3000], rows_per_req=2)
     key = _equal_score_key()
     gidx, ridx = _fused_topk_case(w, {p: key for p in range(3000)}, expect_fallback=False)
     assert np.array_equal(gidx[0], np.arange(2048))
+
+
+@pytest.mark.parametrize("path", ["direct", "filtered"])
+@pytest.mark.parametrize("k", [100, 1000, 2048])
+def test_topk_row_longer_than_the_bitmap(k, path):
+    """Rows of 300,000 and 600,000 positions, longer than the LDS bitmap that orders the output
+    of shorter rows: the selection is ordered by a bitonic network padded to a power of two
+    (128, 1024, 2048), and rows of over 8,192 samples take the long threshold kernel.  The fused
+    and the separate calls against the oracle's set; both ascending and equal."""
+    _announce(f"top-k of rows longer than the bitmap, k={k}, {path} fused path")
+    w = gi.make_decode("long_rows_k", gi.SEED_BASE + 74, [300000, 600000])
+    L = DeviceLayer(w, latent_layers=[])
+    dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
+    cache = oracle_index_cache(w)
+    q, wt, _ = queries(w, [])
+    q8, qs = orc.quant_fp8(q.reshape(-1, 128))
+    lg = orc.indexer_logits(q8.reshape(-1, 32, 128), qs.reshape(-1, 32), wt, w.row_req, w.row_pos, w.page_table,
+                            cache)
+    ridx, kth = orc.topk(lg, w.row_pos, k)
+    stride = L.logits.shape[-1]
+    ws = torch.empty(max(dsa.dsa_topk_workspace_size(w.R, stride, k), 256), dtype=torch.uint8, device="cuda")
+    idx = torch.full((w.R, k), -7, dtype=torch.int32, device="cuda")
+    with topk_path(path):
+        dsa.dsa_indexer_topk(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits, k, idx, ws)
+    torch.cuda.synchronize()
+    fused = host(idx)
+    dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
+    idx.fill_(-7)
+    dsa.dsa_topk(L.logits, L.rows, k, idx, ws)
+    torch.cuda.synchronize()
+    sep = host(idx)
+    for g in (fused, sep):
+        assert np.all(np.diff(g, axis=1) > 0), "positions not strictly ascending"
+    assert np.array_equal(fused, sep)
+    topk_sets_match(fused, ridx, lg, kth)                 # differences only at near-ties
+    dsa.dsa_check_device_errors()

@@ -8,7 +8,7 @@ import torch
 
 import dsa_inputs as gi
 import oracle as orc
-from parity import LN_EPS, THETA, all_tokens, assert_logits_close, queries, raw_k, topk_sets_match
+from parity import LN_EPS, THETA, all_tokens, assert_logits_close, queries, raw_k, topk_path, topk_sets_match
 
 pytestmark = pytest.mark.gpu
 
@@ -86,9 +86,10 @@ def test_mxfp4_logits_stage(cid):
     assert_logits_close(host(logits), ref)
 
 
+@pytest.mark.parametrize("path", ["direct", "filtered"])
 @pytest.mark.parametrize("cid", [0, 1, 2])
-def test_mxfp4_fused_topk(cid):
-    _announce(f"mxfp4 fused indexer+topk c{cid}")
+def test_mxfp4_fused_topk(cid, path):
+    _announce(f"mxfp4 fused indexer+topk c{cid}, {path} path")
     w = gi.config(cid, "small")
     cache = gpu_mx_cache(w)
     q8, qs, wt = q_inputs(w)
@@ -98,7 +99,8 @@ def test_mxfp4_fused_topk(cid):
     idx = torch.full((w.R, 2048), -7, dtype=torch.int32, device=DEV)
     ws = torch.empty(dsa.dsa_topk_workspace_size(w.R, stride, 2048), dtype=torch.uint8, device=DEV)
     dq8, dqs, dwt = dev(q8), dev(qs), dev(wt)
-    dsa.dsa_indexer_topk_mxfp4(dq8, dqs, dwt, rows, pages, cache, logits, 2048, idx, ws)
+    with topk_path(path):
+        dsa.dsa_indexer_topk_mxfp4(dq8, dqs, dwt, rows, pages, cache, logits, 2048, idx, ws)
     torch.cuda.synchronize()
     fused = host(idx).copy()
     dsa.dsa_indexer_logits_mxfp4(dq8, dqs, dwt, rows, pages, cache, logits)
@@ -153,7 +155,7 @@ def oracle_mx_cache_of(w, b, overrides=None):
     return cache, pt
 
 
-def _full_size_mx(w, sample_reqs, overrides=None):
+def _full_size_mx(w, sample_reqs, overrides=None, path=None):
     """The benchmark's launch configuration on the whole batch (every request stored, scored and
     selected on the GPU), checked against the oracle on the sampled requests' rows: logits
     element-wise, the fused and the separate selections against the oracle's sets."""
@@ -162,7 +164,8 @@ def _full_size_mx(w, sample_reqs, overrides=None):
     L = DeviceLayer(w, latent_layers=[], k_overrides=overrides)
     cache = L.build_mxfp4_index(0)
     dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
-    dsa.dsa_indexer_topk_mxfp4(L.q8, L.qs, L.w_head, L.rows, L.pages, cache, L.logits, 2048, L.idx, L.ws_topk)
+    with topk_path(path):
+        dsa.dsa_indexer_topk_mxfp4(L.q8, L.qs, L.w_head, L.rows, L.pages, cache, L.logits, 2048, L.idx, L.ws_topk)
     torch.cuda.synchronize()
     fused = host(L.idx).copy()
     dsa.dsa_indexer_logits_mxfp4(L.q8, L.qs, L.w_head, L.rows, L.pages, cache, L.logits)
@@ -202,8 +205,9 @@ def test_mxfp4_full_c2_verify_128k_sampled_requests():
     assert n_same >= 0.9 * n, f"only {n_same}/{n} rows have the oracle's exact set"
 
 
-def test_mxfp4_full_c3_long_1m():
-    _announce("mxfp4 full size c3: 1 request at 1M context (needle keys stored as MXFP4)")
+@pytest.mark.parametrize("path", ["direct", "filtered"])
+def test_mxfp4_full_c3_long_1m(path):
+    _announce(f"mxfp4 full size c3: 1 request at 1M context (needle keys stored as MXFP4), {path} top-k")
     from parity import needle_overrides
     w = gi.config(3, "full")
-    _full_size_mx(w, [0], needle_overrides(w))          # the set differs only at near-ties
+    _full_size_mx(w, [0], needle_overrides(w), path)    # the set differs only at near-ties

@@ -17,7 +17,7 @@ import torch
 import dsa_inputs as gi
 import oracle as orc
 from parity import (SM, all_tokens, assert_attention_close, assert_logits_close, oracle_index_cache,
-                    oracle_latent_cache, queries, raw_k, topk_sets_match)
+                    oracle_latent_cache, queries, raw_k, topk_path, topk_sets_match)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,8 +64,9 @@ PAD_CASES = [
 
 @pytest.mark.parametrize("name,ctx,g,pad", PAD_CASES, ids=[c[0] for c in PAD_CASES])
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-def test_logits_and_topk_padded_rows(name, ctx, g, pad, fmt):
-    _announce(f"padded rows: logits + top-k, {name}, {fmt}")
+@pytest.mark.parametrize("path", ["direct", "filtered"])
+def test_logits_and_topk_padded_rows(name, ctx, g, pad, fmt, path):
+    _announce(f"padded rows: logits + top-k, {name}, {fmt}, {path} fused path")
     w = gi.make_decode(f"pad_{name}", gi.SEED_BASE + 80, ctx, rows_per_req=g)
     L = DeviceLayer(w)
     pos = _padded(w, pad)
@@ -107,7 +108,8 @@ def test_logits_and_topk_padded_rows(name, ctx, g, pad, fmt):
     topk_sets_match(sep, ridx, ref, kth)                  # differences only at near-ties
     idx.fill_(-7)
     logits.fill_(float("nan"))
-    topk_fn(L.q8, L.qs, L.w_head, rows, L.pages, cache_dev, logits, 2048, idx, ws)
+    with topk_path(path):
+        topk_fn(L.q8, L.qs, L.w_head, rows, L.pages, cache_dev, logits, 2048, idx, ws)
     torch.cuda.synchronize()
     fused = host(idx)
     for r in pad:

@@ -11,7 +11,7 @@ import torch
 import dsa_inputs as gi
 import oracle as orc
 from parity import (LN_EPS, SM, THETA, assert_attention_close, assert_logits_close, bf16_to_f64, needle_overrides,
-                    oracle_index_cache, oracle_latent_cache, queries, topk_sets_match)
+                    oracle_index_cache, oracle_latent_cache, queries, topk_path, topk_sets_match)
 
 pytestmark = pytest.mark.gpu
 
@@ -291,13 +291,15 @@ def test_bad_page_id_is_flagged_not_dereferenced():
     dsa.dsa_check_device_errors()                          # the flag was cleared
 
 
+@pytest.mark.parametrize("path", ["direct", "filtered"])
 @pytest.mark.parametrize("cid", [1, 2, 3])
-def test_fused_indexer_topk_equals_separate_calls(cid):
-    _announce(f"fused indexer+topk c{cid}")
+def test_fused_indexer_topk_equals_separate_calls(cid, path):
+    _announce(f"fused indexer+topk c{cid}, {path} path")
     w = gi.config(cid, "small")
     L = DeviceLayer(w)
     dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
-    L.indexer_topk(0)
+    with topk_path(path):
+        L.indexer_topk(0)
     torch.cuda.synchronize()
     fused_idx = host(L.idx).copy()
     dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
