@@ -243,7 +243,9 @@ size_t dsa_topk_workspace_size(int32_t R, int64_t stride, int32_t k);
  * largest logits among s <= pos[r], written in ascending position order.  If
  * pos[r] + 1 <= k the row is [0, 1, ..., pos[r], -1, ...] without reading logits
  * ([IDXC] §优化二:短上下文直接跳过打分); a padded row is all -1.  Among exactly
- * equal scores at the threshold the lower positions are kept.  k in [1, 2048]. */
+ * equal scores at the threshold the lower positions are kept.  k in [1, 2048].  Rows of at
+ * most 32,768 visible scores are selected by one work-group each, which uses no workspace;
+ * ws is still checked. */
 dsa_status dsa_topk(const float* logits, int64_t stride, const dsa_rows* rows, int32_t k,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
@@ -253,7 +255,8 @@ dsa_status dsa_topk(const float* logits, int64_t stride, const dsa_rows* rows, i
  * top-k runs over those.  A row whose pairs come out fewer than k or more than the list
  * holds is scored in full and takes the radix top-k instead, so the selection never
  * depends on the sample.  `logits` is scratch: on return it holds the sampled pages'
- * scores and the full scores of rows that fell back; other entries are unspecified.  A
+ * scores and the full scores of rows that fell back (on the direct path below, the scores of
+ * every scored row group); other entries are unspecified.  A
  * row group (rows->group consecutive rows) whose rows all have pos + 1 <= k is not scored
  * ([IDXC] §优化二:短上下文直接跳过打分).  A call whose R x stride is at most the direct
  * limit (dsa_set_topk_direct_limit; 4,194,304 scores by default) writes every score and takes

@@ -251,9 +251,18 @@ static dsa_status indexer_topk_impl(const uint8_t* q8, const float* qs, const fl
   const int R = rows->n;
   if ((int64_t)R * stride <= g_topk_direct_limit.load(std::memory_order_relaxed)) {
     // few scores: writing them all and selecting with the radix passes costs less than the
-    // filtered path's extra launches and single-work-group steps.  Every row is flagged, so the
-    // exact path's kernels (full scores with the row ranges, histogram, select, final) take it;
-    // row groups whose rows are all short are still not scored.
+    // filtered path's extra launches and single-work-group steps.  Rows of at most 32,768
+    // scores are selected by one work-group each, straight from the plain scores.
+    if (dsa::topk_single_group_rows(rows->max_pos)) {
+      dsa::LogitsMode m;
+      m.skip_upto = k;                 // row groups whose rows are all short need no score
+      hipError_t e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, m, fmt, s);
+      if (e == hipSuccess) e = dsa::launch_row_topk(logits, stride, rv, k, idx, s);
+      return hip_status(e, name);
+    }
+    // Longer rows: every row is flagged, so the exact path's kernels (full scores with the row
+    // ranges, histogram, select, final) take it; row groups whose rows are all short are still
+    // not scored.
     hipError_t e = dsa::launch_topk_init(R, k, ws, s, true, true);
     if (e == hipSuccess)
       e = dsa::launch_indexer_logits(q8, qs, w, rv, pv, cache, logits, stride, dsa::topk_fallback_mode(ws, R, k, k), fmt,

@@ -77,6 +77,11 @@ hipError_t launch_indexer_logits(const uint8_t* q8, const float* qs, const float
 size_t topk_workspace_bytes(int32_t R, int64_t stride, int32_t k);
 hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
                        void* ws, hipStream_t s);
+// Rows of at most 32,768 visible scores: one work-group per row selects the whole row (no
+// workspace, one launch); launch_topk takes it by itself for such rows.
+bool topk_single_group_rows(int64_t max_pos);
+hipError_t launch_row_topk(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
+                           hipStream_t s);
 // Pieces of the top-k used by the fused indexer + top-k entry (threshold-filtered):
 //  init; sample scores (logits kernel, sample mode, with the row ranges); per-row threshold;
 //  filtered scores (logits kernel, filter mode); exact top-k over each row's candidates,

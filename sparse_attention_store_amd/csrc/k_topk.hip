@@ -704,9 +704,154 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ p
   write_ascending(sel, min(nsel, k), n, k, out, bitmap, scan);
 }
 
+// Rows of at most 32 x NT scores: one work-group of NT threads per row does the whole
+// selection, with the row's keys in registers (thread t holds positions [32t, 32t + 32)):
+//  * the row's key range by a block reduction;
+//  * radix rounds of 12 bits over (key - kmin) from the range's width down, until the bin
+//    holding the k-th largest holds at most NT keys; those are gathered in LDS and each is
+//    ranked against the others, which gives the exact key of the k-th largest without the
+//    remaining rounds;
+//  * the keys above it and the lowest positions among the exact ties at it, written in
+//    ascending order from one block prefix count of each thread's (above, tie) counts.
+// No workspace and no other launch.
+constexpr int kRowPer = 32;
+constexpr int kRowMax = kRowPer * kFinalThreads;        // 32,768 scores
+constexpr int kRowSmallThreads = 256;                   // rows of at most 8,192 scores
+template <int NT>
+__global__ void __launch_bounds__(NT) k_row_topk(const float* __restrict__ logits, int64_t stride,
+                                                 const int32_t* __restrict__ pos, int32_t k,
+                                                 int32_t* __restrict__ idx) {
+  static_assert(kBins % NT == 0 && kRowPer * NT <= 65535, "bins per thread; packed 16-bit counts");
+  __shared__ int h[kBins];
+  __shared__ int scan[NT / 64];
+  __shared__ int res[2];
+  __shared__ uint32_t red[2 * (NT / 64)];
+  __shared__ uint32_t cand[NT];
+  __shared__ int ncand;
+  __shared__ uint32_t thr_found;
+  __shared__ int need_found;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n = row_len(pos, r, stride);
+  int32_t* out = idx + (int64_t)r * k;
+  if (n <= k) {                        // short context or padded row: every visible position
+    for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
+    return;
+  }
+  const float* row = logits + (int64_t)r * stride;
+  const int base = kRowPer * tid;
+  const int n4 = (int)((n + 3) & ~int64_t{3});           // <= stride (a multiple of 256)
+  uint32_t key[kRowPer];
+#pragma unroll
+  for (int u = 0; u < kRowPer / 4; u++) {
+    const int i = base + 4 * u;
+    const float4 v = i < n4 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    key[4 * u] = ord_key(v.x);
+    key[4 * u + 1] = ord_key(v.y);
+    key[4 * u + 2] = ord_key(v.z);
+    key[4 * u + 3] = ord_key(v.w);
+  }
+  const int nv = (int)min((int64_t)kRowPer, max((int64_t)0, n - base));   // this thread's valid positions
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < kRowPer; j++)
+    if (j < nv) { mn = min(mn, key[j]); mx = max(mx, key[j]); }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  }
+  if (lane == 0) { red[2 * wave] = mn; red[2 * wave + 1] = mx; }
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int w2 = 0; w2 < NT / 64; w2++) { kmin = min(kmin, red[2 * w2]); kmax = max(kmax, red[2 * w2 + 1]); }
+  // radix rounds over d = key - kmin: the bits above `low` are known (prefix); `need` of the
+  // keys whose high bits are prefix still belong to the k largest
+  const uint32_t span = kmax - kmin;
+  int low = span == 0u ? 0 : 32 - __clz(span);
+  uint32_t prefix = 0;
+  int need = k;
+  bool ranked = false;
+  uint32_t thr = kmin;
+  while (low > 0) {
+    const int take = low > 12 ? 12 : low;
+    const int sh = low - take;
+    for (int i = tid; i < kBins; i += NT) h[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRowPer; j++) {
+      const uint32_t d = key[j] - kmin;
+      if (j < nv && (low >= 32 || (d >> low) == prefix)) atomicAdd(&h[(d >> sh) & ((1u << take) - 1)], 1);
+    }
+    __syncthreads();
+    const int dg = find_threshold<NT, kBins>(h, need, scan, res);
+    need -= res[1];
+    prefix = (prefix << take) | (uint32_t)dg;
+    low = sh;
+    const int in_bin = h[dg];
+    __syncthreads();
+    if (low > 0 && in_bin <= NT) {
+      // few keys left in the bin: rank each against the others
+#pragma unroll
+      for (int j = 0; j < kRowPer; j++)
+        if (j < nv && ((key[j] - kmin) >> low) == prefix) cand[atomicAdd(&ncand, 1)] = key[j];
+      __syncthreads();
+      if (tid < in_bin) {
+        const uint32_t x = cand[tid];
+        int gt = 0, eq = 0;
+        for (int i = 0; i < in_bin; i++) {
+          const uint32_t y = cand[i];
+          gt += y > x;
+          eq += y == x;
+        }
+        if (gt < need && need <= gt + eq) { thr_found = x; need_found = need - gt; }   // one value, maybe several writers
+      }
+      __syncthreads();
+      thr = thr_found;
+      need = need_found;
+      ranked = true;
+      break;
+    }
+  }
+  if (!ranked) thr = kmin + prefix;    // exact key of the k-th largest; `need` ties at it are kept
+  int above = 0, ties = 0;
+#pragma unroll
+  for (int j = 0; j < kRowPer; j++)
+    if (j < nv) { above += key[j] > thr; ties += key[j] == thr; }
+  // (above, ties) packed in one int: both totals are at most 32 x NT < 2^16
+  int all;
+  const int incl = block_prefix<NT>((above << 16) | ties, scan, &all);
+  const int above_before = (incl >> 16) - above, ties_before = (incl & 0xFFFF) - ties;
+  const int keep_ties = max(0, min(ties, need - ties_before));        // the lowest positions among the ties
+  int o = above_before + min(need, ties_before);
+  int kept_ties = 0;
+#pragma unroll
+  for (int j = 0; j < kRowPer; j++) {
+    if (j >= nv) continue;
+    const bool tie = key[j] == thr;
+    const bool keep = key[j] > thr || (tie && kept_ties < keep_ties);
+    kept_ties += tie;
+    if (keep) out[o++] = base + j;
+  }
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int32_t R, int64_t /*stride*/, int32_t k) { return ws_bytes(R, k); }
+
+bool topk_single_group_rows(int64_t max_pos) { return max_pos + 1 <= kRowMax; }
+
+hipError_t launch_row_topk(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
+                           hipStream_t s) {
+  if (rows.n <= 0) return hipSuccess;
+  if ((int64_t)rows.max_pos + 1 <= (int64_t)kRowPer * kRowSmallThreads)
+    hipLaunchKernelGGL(k_row_topk<kRowSmallThreads>, dim3(rows.n), dim3(kRowSmallThreads), 0, s, logits, stride,
+                       rows.pos, k, idx);
+  else
+    hipLaunchKernelGGL(k_row_topk<kFinalThreads>, dim3(rows.n), dim3(kFinalThreads), 0, s, logits, stride, rows.pos,
+                       k, idx);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk_init(int32_t R, int32_t k, void* ws, hipStream_t s, bool flag_all, bool zero_hist) {
   Ws w = carve(ws, R, k);
@@ -738,6 +883,7 @@ hipError_t launch_topk(const float* logits, int64_t stride, RowsView rows, int32
                        hipStream_t s) {
   const int R = rows.n;
   if (R <= 0) return hipSuccess;
+  if (topk_single_group_rows(rows.max_pos)) return launch_row_topk(logits, stride, rows, k, idx, s);
   hipError_t e = launch_topk_init(R, k, ws, s, false, true);
   if (e != hipSuccess) return e;
   Ws w = carve(ws, R, k);

@@ -383,3 +383,25 @@ def test_topk_row_longer_than_the_bitmap(k, path):
     assert np.array_equal(fused, sep)
     topk_sets_match(fused, ridx, lg, kth)                 # differences only at near-ties
     dsa.dsa_check_device_errors()
+
+
+@pytest.mark.parametrize("n", [5000, 30000])
+def test_direct_topk_all_equal_scores(n):
+    """Every score of the row equal (an empty key range): the one-work-group row top-k of the
+    direct path (256 threads up to 8,192 positions, 1024 above) keeps the lowest positions, as
+    does the separate top-k over the plain scores."""
+    _announce(f"direct-path top-k, {n} equal scores")
+    w = gi.make_decode(f"eq_direct_{n}", gi.SEED_BASE + 75, [n])
+    key = _equal_score_key()
+    L = DeviceLayer(w, latent_layers=[], k_overrides={p: key for p in range(n)})
+    dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)
+    with topk_path("direct"):
+        L.indexer_topk(0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(L.idx)[0], np.arange(2048))
+    dsa.dsa_indexer_logits(L.q8, L.qs, L.w_head, L.rows, L.pages, L.index_cache[0], L.logits)
+    L.idx.fill_(-7)
+    dsa.dsa_topk(L.logits, L.rows, 2048, L.idx, L.ws_topk)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(L.idx)[0], np.arange(2048))
+    dsa.dsa_check_device_errors()
