@@ -6,19 +6,19 @@
 // by all heads and also serves as the value: "GLM-5.3 推理全链路(一)", section on the
 // decode MQA form and absorption).
 //
-// Work-group = (row, split of the row's selected keys); 8 waves; keys in tiles of 32.
+// Work-group = (row, split of the row's selected keys); 8 waves; keys in tiles of kTile (64).
 //  * Record addresses of the split are resolved once into LDS (idx -> page table).
-//  * Each tile's 32 records (656 B each: fp8 latent, 4 scales, bf16 rope) are copied from
-//    HBM straight into LDS with gfx950's global_load_lds_dwordx4, two tiles ahead of the
-//    compute (explicit vmcnt waits + raw s_barrier: a full __syncthreads() would drain the
-//    in-flight copies every tile).  The copies scatter the records' 16-B chunks so that every
+//  * Each tile's records (656 B each: fp8 latent, 4 scales, bf16 rope) are copied from HBM
+//    straight into LDS with gfx950's global_load_lds_dwordx4, kDepth tiles ahead of the compute
+//    (one for 64-key tiles; explicit vmcnt waits + raw s_barrier: a full __syncthreads() would
+//    drain the in-flight copies every tile).  The copies scatter the records' 16-B chunks so that every
 //    wave-wide LDS access of the tile reads one contiguous block (see the tile layout below).
-//  * Wave specialisation, one barrier per tile: waves 0-3 score tile t (S^T[32 keys x 16
+//  * Wave specialisation, one barrier per tile: waves 0-3 score tile t (S^T[64 keys x 16
 //    heads]; the 512 latent dims on the block-scaled FP8 MFMA v_mfma_scale_f32_16x16x128_
 //    f8f6f4 fed with the cached codes and their ue8m0 scales as E8M0 operands, against a
 //    two-term FP8 expansion of q that keeps bf16's precision; the 64 rope dims on the bf16
 //    MFMA), run the online softmax (exp2
-//    domain, lazy rescaling of the running max) and write P (fp32) to LDS; at the same time
+//    domain, lazy rescaling of the running max) and write P (bf16, unscaled) to LDS; at the same time
 //    waves 4-7 accumulate O += P V for tile t-1 (each owns 128 value dims = one value block
 //    of all 64 heads): they scale P by each key's scale of their block, pack it to bf16 and
 //    read V transposed straight from the fp8 key tile with ds_read_b64_tr_b8.  Each SIMD so
