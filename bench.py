@@ -70,7 +70,8 @@ def kernel_sources(name):
     for key, src in (("k_logits_decode", _IDX_SRC), ("k_sparse_mla", _MLA_SRC), ("k_mla_", _MLA_SRC),
                      ("k_fused_norm", _STORE_SRC), ("k_index_k_store", _STORE_SRC), ("k_latent_store", _STORE_SRC),
                      ("k_quant_fp8", _STORE_SRC), ("k_filt", _TOPK_SRC), ("k_init", _TOPK_SRC), ("k_hist", _TOPK_SRC),
-                     ("k_select", _TOPK_SRC), ("k_final", _TOPK_SRC), ("k_range", _TOPK_SRC)):
+                     ("k_select", _TOPK_SRC), ("k_final", _TOPK_SRC), ("k_range", _TOPK_SRC),
+                     ("k_row_topk", _TOPK_SRC)):
         if key in name:
             return src
     return None
