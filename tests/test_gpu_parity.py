@@ -120,6 +120,25 @@ def test_topk_stage_exact():
     assert np.array_equal(_topk_gpu(lg, pos, 8), ref8)
 
 
+@pytest.mark.parametrize("n", [2049, 8192, 8193, 32768, 32769])
+def test_topk_stage_exact_at_kernel_limits(n):
+    """The patterns above at row lengths on both sides of the one-work-group top-k's limits
+    (8,192 scores for its 256-thread form, 32,768 for 1024 threads; a call whose longest row is
+    longer takes the multi-kernel radix), for k = 2048, 1000 and 8."""
+    _announce(f"topk stage at n={n}")
+    rng = np.random.default_rng(n)
+    stride = orc.logits_stride(n - 1)
+    lg = np.full((8, stride), -np.inf, np.float32)
+    lg[:, :n] = np.abs(rng.standard_normal((8, n))).astype(np.float32) * 10
+    lg[1, :n] = np.round(lg[1, :n] * 4) / 4                # heavy exact ties around the threshold
+    lg[2, :n] = 1.0                                       # all equal: lowest positions win
+    lg[3, :n] = rng.integers(0, 3, n).astype(np.float32)  # far more ties than the work-group has threads
+    pos = np.array([n - 1, n - 1, n - 1, n - 1, 2047, 2048, -1, n // 2], np.int32)
+    for k in (2048, 1000, 8):
+        ref, _ = orc.topk(lg, pos, k)
+        assert np.array_equal(_topk_gpu(lg, pos, k), ref), f"k={k}"
+
+
 @pytest.mark.parametrize("cid", [0, 2])
 def test_mla_stage(cid):
     _announce(f"mla stage c{cid}")
