@@ -396,12 +396,12 @@ hipError_t launch_rg(const uint8_t* q8, const float* qs, const float* w, RowsVie
   // enough work-groups to cover the chip (each page is one wave-iteration); the sampling pass
   // reads few pages, so it stops at one round of resident work-groups to amortise the q staging,
   // and so does the fused call's fallback, whose work-groups mostly find no flagged row and exit.
-  // One request's rows (a single long context) take fewer, longer work-groups: 1M keys scored in
-  // 28.7 us by 2,048 work-groups of 8 pages, in 23.5 us by 512 of 32.  Several requests keep more
-  // chunks, which also spreads requests of uneven length (a 32-request batch of 8K-32K: 18.8 us
-  // with the 2,048 target, 21.7 with 512).
+  // A few long requests take fewer, longer work-groups, 512 per request (with >= 2 GB of cache
+  // copies rotated so that HBM serves every page: one 1M-context row 34.0 -> 29.4 us, two
+  // 512K-context rows 34.2 -> 30.6 us).  Four or more requests keep more chunks, which also
+  // spreads requests of uneven length (a 32-request batch of 8K-32K is slower with fewer).
   int64_t want = KIND == kLogitsSample || KIND == kLogitsFallback ? 1024 : 2048;
-  if (n_groups == 1) want = 512;
+  if (n_groups < 4) want = min(want, 512 * n_groups);
   // 32 pages per work-group; the filter pass, which writes no logits, takes up to 128 as its
   // stage allows (fewer work-groups amortise the q staging: 64 took 3% off the c2 filter pass
   // and 128 1.6% off the 1M prefill indexer, while the logits-writing pass was 1% slower with 64)
