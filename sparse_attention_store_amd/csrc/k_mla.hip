@@ -763,10 +763,10 @@ k_sparse_mla_stream(const uint16_t* __restrict__ q, const int32_t* __restrict__ 
 
 // Merges the splits of one row: block = (row, head), 128 threads x 4 dims.  Every split's (m, l)
 // and partial O are loaded before any is used (a split count of at most kMaxSplits, predicated),
-// so the loads are in flight together instead of one memory round trip per split.  At most 8
-// splits: one row of 2048 keys took 26.6 us in 16 splits of 128 keys, 22.6 in 8 of 256 and 29.5
-// in 4 of 512 (split kernel + combine; the partials to merge grow with the split count).
-constexpr int kMaxSplits = 8;
+// so the loads are in flight together instead of one memory round trip per split.  At most 16
+// splits: one row of 2048 keys took 20.3 us in 16 splits of 128 keys and 23.4 in 8 of 256 (split
+// kernel + combine), and 29.5 in 4 of 512; rows of 32 or more never reach 8 splits.
+constexpr int kMaxSplits = 16;
 __global__ void __launch_bounds__(128) k_mla_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                                                      int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int r = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
