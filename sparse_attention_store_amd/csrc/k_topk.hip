@@ -489,12 +489,46 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
   write_ascending(sel, min(nsel, k), n, k, out, bitmap, scan);
 }
 
+// Rank finish of a radix select: the bin that holds the need-th largest has in_bin <= kRankMax
+// keys left (those whose (key - base) >> low equals prefix).  They are gathered into h and each
+// is counted against the others: the key x with count(> x) < need <= count(>= x) is the
+// need-th largest, and need - count(> x) of its exact ties belong to the selection.  This
+// replaces the remaining radix rounds (a histogram clear, fill and scan each).  Returns x - base
+// and sets need_eq; all NT threads call it; res and scan are scratch (res[0] counts the gather).
+constexpr int kRankMax = 256;
+template <int NT, int kPer>
+__device__ inline uint32_t rank_finish(const uint32_t (&v)[kPer], int nv, int low, uint32_t prefix, int in_bin,
+                                       int need, int* h, int* scan, int* res, int& need_eq) {
+  const int tid = threadIdx.x;
+  if (tid == 0) res[0] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; j++)
+    if (j < nv && (v[j] >> low) == prefix) h[atomicAdd(&res[0], 1)] = (int)v[j];
+  __syncthreads();
+  if (tid < in_bin) {
+    const uint32_t x = (uint32_t)h[tid];
+    int gt = 0, eq = 0;
+    for (int i = 0; i < in_bin; i++) {
+      const uint32_t y = (uint32_t)h[i];
+      gt += y > x;
+      eq += y == x;
+    }
+    if (gt < need && need <= gt + eq) { scan[0] = (int)x; scan[1] = need - gt; }   // one value, maybe several writers
+  }
+  __syncthreads();
+  const uint32_t x = (uint32_t)scan[0];
+  need_eq = scan[1];
+  __syncthreads();                     // h, scan and res are free again
+  return x;
+}
+
 // ----------------------------------------------------------------------------- fused path
 // Per row: the filter threshold from the sampled scores (pages 0, S, 2S, ... of the row,
 // positions <= pos).  With n_s sampled positions of the row's n, m = ceil(margin * k * n_s / n)
-// samples should pass; the threshold is the lower edge of the histogram bin holding the
-// m-th largest sample, so at least m samples, and about margin * k of the row's scores,
-// lie at or above it.  Short rows (n <= k) get a threshold nothing reaches; rows with too
+// samples should pass; the threshold is the m-th largest sample itself when the histogram bin
+// holding it has few samples left to rank, else the lower edge of that bin after two rounds, so
+// at least m samples, and about margin * k of the row's scores, lie at or above it.  Short rows (n <= k) get a threshold nothing reaches; rows with too
 // few samples get 0 (every score passes).
 template <int kPer>
 __device__ inline void filt_thresh(const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ pos,
@@ -505,6 +539,22 @@ __device__ inline void filt_thresh(const float* __restrict__ logits, int64_t str
   __shared__ int scan[kFinalThreads / 64];
   __shared__ int res[2];
   const int r = blockIdx.x, tid = threadIdx.x;
+  const float* row = logits + (int64_t)r * stride;
+  // The held samples are requested first, together with the row's position and range, so the
+  // kernel waits one memory round trip for all of them (the pass is latency-bound).  Sample
+  // i = tid + j * kFinalThreads sits at position (i / 64) * step * 64 + i % 64: one lane offset
+  // plus a per-j constant, read through a buffer descriptor of the whole logits row (reads past
+  // it return 0; samples past the row's own ns are not counted below).
+  uint32_t v[kPer];
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, (int)min(stride * 4, (int64_t)INT32_MAX), kBufferWord3);
+    const int o0 = ((tid >> 6) * (step * 64) + (tid & 63)) * 4;
+    constexpr int kJump = (kFinalThreads / 64) * step * 64 * 4;
+#pragma unroll
+    for (int j = 0; j < kPer; j++) v[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, o0 + j * kJump, 0, 0);
+  }
+  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
   const int64_t n = row_len(pos, r, stride);
   if (n <= k) {
     if (tid == 0) ws.thr[r] = 0xFFFFFFFFu;
@@ -518,29 +568,17 @@ __device__ inline void filt_thresh(const float* __restrict__ logits, int64_t str
     if (tid == 0) ws.thr[r] = 0u;
     return;
   }
-  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
-  const float* row = logits + (int64_t)r * stride;
-  // rows with few enough samples keep theirs in registers for both rounds, all requested
-  // before any is used (the pass is latency-bound, not bandwidth-bound)
+  // rows with few enough samples keep theirs in registers for both rounds
   const bool held = ns <= kThrSamples;
-  uint32_t v[kPer];
   if (held) {
-    // sample i = tid + j * kFinalThreads sits at position (i / 64) * step * 64 + i % 64: one
-    // lane offset plus a per-j constant, read through a buffer descriptor of the row's n scores
-    // (reads past it return 0 and are not counted below)
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, (int)(n * 4), kBufferWord3);
-    const int o0 = ((tid >> 6) * (step * 64) + (tid & 63)) * 4;
-    constexpr int kJump = (kFinalThreads / 64) * step * 64 * 4;
-#pragma unroll
-    for (int j = 0; j < kPer; j++) v[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, o0 + j * kJump, 0, 0);
 #pragma unroll
     for (int j = 0; j < kPer; j++) v[j] = min(max(ord_key(__uint_as_float(v[j])), kmin), kmax) - kmin;
   }
   // this thread's samples are v[0 .. jn): sample tid + j * kFinalThreads exists for j < jn
   const int jn = held ? (int)min((int64_t)kPer, (ns - tid + kFinalThreads - 1) / kFinalThreads) : 0;
-  // two 12-bit rounds over (key - kmin): keys are close to logarithmic in the score, so one
-  // round's bin near the top of the range is far too wide a step for the threshold
+  // up to two 12-bit rounds over (key - kmin) (keys are close to logarithmic in the score, so
+  // one round's bin near the top of the range is far too wide a step for the threshold), or one
+  // round and a rank finish
   const int shift = range_shift(kmin, kmax);
   uint32_t prefix = 0;                 // high bits of (threshold - kmin) found so far
   int low = shift + 12, need = (int)m;
@@ -579,7 +617,15 @@ __device__ inline void filt_thresh(const float* __restrict__ logits, int64_t str
     need -= res[1];
     prefix = (prefix << take) | (uint32_t)d;
     low = sh;
+    const int in_bin = h[d];
     __syncthreads();
+    if (held && low > 0 && in_bin <= kRankMax) {
+      // the m-th largest sample itself, by ranking the few samples left in its bin
+      int unused;
+      const uint32_t x = rank_finish<kFinalThreads, kPer>(v, jn, low, prefix, in_bin, need, h, scan, res, unused);
+      if (tid == 0) ws.thr[r] = kmin + x;
+      return;
+    }
   }
   if (tid == 0) ws.thr[r] = kmin + (prefix << low);   // lower edge of the final bin
 }
@@ -594,14 +640,24 @@ __global__ void __launch_bounds__(kFinalThreads) k_filt_thresh_long(const float*
 }
 
 // The need-th largest (1 <= need <= cnt) of keys[0..cnt) in LDS, all in [base, base + 2^width),
-// in radix rounds of at most 12 bits over (key - base) from bit `width` down.  need_eq receives
-// how many keys equal to it belong to the need largest.  All kFinalThreads threads call it;
-// h holds kFinalBins ints.
+// in radix rounds of at most 12 bits over (key - base) from bit `width` down, and a rank finish
+// once the threshold bin holds at most kRankMax keys.  need_eq receives how many keys equal to
+// it belong to the need largest.  All kFinalThreads threads call it; cnt <= kCap; h holds
+// kFinalBins ints.
 constexpr int kFinalBits = 12;
 constexpr int kFinalBins = 1 << kFinalBits;
 __device__ inline uint32_t kth_largest(const uint32_t* keys, int cnt, int need, uint32_t base, int width, int* h,
                                        int* scan, int* res, int& need_eq) {
+  constexpr int kPer = kCap / kFinalThreads;
   const int tid = threadIdx.x;
+  // this thread's keys (tid + j * kFinalThreads), relative to base, for the rank finish
+  uint32_t kv[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int i = tid + j * kFinalThreads;
+    kv[j] = i < cnt ? keys[i] - base : 0u;
+  }
+  const int nv = (int)min((int64_t)kPer, max((int64_t)0, ((int64_t)cnt - tid + kFinalThreads - 1) / kFinalThreads));
   uint32_t prefix = 0;
   int low = width;
   while (low > 0) {
@@ -609,16 +665,18 @@ __device__ inline uint32_t kth_largest(const uint32_t* keys, int cnt, int need, 
     const int sh = low - take;
     for (int i = tid; i < kFinalBins; i += kFinalThreads) h[i] = 0;
     __syncthreads();
-    for (int i = tid; i < cnt; i += kFinalThreads) {
-      const uint32_t v = keys[i] - base;
-      if (low >= 32 || (v >> low) == prefix) atomicAdd(&h[(v >> sh) & ((1u << take) - 1)], 1);
-    }
+#pragma unroll
+    for (int j = 0; j < kPer; j++)
+      if (j < nv && (low >= 32 || (kv[j] >> low) == prefix)) atomicAdd(&h[(kv[j] >> sh) & ((1u << take) - 1)], 1);
     __syncthreads();
     const int d = find_threshold<kFinalThreads, kFinalBins>(h, need, scan, res);
     need -= res[1];
     prefix = (prefix << take) | (uint32_t)d;
     low = sh;
+    const int in_bin = h[d];
     __syncthreads();
+    if (low > 0 && in_bin <= kRankMax)
+      return base + rank_finish<kFinalThreads, kPer>(kv, nv, low, prefix, in_bin, need, h, scan, res, need_eq);
   }
   need_eq = need;
   return base + prefix;
@@ -647,13 +705,24 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ p
   int* spos = (int*)(cand + kCap);
   uint32_t* bitmap = cand;
   const int r = blockIdx.x, tid = threadIdx.x;
+  // every candidate slot of the row is read at once, before the count arrives (slots past the
+  // count hold stale words that are never used), so the candidates cost one memory round trip
+  constexpr int kPer = kCap / kFinalThreads;
+  uint32_t key[kPer];
+  int p[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    key[j] = ws.ckey[(int64_t)r * kCap + tid + j * kFinalThreads];
+    p[j] = ws.cpos[(int64_t)r * kCap + tid + j * kFinalThreads];
+  }
+  const int c = ws.fcnt[r];
+  const uint32_t base = ws.thr[r];
   const int64_t n = row_len(pos, r, stride);
   int32_t* out = idx + (int64_t)r * k;
   if (n <= k) {                       // short context or padded row: every visible position
     for (int j = tid; j < k; j += kFinalThreads) out[j] = j < n ? j : -1;
     return;
   }
-  const int c = ws.fcnt[r];
   if (c < k || c > kCap) {            // the filter kept too few (or too many): exact fallback,
     for (int i = tid; i < kBins; i += kFinalThreads) ws.hist[(int64_t)r * kBins + i] = 0;   // from a clear histogram
     if (tid == 0) ws.flag[r] = 1;
@@ -663,15 +732,6 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ p
   __syncthreads();
   uint32_t mx = 0u;
   {
-    constexpr int kPer = kCap / kFinalThreads;   // every load in flight before the first use
-    uint32_t key[kPer];
-    int p[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; j++) {
-      const int i = tid + j * kFinalThreads;
-      key[j] = i < c ? ws.ckey[(int64_t)r * kCap + i] : 0u;
-      p[j] = i < c ? ws.cpos[(int64_t)r * kCap + i] : 0;
-    }
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
       const int i = tid + j * kFinalThreads;
@@ -682,7 +742,6 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ p
   if ((tid & 63) == 0) atomicMax(&cmax, mx);     // one LDS atomic per wave, not per thread
   __syncthreads();
   // every candidate lies in [filter threshold, cmax]: the rounds start at that span's width
-  const uint32_t base = ws.thr[r];
   const uint32_t span = cmax - base;
   const int width = span == 0u ? 0 : 32 - __clz(span);
   int need = 0;
