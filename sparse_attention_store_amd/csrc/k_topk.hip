@@ -17,9 +17,9 @@
 //               d > T are selected and keys with d == T become candidates.  Appends are
 //               gathered per work-group in LDS and reserved with one global atomic per list.
 //  4. k_final:  one work-group per row resolves the low `shift` bits over the candidates in
-//               LDS (10-bit rounds), keeps the lowest positions among exact ties at the
-//               threshold, and writes the k positions in ascending order via an LDS bitmap of
-//               the row (or a bitonic sort for rows too long for the bitmap).  If more
+//               LDS (by ranking them against each other when few, else 10-bit rounds), keeps
+//               the lowest positions among exact ties at the threshold, and writes the k
+//               positions in ascending order (a counting sort on their high bits).  If more
 //               candidates than fit in LDS share the threshold bin (massive exact ties), the
 //               rounds and the tie walk run over the row in global memory instead.
 #include "dsa_device.hpp"
@@ -43,7 +43,6 @@ constexpr int kBufferWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit r
 // launches with longer rows
 constexpr int kThrPer = 8, kThrPerLong = 32;
 static_assert(kCap % kFinalThreads == 0, "whole loads per thread");
-constexpr int kBitmapMaxN = 1 << 18; // rows up to 256K positions use the LDS bitmap (32 KiB)
 // fused path: the filter keeps about kMarginNum / kMarginDen times k candidates per row
 constexpr int kMarginNum = 3, kMarginDen = 2;
 
@@ -149,13 +148,17 @@ __global__ void __launch_bounds__(256) k_range(const float* __restrict__ logits,
   }
 }
 
-constexpr int kPerThread = kChunk / 256 / 4;   // float4 loads per thread per chunk (8)
+// Passes 2 and 3 run 1024 threads per work-group, two float4 of the chunk each: with 256
+// threads (eight each) one wave per SIMD walked the chunk alone and its dependent VALU chain set
+// the pass time (a 1M-score row: select 26.6K cycles per work-group, 9K of them in the loop).
+constexpr int kPassThreads = 1024;
+constexpr int kPerThread = kChunk / kPassThreads / 4;   // float4 loads per thread per chunk (2)
 
 // Loads this thread's share of a chunk (all loads issued before any use).
 __device__ inline void load_chunk(const float* row, int64_t c0, int64_t c1, float4 (&v)[kPerThread]) {
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
-    const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
+    const int64_t i = c0 + 4 * (threadIdx.x + kPassThreads * u);
     v[u] = i < c1 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
@@ -163,7 +166,7 @@ __device__ inline void load_chunk(const float* row, int64_t c0, int64_t c1, floa
 // Passes 2 and 3 take chunks blockIdx.x, blockIdx.x + gridDim.x, ... of their row: one chunk
 // per work-group for the plain top-k, a few work-groups per row for the fused call's fallback,
 // whose grid is mostly rows that are not flagged and exit at once.
-__global__ void __launch_bounds__(256) k_hist(const float* __restrict__ logits, int64_t stride,
+__global__ void __launch_bounds__(kPassThreads) k_hist(const float* __restrict__ logits, int64_t stride,
                                               const int32_t* __restrict__ pos, int32_t k, Ws ws,
                                               const int* __restrict__ gate) {
   __shared__ int h[kBins];
@@ -178,11 +181,11 @@ __global__ void __launch_bounds__(256) k_hist(const float* __restrict__ logits, 
     const int64_t c1 = min(c0 + kChunk, n);
     float4 v[kPerThread];
     load_chunk(logits + (int64_t)r * stride, c0, c1, v);
-    for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
+    for (int i = threadIdx.x; i < kBins; i += kPassThreads) h[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kPerThread; u++) {
-      const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
+      const int64_t i = c0 + 4 * (threadIdx.x + kPassThreads * u);
       const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int j = 0; j < 4; j++)
@@ -193,7 +196,7 @@ __global__ void __launch_bounds__(256) k_hist(const float* __restrict__ logits, 
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kBins; i += 256)
+    for (int i = threadIdx.x; i < kBins; i += kPassThreads)
       if (h[i]) atomicAdd(&gh[i], h[i]);
     __syncthreads();                  // h is cleared again for the next chunk
   }
@@ -242,251 +245,6 @@ __device__ inline int find_threshold(const int* h, int k, int* scan, int* result
   }
   __syncthreads();
   return result[0];
-}
-
-constexpr int kSelCap = 1024;    // candidates gathered per work-group before spilling to global appends
-
-__global__ void __launch_bounds__(256) k_select(const float* __restrict__ logits, int64_t stride,
-                                                const int32_t* __restrict__ pos, int32_t k, Ws ws,
-                                                const int* __restrict__ gate) {
-  __shared__ int l_above[kTopkMax];
-  __shared__ uint32_t l_ckey[kSelCap];
-  __shared__ int l_cpos[kSelCap];
-  __shared__ int n_above, n_cand, base_above, base_cand;
-  __shared__ int h[kBins];
-  __shared__ int scan[256 / 64];
-  __shared__ int res[2];
-  const int r = blockIdx.y;
-  if (gate != nullptr && !gate[r]) return;
-  const int64_t n = row_len(pos, r, stride);
-  int64_t c0 = (int64_t)blockIdx.x * kChunk;
-  if (n <= k || c0 >= n) return;
-  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
-  const int shift = range_shift(kmin, kmax);
-  float4 v[kPerThread];
-  load_chunk(logits + (int64_t)r * stride, c0, min(c0 + kChunk, n), v);
-  // the threshold bin from the row's merged histogram (every work-group of the row finds the
-  // same one; the first chunk's logits load meanwhile)
-  for (int i = threadIdx.x; i < kBins; i += 256) h[i] = ws.hist[(int64_t)r * kBins + i];
-  __syncthreads();
-  const uint32_t T = (uint32_t)find_threshold<256, kBins>(h, k, scan, res);
-  uint32_t* ckey = ws.ckey + (int64_t)r * kCap;
-  int* cpos = ws.cpos + (int64_t)r * kCap;
-  for (;;) {
-    const int64_t c1 = min(c0 + kChunk, n);
-    if (threadIdx.x == 0) { n_above = 0; n_cand = 0; }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kPerThread; u++) {
-      const int64_t i = c0 + 4 * (threadIdx.x + 256 * u);
-      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        if (i + j >= c1) continue;
-        const uint32_t key = min(max(ord_key(e[j]), kmin), kmax);
-        const uint32_t d = (key - kmin) >> shift;
-        if (d > T) {
-          const int sl = atomicAdd(&n_above, 1);
-          if (sl < kTopkMax) l_above[sl] = (int)(i + j);
-        } else if (d == T) {
-          const int sl = atomicAdd(&n_cand, 1);
-          if (sl < kSelCap) {
-            l_ckey[sl] = key; l_cpos[sl] = (int)(i + j);
-          } else {                                  // rare: many ties in this chunk
-            const int gsl = atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], 1);
-            if (gsl < kCap) { ckey[gsl] = key; cpos[gsl] = (int)(i + j); }
-          }
-        }
-      }
-    }
-    __syncthreads();
-    // fewer than k keys of the whole row lie above T, so n_above < k here
-    const int nc_local = min(n_cand, kSelCap);
-    if (threadIdx.x == 0) {
-      base_above = n_above ? atomicAdd(&ws.cnt[(int64_t)r * 4], n_above) : 0;
-      base_cand = nc_local ? atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], nc_local) : 0;
-    }
-    __syncthreads();
-    int* above = ws.above + (int64_t)r * k;
-    for (int i = threadIdx.x; i < min(n_above, kTopkMax); i += 256)
-      if (base_above + i < k) above[base_above + i] = l_above[i];
-    for (int i = threadIdx.x; i < nc_local; i += 256)
-      if (base_cand + i < kCap) { ckey[base_cand + i] = l_ckey[i]; cpos[base_cand + i] = l_cpos[i]; }
-    c0 += (int64_t)gridDim.x * kChunk;
-    if (c0 >= n) break;
-    load_chunk(logits + (int64_t)r * stride, c0, min(c0 + kChunk, n), v);
-    __syncthreads();                    // the stage and its counters are reused for the next chunk
-  }
-}
-
-__device__ inline void push(int* sel, int* n, int v) {
-  const int s = atomicAdd(n, 1);
-  if (s < kTopkMax) sel[s] = v;
-}
-
-// Writes the ns <= k selected positions sel[] of a row of n positions to out[0..k) in
-// ascending order, -1 after them: an LDS bitmap of the row and a prefix count of set bits
-// (rows up to kBitmapMaxN), else a bitonic sort in registers and LDS.  All kFinalThreads
-// threads call it.
-__device__ inline void write_ascending(int* sel, int ns, int64_t n, int k, int32_t* out, uint32_t* bitmap,
-                                       int* scan) {
-  const int tid = threadIdx.x;
-  if (n <= kBitmapMaxN) {
-    const int nwords = (int)((n + 31) / 32);
-    for (int i = tid; i < nwords; i += kFinalThreads) bitmap[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < ns; i += kFinalThreads) atomicOr(&bitmap[sel[i] >> 5], 1u << (sel[i] & 31));
-    __syncthreads();
-    const int per = (nwords + kFinalThreads - 1) / kFinalThreads;      // words per thread
-    const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
-    int c = 0;
-    for (int wd = w0; wd < w1; wd++) c += __popc(bitmap[wd]);
-    int all;
-    int o = block_prefix<kFinalThreads>(c, scan, &all) - c;
-    for (int wd = w0; wd < w1; wd++) {
-      uint32_t m = bitmap[wd];
-      while (m) {
-        const int b = __ffs(m) - 1;
-        m &= m - 1;
-        if (o < k) out[o] = wd * 32 + b;
-        o++;
-      }
-    }
-    for (int j = ns + tid; j < k; j += kFinalThreads) out[j] = -1;
-  } else {
-    // a bitonic sort of the selection padded to m (a power of two <= 2 * kFinalThreads): thread
-    // t holds elements 2t and 2t + 1; the partner of a compare-exchange at stride st is thread
-    // t ^ (st / 2), in the same wave up to st = 64 (a lane shuffle) and through LDS above
-    static_assert(kTopkMax <= 2 * kFinalThreads, "two elements per thread");
-    int m = 1;
-    while (m < k) m <<= 1;
-    int e0 = 2 * tid < ns ? sel[2 * tid] : 0x7FFFFFFF;
-    int e1 = 2 * tid + 1 < ns ? sel[2 * tid + 1] : 0x7FFFFFFF;
-    __syncthreads();                  // sel is the exchange buffer from here on
-    for (int size = 2; size <= m; size <<= 1) {
-      const bool asc = ((2 * tid) & size) == 0;
-      for (int st = size >> 1; st > 1; st >>= 1) {
-        const int pl = st >> 1;
-        int p0, p1;
-        if (pl < 64) {
-          p0 = __shfl_xor(e0, pl, 64);
-          p1 = __shfl_xor(e1, pl, 64);
-        } else {
-          sel[2 * tid] = e0;
-          sel[2 * tid + 1] = e1;
-          __syncthreads();
-          p0 = sel[2 * (tid ^ pl)];
-          p1 = sel[2 * (tid ^ pl) + 1];
-          __syncthreads();
-        }
-        const bool keep_min = ((tid & pl) == 0) == asc;   // the lower index keeps the min when ascending
-        e0 = keep_min ? min(e0, p0) : max(e0, p0);
-        e1 = keep_min ? min(e1, p1) : max(e1, p1);
-      }
-      const int lo = min(e0, e1), hi = max(e0, e1);      // stride 1: the thread's own pair
-      e0 = asc ? lo : hi;
-      e1 = asc ? hi : lo;
-    }
-    if (2 * tid < k) out[2 * tid] = 2 * tid < ns ? e0 : -1;
-    if (2 * tid + 1 < k) out[2 * tid + 1] = 2 * tid + 1 < ns ? e1 : -1;
-  }
-}
-
-__global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict__ logits, int64_t stride,
-                                                         const int32_t* __restrict__ pos, int32_t k,
-                                                         int32_t* __restrict__ idx, Ws ws,
-                                                         const int* __restrict__ gate) {
-  __shared__ uint32_t skey[kCap];
-  __shared__ int spos[kCap];
-  __shared__ int sel[kTopkMax];
-  __shared__ uint32_t bitmap[kBitmapMaxN / 32];
-  __shared__ int h[1024];
-  __shared__ int scan[kFinalThreads / 64];
-  __shared__ int res[2];
-  __shared__ int nsel;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  if (gate != nullptr && !gate[r]) return;
-  const int64_t n = row_len(pos, r, stride);
-  int32_t* out = idx + (int64_t)r * k;
-  if (n <= k) {                       // short context or padded row: every visible position
-    for (int j = tid; j < k; j += kFinalThreads) out[j] = j < n ? j : -1;
-    return;
-  }
-  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
-  const int shift = range_shift(kmin, kmax);
-  const int* cnt = ws.cnt + (int64_t)r * 4;
-  const int na = min(cnt[0], k);
-  const int nc = cnt[1];
-  const int need = k - na;            // >= 1: the threshold bin holds the k-th key
-  const float* row = logits + (int64_t)r * stride;
-  const bool in_lds = nc <= kCap;
-  if (in_lds)
-    for (int i = tid; i < nc; i += kFinalThreads) { skey[i] = ws.ckey[(int64_t)r * kCap + i]; spos[i] = ws.cpos[(int64_t)r * kCap + i]; }
-  if (tid == 0) nsel = 0;
-  __syncthreads();
-  // threshold bin, recovered from any candidate (all share it)
-  const uint32_t T = ((in_lds ? skey[0] : ws.ckey[(int64_t)r * kCap]) - kmin) >> shift;
-
-  // resolve the low `shift` bits of (key - kmin) in rounds of at most 10 bits
-  uint32_t prefix = T;                // known high part of (key - kmin)
-  int low = shift;                    // bits still to resolve
-  int need_r = need;
-  while (low > 0) {
-    const int take = low > 10 ? 10 : low;
-    const int sh = low - take;
-    for (int i = tid; i < 1024; i += kFinalThreads) h[i] = 0;
-    __syncthreads();
-    if (in_lds) {
-      for (int i = tid; i < nc; i += kFinalThreads) {
-        const uint32_t v = skey[i] - kmin;
-        if ((v >> low) == prefix) atomicAdd(&h[(v >> sh) & ((1u << take) - 1)], 1);
-      }
-    } else {
-      for (int64_t i = tid; i < n; i += kFinalThreads) {
-        const uint32_t v = min(max(ord_key(row[i]), kmin), kmax) - kmin;
-        if ((v >> low) == prefix) atomicAdd(&h[(v >> sh) & ((1u << take) - 1)], 1);
-      }
-    }
-    __syncthreads();
-    const int d = find_threshold<kFinalThreads, 1024>(h, need_r, scan, res);
-    need_r -= res[1];
-    prefix = (prefix << take) | (uint32_t)d;
-    low = sh;
-    __syncthreads();
-  }
-  const uint32_t thr = prefix + kmin;   // exact key of the k-th largest
-  const int need_ties = need_r;         // elements equal to thr to keep (lowest positions)
-
-  for (int i = tid; i < na; i += kFinalThreads) sel[i] = ws.above[(int64_t)r * k + i];
-  if (tid == 0) nsel = na;
-  __syncthreads();
-  if (in_lds) {
-    for (int i = tid; i < nc; i += kFinalThreads) {
-      if (skey[i] > thr) {
-        push(sel, &nsel, spos[i]);
-      } else if (skey[i] == thr) {
-        int rank = 0;                     // position rank among the exact ties
-        for (int j = 0; j < nc; j++) rank += (skey[j] == thr && spos[j] < spos[i]);
-        if (rank < need_ties) push(sel, &nsel, spos[i]);
-      }
-    }
-  } else {
-    // more candidates than LDS holds: walk the row in position order
-    int nties_seen = 0;
-    for (int64_t b = 0; b < n; b += kFinalThreads) {
-      const int64_t i = b + tid;
-      const uint32_t key = i < n ? min(max(ord_key(row[i]), kmin), kmax) : 0u;
-      const bool inT = i < n && ((key - kmin) >> shift) == T;
-      if (inT && key > thr) push(sel, &nsel, (int)i);
-      const int tie = (inT && key == thr) ? 1 : 0;
-      int all;
-      const int incl = block_prefix<kFinalThreads>(tie, scan, &all);
-      if (tie && nties_seen + incl - 1 < need_ties) push(sel, &nsel, (int)i);
-      nties_seen += all;
-    }
-  }
-  __syncthreads();
-  write_ascending(sel, min(nsel, k), n, k, out, bitmap, scan);
 }
 
 // Rank finish of a radix select: the bin that holds the need-th largest has in_bin <= kRankMax
@@ -639,6 +397,250 @@ __global__ void __launch_bounds__(kFinalThreads) k_filt_thresh_long(const float*
   filt_thresh<kThrPerLong>(logits, stride, pos, k, ws);
 }
 
+constexpr int kSelCap = 1024;    // candidates gathered per work-group before spilling to global appends
+
+__global__ void __launch_bounds__(kPassThreads) k_select(const float* __restrict__ logits, int64_t stride,
+                                                const int32_t* __restrict__ pos, int32_t k, Ws ws,
+                                                const int* __restrict__ gate) {
+  __shared__ int l_above[kTopkMax];
+  __shared__ uint32_t l_ckey[kSelCap];
+  __shared__ int l_cpos[kSelCap];
+  __shared__ int n_above, n_cand, base_above, base_cand;
+  __shared__ int h[kBins];
+  __shared__ int scan[kPassThreads / 64];
+  __shared__ int res[2];
+  const int r = blockIdx.y;
+  if (gate != nullptr && !gate[r]) return;
+  const int64_t n = row_len(pos, r, stride);
+  int64_t c0 = (int64_t)blockIdx.x * kChunk;
+  if (n <= k || c0 >= n) return;
+  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
+  const int shift = range_shift(kmin, kmax);
+  float4 v[kPerThread];
+  load_chunk(logits + (int64_t)r * stride, c0, min(c0 + kChunk, n), v);
+  // the threshold bin from the row's merged histogram (every work-group of the row finds the
+  // same one; the first chunk's logits load meanwhile)
+  for (int i = threadIdx.x; i < kBins; i += kPassThreads) h[i] = ws.hist[(int64_t)r * kBins + i];
+  __syncthreads();
+  const uint32_t T = (uint32_t)find_threshold<kPassThreads, kBins>(h, k, scan, res);
+  uint32_t* ckey = ws.ckey + (int64_t)r * kCap;
+  int* cpos = ws.cpos + (int64_t)r * kCap;
+  for (;;) {
+    const int64_t c1 = min(c0 + kChunk, n);
+    if (threadIdx.x == 0) { n_above = 0; n_cand = 0; }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPerThread; u++) {
+      const int64_t i = c0 + 4 * (threadIdx.x + kPassThreads * u);
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (i + j >= c1) continue;
+        const uint32_t key = min(max(ord_key(e[j]), kmin), kmax);
+        const uint32_t d = (key - kmin) >> shift;
+        if (d > T) {
+          const int sl = atomicAdd(&n_above, 1);
+          if (sl < kTopkMax) l_above[sl] = (int)(i + j);
+        } else if (d == T) {
+          const int sl = atomicAdd(&n_cand, 1);
+          if (sl < kSelCap) {
+            l_ckey[sl] = key; l_cpos[sl] = (int)(i + j);
+          } else {                                  // rare: many ties in this chunk
+            const int gsl = atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], 1);
+            if (gsl < kCap) { ckey[gsl] = key; cpos[gsl] = (int)(i + j); }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // fewer than k keys of the whole row lie above T, so n_above < k here
+    const int nc_local = min(n_cand, kSelCap);
+    if (threadIdx.x == 0) {
+      base_above = n_above ? atomicAdd(&ws.cnt[(int64_t)r * 4], n_above) : 0;
+      base_cand = nc_local ? atomicAdd(&ws.cnt[(int64_t)r * 4 + 1], nc_local) : 0;
+    }
+    __syncthreads();
+    int* above = ws.above + (int64_t)r * k;
+    for (int i = threadIdx.x; i < min(n_above, kTopkMax); i += kPassThreads)
+      if (base_above + i < k) above[base_above + i] = l_above[i];
+    for (int i = threadIdx.x; i < nc_local; i += kPassThreads)
+      if (base_cand + i < kCap) { ckey[base_cand + i] = l_ckey[i]; cpos[base_cand + i] = l_cpos[i]; }
+    c0 += (int64_t)gridDim.x * kChunk;
+    if (c0 >= n) break;
+    load_chunk(logits + (int64_t)r * stride, c0, min(c0 + kChunk, n), v);
+    __syncthreads();                    // the stage and its counters are reused for the next chunk
+  }
+}
+
+__device__ inline void push(int* sel, int* n, int v) {
+  const int s = atomicAdd(n, 1);
+  if (s < kTopkMax) sel[s] = v;
+}
+
+// Writes the ns <= k selected positions sel[] (distinct, any order) of a row of n positions to
+// out[0..k) in ascending order, -1 after them, by a counting sort on the positions' high bits:
+// 2048 buckets of 2^s positions each (the smallest s with (n - 1) >> s < 2048), a block prefix
+// over the bucket counts, then each position's rank among the few others of its bucket.  The
+// sorted positions go back to sel and leave as one coalesced copy.  Unlike a bitmap of the row,
+// the cost does not grow with n (an LDS bitmap of a 1M-position row took 71K cycles: each thread
+// owned 32 consecutive words, so a wave's reads of them hit one bank), and it takes 5 barriers
+// where a bitonic network over 2048 elements took 20 plus 56 lane-shuffle steps.  A bucket
+// holds about one position; a row whose selection falls in one bucket costs ns compares per
+// position.  scratch holds 2 * kTopkMax ints.  All kFinalThreads threads call it.
+constexpr int kSortBuckets = kTopkMax;
+__device__ inline void write_ascending(int* sel, int ns, int64_t n, int k, int32_t* out, int* scratch, int* scan) {
+  static_assert(kTopkMax <= 2 * kFinalThreads && kSortBuckets == 2 * kFinalThreads, "two per thread");
+  const int tid = threadIdx.x;
+  int* start = scratch;                     // bucket counts, then start offsets
+  int* grouped = scratch + kSortBuckets;    // positions grouped by bucket
+  int s = 0;
+  while (((n - 1) >> s) >= kSortBuckets) s++;
+  start[2 * tid] = 0;
+  start[2 * tid + 1] = 0;
+  __syncthreads();
+  int p[2], b[2], slot[2];
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int i = tid + u * kFinalThreads;
+    p[u] = i < ns ? sel[i] : 0;
+    b[u] = p[u] >> s;
+    slot[u] = i < ns ? atomicAdd(&start[b[u]], 1) : 0;
+  }
+  __syncthreads();
+  const int c0 = start[2 * tid], c1 = start[2 * tid + 1];
+  int all;
+  const int before = block_prefix<kFinalThreads>(c0 + c1, scan, &all) - c0 - c1;
+  start[2 * tid] = before;
+  start[2 * tid + 1] = before + c0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; u++)
+    if (tid + u * kFinalThreads < ns) grouped[start[b[u]] + slot[u]] = p[u];
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    if (tid + u * kFinalThreads >= ns) continue;
+    const int b0 = start[b[u]], b1 = b[u] + 1 < kSortBuckets ? start[b[u] + 1] : ns;
+    int rank = 0;
+    for (int j = b0; j < b1; j++) rank += grouped[j] < p[u];
+    sel[b0 + rank] = p[u];
+  }
+  __syncthreads();
+  for (int j = tid; j < k; j += kFinalThreads) out[j] = j < ns ? sel[j] : -1;
+}
+
+__global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict__ logits, int64_t stride,
+                                                         const int32_t* __restrict__ pos, int32_t k,
+                                                         int32_t* __restrict__ idx, Ws ws,
+                                                         const int* __restrict__ gate) {
+  __shared__ uint32_t skey[kCap];    // candidate keys; the output sort's scratch once sel is complete
+  __shared__ int spos[kCap];
+  static_assert(kCap >= 2 * kTopkMax, "the sort scratch fits the candidate keys");
+  __shared__ int sel[kTopkMax];
+  __shared__ int h[1024];
+  __shared__ int scan[kFinalThreads / 64];
+  __shared__ int res[2];
+  __shared__ int nsel;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (gate != nullptr && !gate[r]) return;
+  const int64_t n = row_len(pos, r, stride);
+  int32_t* out = idx + (int64_t)r * k;
+  if (n <= k) {                       // short context or padded row: every visible position
+    for (int j = tid; j < k; j += kFinalThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  const uint32_t kmin = ws.range[2 * r], kmax = ws.range[2 * r + 1];
+  const int shift = range_shift(kmin, kmax);
+  const int* cnt = ws.cnt + (int64_t)r * 4;
+  const int na = min(cnt[0], k);
+  const int nc = cnt[1];
+  const int need = k - na;            // >= 1: the threshold bin holds the k-th key
+  const float* row = logits + (int64_t)r * stride;
+  const bool in_lds = nc <= kCap;
+  if (in_lds)
+    for (int i = tid; i < nc; i += kFinalThreads) { skey[i] = ws.ckey[(int64_t)r * kCap + i]; spos[i] = ws.cpos[(int64_t)r * kCap + i]; }
+  if (tid == 0) nsel = 0;
+  __syncthreads();
+  // threshold bin, recovered from any candidate (all share it)
+  const uint32_t T = ((in_lds ? skey[0] : ws.ckey[(int64_t)r * kCap]) - kmin) >> shift;
+
+  // resolve the low `shift` bits of (key - kmin): by ranking the candidates against each other
+  // when there are few, else in rounds of at most 10 bits
+  uint32_t prefix = T;                // known high part of (key - kmin)
+  int low = shift;                    // bits still to resolve
+  int need_r = need;
+  if (in_lds && low > 0 && nc <= kRankMax) {
+    constexpr int kPer = kCap / kFinalThreads;
+    uint32_t v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      const int i = tid + j * kFinalThreads;
+      v[j] = i < nc ? skey[i] - kmin : 0u;
+    }
+    const int nv = (int)min((int64_t)kPer, max((int64_t)0, ((int64_t)nc - tid + kFinalThreads - 1) / kFinalThreads));
+    int need_eq = 0;
+    prefix = rank_finish<kFinalThreads, kPer>(v, nv, low, prefix, nc, need_r, h, scan, res, need_eq);   // key - kmin
+    need_r = need_eq;
+    low = 0;
+  }
+  while (low > 0) {
+    const int take = low > 10 ? 10 : low;
+    const int sh = low - take;
+    for (int i = tid; i < 1024; i += kFinalThreads) h[i] = 0;
+    __syncthreads();
+    if (in_lds) {
+      for (int i = tid; i < nc; i += kFinalThreads) {
+        const uint32_t v = skey[i] - kmin;
+        if ((v >> low) == prefix) atomicAdd(&h[(v >> sh) & ((1u << take) - 1)], 1);
+      }
+    } else {
+      for (int64_t i = tid; i < n; i += kFinalThreads) {
+        const uint32_t v = min(max(ord_key(row[i]), kmin), kmax) - kmin;
+        if ((v >> low) == prefix) atomicAdd(&h[(v >> sh) & ((1u << take) - 1)], 1);
+      }
+    }
+    __syncthreads();
+    const int d = find_threshold<kFinalThreads, 1024>(h, need_r, scan, res);
+    need_r -= res[1];
+    prefix = (prefix << take) | (uint32_t)d;
+    low = sh;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix + kmin;   // exact key of the k-th largest
+  const int need_ties = need_r;         // elements equal to thr to keep (lowest positions)
+
+  for (int i = tid; i < na; i += kFinalThreads) sel[i] = ws.above[(int64_t)r * k + i];
+  if (tid == 0) nsel = na;
+  __syncthreads();
+  if (in_lds) {
+    for (int i = tid; i < nc; i += kFinalThreads) {
+      if (skey[i] > thr) {
+        push(sel, &nsel, spos[i]);
+      } else if (skey[i] == thr) {
+        int rank = 0;                     // position rank among the exact ties
+        for (int j = 0; j < nc; j++) rank += (skey[j] == thr && spos[j] < spos[i]);
+        if (rank < need_ties) push(sel, &nsel, spos[i]);
+      }
+    }
+  } else {
+    // more candidates than LDS holds: walk the row in position order
+    int nties_seen = 0;
+    for (int64_t b = 0; b < n; b += kFinalThreads) {
+      const int64_t i = b + tid;
+      const uint32_t key = i < n ? min(max(ord_key(row[i]), kmin), kmax) : 0u;
+      const bool inT = i < n && ((key - kmin) >> shift) == T;
+      if (inT && key > thr) push(sel, &nsel, (int)i);
+      const int tie = (inT && key == thr) ? 1 : 0;
+      int all;
+      const int incl = block_prefix<kFinalThreads>(tie, scan, &all);
+      if (tie && nties_seen + incl - 1 < need_ties) push(sel, &nsel, (int)i);
+      nties_seen += all;
+    }
+  }
+  __syncthreads();
+  write_ascending(sel, min(nsel, k), n, k, out, (int*)skey, scan);
+}
+
 // The need-th largest (1 <= need <= cnt) of keys[0..cnt) in LDS, all in [base, base + 2^width),
 // in radix rounds of at most 12 bits over (key - base) from bit `width` down, and a rank finish
 // once the threshold bin holds at most kRankMax keys.  need_eq receives how many keys equal to
@@ -690,8 +692,8 @@ __device__ inline uint32_t kth_largest(const uint32_t* keys, int cnt, int need, 
 __global__ void DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ pos, int64_t stride,
                                                               int32_t k, int32_t* __restrict__ idx, Ws ws) {
   // Under 64 KiB of LDS, so two work-groups share a CU.  The candidates (keys, then positions)
-  // and, once they are selected, the output bitmap share one buffer; the radix histogram lives
-  // in whichever of the tie list and the candidate buffer is idle at the time.
+  // and, once they are selected, the output sort's scratch share one buffer; the radix
+  // histogram lives in whichever of the tie list and the candidate buffer is idle at the time.
   __shared__ uint32_t cand[2 * kCap];
   __shared__ uint32_t ties[kCap];
   __shared__ int sel[kTopkMax];
@@ -700,10 +702,9 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ p
   __shared__ int res[2];
   __shared__ int nsel, nties;
   __shared__ uint32_t cmax;
-  static_assert(2 * kCap == kBitmapMaxN / 32, "the output bitmap reuses the candidate buffer");
+  static_assert(2 * kCap >= 2 * kTopkMax, "the output sort's scratch reuses the candidate buffer");
   uint32_t* skey = cand;
   int* spos = (int*)(cand + kCap);
-  uint32_t* bitmap = cand;
   const int r = blockIdx.x, tid = threadIdx.x;
   // every candidate slot of the row is read at once, before the count arrives (slots past the
   // count hold stale words that are never used), so the candidates cost one memory round trip
@@ -760,7 +761,7 @@ __global__ void DSA_TWO_GROUPS_PER_CU k_filt_final(const int32_t* __restrict__ p
   for (int i = tid; i < nt; i += kFinalThreads)
     if (ties[i] >= tcut) push(sel, &nsel, (int)~ties[i]);
   __syncthreads();
-  write_ascending(sel, min(nsel, k), n, k, out, bitmap, scan);
+  write_ascending(sel, min(nsel, k), n, k, out, (int*)cand, scan);
 }
 
 // Rows of at most 32 x NT scores: one work-group of NT threads per row does the whole
@@ -931,8 +932,8 @@ static hipError_t launch_radix_passes(const float* logits, int64_t stride, RowsV
   if (visible > k) {
     unsigned nchunk = (unsigned)((visible + kChunk - 1) / kChunk);
     if (few_flagged && nchunk > kGatedChunkGroups) nchunk = kGatedChunkGroups;
-    hipLaunchKernelGGL(k_hist, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
-    hipLaunchKernelGGL(k_select, dim3(nchunk, R), dim3(256), 0, s, logits, stride, rows.pos, k, w, gate);
+    hipLaunchKernelGGL(k_hist, dim3(nchunk, R), dim3(kPassThreads), 0, s, logits, stride, rows.pos, k, w, gate);
+    hipLaunchKernelGGL(k_select, dim3(nchunk, R), dim3(kPassThreads), 0, s, logits, stride, rows.pos, k, w, gate);
   }
   hipLaunchKernelGGL(k_final, dim3(R), dim3(kFinalThreads), 0, s, logits, stride, rows.pos, k, idx, w, gate);
   return hipGetLastError();
