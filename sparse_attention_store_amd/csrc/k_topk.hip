@@ -252,11 +252,12 @@ __device__ inline int find_threshold(const int* h, int k, int* scan, int* result
 // is counted against the others: the key x with count(> x) < need <= count(>= x) is the
 // need-th largest, and need - count(> x) of its exact ties belong to the selection.  This
 // replaces the remaining radix rounds (a histogram clear, fill and scan each).  Returns x - base
-// and sets need_eq; all NT threads call it; res and scan are scratch (res[0] counts the gather).
+// and sets need_eq (and *n_eq, when given, to the number of in-bin keys equal to x); all NT
+// threads call it; res and scan (at least 3 ints) are scratch (res[0] counts the gather).
 constexpr int kRankMax = 256;
 template <int NT, int kPer>
 __device__ inline uint32_t rank_finish(const uint32_t (&v)[kPer], int nv, int low, uint32_t prefix, int in_bin,
-                                       int need, int* h, int* scan, int* res, int& need_eq) {
+                                       int need, int* h, int* scan, int* res, int& need_eq, int* n_eq = nullptr) {
   const int tid = threadIdx.x;
   if (tid == 0) res[0] = 0;
   __syncthreads();
@@ -272,11 +273,12 @@ __device__ inline uint32_t rank_finish(const uint32_t (&v)[kPer], int nv, int lo
       gt += y > x;
       eq += y == x;
     }
-    if (gt < need && need <= gt + eq) { scan[0] = (int)x; scan[1] = need - gt; }   // one value, maybe several writers
+    if (gt < need && need <= gt + eq) { scan[0] = (int)x; scan[1] = need - gt; scan[2] = eq; }   // one value, maybe several writers
   }
   __syncthreads();
   const uint32_t x = (uint32_t)scan[0];
   need_eq = scan[1];
+  if (n_eq != nullptr) *n_eq = scan[2];
   __syncthreads();                     // h, scan and res are free again
   return x;
 }
@@ -569,6 +571,7 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
   uint32_t prefix = T;                // known high part of (key - kmin)
   int low = shift;                    // bits still to resolve
   int need_r = need;
+  int n_eq = -1;                      // exact ties at the threshold among the candidates, when known
   if (in_lds && low > 0 && nc <= kRankMax) {
     constexpr int kPer = kCap / kFinalThreads;
     uint32_t v[kPer];
@@ -579,7 +582,7 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
     }
     const int nv = (int)min((int64_t)kPer, max((int64_t)0, ((int64_t)nc - tid + kFinalThreads - 1) / kFinalThreads));
     int need_eq = 0;
-    prefix = rank_finish<kFinalThreads, kPer>(v, nv, low, prefix, nc, need_r, h, scan, res, need_eq);   // key - kmin
+    prefix = rank_finish<kFinalThreads, kPer>(v, nv, low, prefix, nc, need_r, h, scan, res, need_eq, &n_eq);   // key - kmin
     need_r = need_eq;
     low = 0;
   }
@@ -617,8 +620,12 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
       if (skey[i] > thr) {
         push(sel, &nsel, spos[i]);
       } else if (skey[i] == thr) {
-        int rank = 0;                     // position rank among the exact ties
-        for (int j = 0; j < nc; j++) rank += (skey[j] == thr && spos[j] < spos[i]);
+        // every tie is kept when there are no more than needed; else the position rank among them
+        int rank = 0;
+        if (n_eq != need_ties) {
+#pragma unroll 8
+          for (int j = 0; j < nc; j++) rank += (skey[j] == thr && spos[j] < spos[i]);
+        }
         if (rank < need_ties) push(sel, &nsel, spos[i]);
       }
     }
