@@ -545,6 +545,21 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
   __shared__ int nsel;
   const int r = blockIdx.x, tid = threadIdx.x;
   if (gate != nullptr && !gate[r]) return;
+  // every candidate slot and every selected-above slot of the row is read at once, before the
+  // counts arrive (slots past them hold stale words that are never used): one memory round trip
+  constexpr int kPer = kCap / kFinalThreads, kPerA = kTopkMax / kFinalThreads;
+  uint32_t ck[kPer];
+  int cp[kPer], ab[kPerA];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    ck[j] = ws.ckey[(int64_t)r * kCap + tid + j * kFinalThreads];
+    cp[j] = ws.cpos[(int64_t)r * kCap + tid + j * kFinalThreads];
+  }
+#pragma unroll
+  for (int j = 0; j < kPerA; j++) {
+    const int i = tid + j * kFinalThreads;
+    ab[j] = i < k ? ws.above[(int64_t)r * k + i] : 0;
+  }
   const int64_t n = row_len(pos, r, stride);
   int32_t* out = idx + (int64_t)r * k;
   if (n <= k) {                       // short context or padded row: every visible position
@@ -559,9 +574,19 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
   const int need = k - na;            // >= 1: the threshold bin holds the k-th key
   const float* row = logits + (int64_t)r * stride;
   const bool in_lds = nc <= kCap;
-  if (in_lds)
-    for (int i = tid; i < nc; i += kFinalThreads) { skey[i] = ws.ckey[(int64_t)r * kCap + i]; spos[i] = ws.cpos[(int64_t)r * kCap + i]; }
-  if (tid == 0) nsel = 0;
+  if (in_lds) {
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      const int i = tid + j * kFinalThreads;
+      if (i < nc) { skey[i] = ck[j]; spos[i] = cp[j]; }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPerA; j++) {
+    const int i = tid + j * kFinalThreads;
+    if (i < na) sel[i] = ab[j];
+  }
+  if (tid == 0) nsel = na;
   __syncthreads();
   // threshold bin, recovered from any candidate (all share it)
   const uint32_t T = ((in_lds ? skey[0] : ws.ckey[(int64_t)r * kCap]) - kmin) >> shift;
@@ -573,7 +598,6 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
   int need_r = need;
   int n_eq = -1;                      // exact ties at the threshold among the candidates, when known
   if (in_lds && low > 0 && nc <= kRankMax) {
-    constexpr int kPer = kCap / kFinalThreads;
     uint32_t v[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
@@ -611,10 +635,6 @@ __global__ void __launch_bounds__(kFinalThreads) k_final(const float* __restrict
   }
   const uint32_t thr = prefix + kmin;   // exact key of the k-th largest
   const int need_ties = need_r;         // elements equal to thr to keep (lowest positions)
-
-  for (int i = tid; i < na; i += kFinalThreads) sel[i] = ws.above[(int64_t)r * k + i];
-  if (tid == 0) nsel = na;
-  __syncthreads();
   if (in_lds) {
     for (int i = tid; i < nc; i += kFinalThreads) {
       if (skey[i] > thr) {
@@ -1018,7 +1038,7 @@ LogitsMode topk_fallback_mode(void* ws, int32_t R, int32_t k, int32_t skip_upto)
 hipError_t launch_topk_fallback(const float* logits, int64_t stride, RowsView rows, int32_t k, int32_t* idx,
                                 void* ws, bool all_flagged, hipStream_t s) {
   const Ws w = carve(ws, rows.n, k);
-  return launch_radix_passes(logits, stride, rows, k, idx, w, w.flag, !all_flagged, s);
+  return launch_radix_passes(logits, stride, rows, k, idx, w, all_flagged ? nullptr : w.flag, !all_flagged, s);
 }
 
 DSA_DEFINE_ERROR_ACCESSOR(take_device_errors_topk)
