@@ -351,12 +351,11 @@ def test_fused_topk_ties_inside_candidate_list():
 
 @pytest.mark.parametrize("path", ["direct", "filtered"])
 @pytest.mark.parametrize("k", [100, 1000, 2048])
-def test_topk_row_longer_than_the_bitmap(k, path):
-    """Rows of 300,000 and 600,000 positions, longer than the LDS bitmap that orders the output
-    of shorter rows: the selection is ordered by a bitonic network padded to a power of two
-    (128, 1024, 2048), and rows of over 8,192 samples take the long threshold kernel.  The fused
+def test_topk_long_rows(k, path):
+    """Rows of 300,000 and 600,000 positions (512-position buckets in the output sort; rows of
+    over 8,192 samples take the long threshold kernel), for k = 100, 1000 and 2048.  The fused
     and the separate calls against the oracle's set; both ascending and equal."""
-    _announce(f"top-k of rows longer than the bitmap, k={k}, {path} fused path")
+    _announce(f"top-k of long rows, k={k}, {path} fused path")
     w = gi.make_decode("long_rows_k", gi.SEED_BASE + 74, [300000, 600000])
     L = DeviceLayer(w, latent_layers=[])
     dsa.dsa_quant_fp8(L.q_idx, L.q8, L.qs)

@@ -139,6 +139,33 @@ def test_topk_stage_exact_at_kernel_limits(n):
         assert np.array_equal(_topk_gpu(lg, pos, k), ref), f"k={k}"
 
 
+@pytest.mark.parametrize("n", [40000, 1048576])
+def test_topk_output_order_bucket_patterns(n):
+    """Rows longer than the one-work-group top-k: the multi-kernel radix writes the selection
+    ascending by a counting sort on the positions' high bits (2048 buckets).  Selections that fill
+    a few buckets completely (a contiguous block at the start, in the middle, at the end), one
+    position per bucket, and a random spread, against the oracle, for k = 2048 and 100."""
+    _announce(f"topk output order, bucket patterns, n={n}")
+    rng = np.random.default_rng(n + 11)
+    stride = orc.logits_stride(n - 1)
+    R = 5
+    lg = np.full((R, stride), -np.inf, np.float32)
+    lg[:, :n] = rng.random((R, n), dtype=np.float32)
+    hi = 2.0 + rng.random(2048, dtype=np.float32)          # planted scores above every other
+    lg[0, :2048] = hi                                      # block at the start
+    mid = (n // 2) & ~511
+    lg[1, mid:mid + 2048] = hi                             # block in the middle, bucket-aligned
+    lg[2, n - 2048:n] = hi                                 # block at the end
+    step = n // 2048
+    lg[3, np.arange(2048) * step] = hi                     # one position per bucket
+    pos = np.full(R, n - 1, np.int32)                      # row 4: the random spread
+    for k in (2048, 100):
+        ref, _ = orc.topk(lg, pos, k)
+        got = _topk_gpu(lg, pos, k)
+        assert np.array_equal(got, ref), f"k={k}"
+        assert (np.diff(got, axis=1) > 0).all(), "ascending"
+
+
 @pytest.mark.parametrize("cid", [0, 2])
 def test_mla_stage(cid):
     _announce(f"mla stage c{cid}")
