@@ -41,13 +41,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kLongGroupRG = 8;         // rows per sub-group of a prefill chunk's long group
-// filter mode: candidates per row and work-group that the launch sizes chunks for
+// filter mode: candidates held per row and work-group (sized so that four work-groups of
+// eight rows fit a CU's LDS: 32 KiB of q + 1 KiB of weights + 8 x 104 x 8 B of candidates)
 template <int RG> constexpr int kStage = RG <= 6 ? 768 / RG : 104;
-// ... and the LDS stage that holds them: each wave has its own slots per row, about 1.5 to 2
-// times its share of kStage (6 B each: key + 16-bit position in the chunk), so that a wave appends
-// with a ballot and a lane count, without an LDS atomic and its round trip per row and page (four
-// work-groups of eight rows still fit a CU's LDS: 32 KiB of q + 1 KiB of weights + 8 x 4 x 36 x 6 B)
-template <int RG> constexpr int kWaveStage = RG <= 6 ? 64 : 36;
 // q rows are 128 B in LDS; the 16-B chunk c of row r sits at chunk c ^ (r & 7), so the 16
 // lanes reading chunk g of 16 consecutive rows hit distinct banks without padding
 __device__ __forceinline__ int qswz(int row, int c) { return row * kIdxDim + 16 * (c ^ (row & 7)); }
@@ -150,12 +146,11 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
                 int chunk_pages, LogitsMode md) {
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[RG * kIdxHeads * kIdxDim];
   __shared__ __attribute__((aligned(16))) float w_lds[RG * kIdxHeads];
-  // filter mode: candidates of this work-group, per row and wave, before one append per row
-  constexpr bool kF = KIND == kLogitsFilter;
-  constexpr int kWS = kWaveStage<RG>;
-  __shared__ uint32_t st_key[kF ? RG : 1][kF ? kWaves : 1][kF ? kWS : 1];
-  __shared__ uint16_t st_lpos[kF ? RG : 1][kF ? kWaves : 1][kF ? kWS : 1];
-  __shared__ int st_n[kF ? RG : 1][kF ? kWaves : 1];
+  // filter mode: candidates of this work-group, per row, before one append per row
+  constexpr int kStage = dsa::kStage<RG>;     // per row
+  __shared__ uint32_t st_key[KIND == kLogitsFilter ? RG : 1][KIND == kLogitsFilter ? kStage : 1];
+  __shared__ int st_pos[KIND == kLogitsFilter ? RG : 1][KIND == kLogitsFilter ? kStage : 1];
+  __shared__ int st_n[RG];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,6 +189,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       const uint32_t f = t <= 0x007FFFFFu ? 0xFF800000u : ((t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t);
       thr_f[r] = __int_as_float(__builtin_amdgcn_readfirstlane((int)f));     // wave-uniform: scalar
     }
+    if (tid < RG) st_n[tid] = 0;
   }
   const int32_t rq = req[row0];
   // pages with a visible key (never past the logits row), in units of `step`
@@ -235,28 +231,17 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       const uint32_t u = __float_as_uint(x);
       return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     };
-    // filter mode: the lanes whose score v of row r passes keep (key, position) in this wave's
-    // slots of the stage: a ballot, each lane's rank among the passing lanes, and a wave-uniform
-    // running count (no LDS atomic)
-    const int s_chunk0 = (int)(pg0 * step * 64);          // first position of the chunk
-    int wcnt[RG];
-#pragma unroll
-    for (int r = 0; r < RG; r++) wcnt[r] = 0;
-    auto stage = [&](int r, int s, float v, bool pass) {
-      const uint64_t m = __ballot(pass);
-      if (m == 0) return;
-      const int sl = wcnt[r] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      wcnt[r] += __popcll(m);
-      if (!pass) return;
-      if (sl < kWS) {
-        st_key[r][wave][sl] = key_of(v);
-        st_lpos[r][wave][sl] = (uint16_t)(s - s_chunk0);
+    // filter mode: one kept (key, position) of row r into the work-group's stage
+    auto stage = [&](int r, int s, uint32_t key) {
+      const int sl = atomicAdd(&st_n[r], 1);
+      if (sl < kStage) {
+        st_key[r][sl] = key;
+        st_pos[r][sl] = s;
       } else {
-        // the wave's slots are full: straight to the row's list (a count past fcap still flags the row)
+        // stage full: straight to the row's list (a count past fcap still flags the row)
         const int gi = atomicAdd(&md.fcnt[row0 + r], 1);
         if (gi < md.fcap) {
-          md.fkey[(row0 + r) * md.fcap + gi] = key_of(v);
+          md.fkey[(row0 + r) * md.fcap + gi] = key;
           md.fpos[(row0 + r) * md.fcap + gi] = s;
         }
       }
@@ -307,7 +292,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         const float v = vis ? mine * key_scale(P) : -INFINITY;
         if (KIND == kLogitsFilter) {
           // keep the scores at or above the row's threshold (rare: a few per cent)
-          stage(r, s, v, vis && v >= thr_f[r]);
+          if (vis && v >= thr_f[r]) stage(r, s, key_of(v));
         } else {
           // nontemporal: 5% off the c2 logits pass, and the top-k that reads them back is no slower
           __builtin_nontemporal_store(v, &logits[(row0 + r) * stride + s]);
@@ -323,6 +308,17 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     // loop takes pages in pairs and leaves only at its end, with the same loads in flight on
     // every path (past the last page the last one is loaded again; a bad id loads page 0 and
     // scores as invisible), so the waits for a page's operands keep the next page in flight.
+    // this wave's first sampled page (filter mode): its stored scores are requested before the
+    // page loop, so they arrive with the first page instead of costing a round trip per row after
+    // the loop (the other sampled pages, when a wave has more than one, follow the loop; groups of
+    // eight rows load after the loop as well, their registers being full)
+    const bool samp0 = RG <= 6 && wave < nsamp;
+    const int s_samp0 = (int)((pg0 + (int64_t)wave * S) * 64) + lane;
+    float vs0[RG];
+    if (samp0) {
+#pragma unroll
+      for (int r = 0; r < RG; r++) vs0[r] = logits[(row0 + r) * stride + s_samp0];
+    }
     PageRegs<FMT> pa, pb;
     auto page_addr = [&](int id) { return cache + (int64_t)(id < 0 ? 0 : id) * kPageBytes<FMT>; };
     auto page_id = [&](int i) { return __builtin_amdgcn_readlane(my_id, min(i, nw - 1)); };
@@ -342,16 +338,21 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       if (i < nw) process(pa, page_vi(i), ida);     // an odd page count: the last page
     }
     // the sampled pages of the chunk: their stored scores against the threshold (a page of a
-    // bad id holds -inf)
-    for (int m = wave; m < nsamp; m += kWaves) {
-      const int s = (int)((pg0 + (int64_t)m * S) * 64) + lane;
+    // bad id holds -inf: a visible key's score is finite, and the scored path never stages those,
+    // whatever the threshold)
+    if (samp0) {
 #pragma unroll
-      for (int r = 0; r < RG; r++) {
-        const float v = logits[(row0 + r) * stride + s];
-        // -inf: a page whose id failed the range check (a visible key's score is finite); the
-        // scored path never stages those, whatever the threshold
-        stage(r, s, v, s <= prow[r] && v > -INFINITY && v >= thr_f[r]);
-      }
+      for (int r = 0; r < RG; r++)
+        if (s_samp0 <= prow[r] && vs0[r] > -INFINITY && vs0[r] >= thr_f[r]) stage(r, s_samp0, key_of(vs0[r]));
+    }
+    for (int m = RG <= 6 ? wave + kWaves : wave; m < nsamp; m += kWaves) {
+      const int s = (int)((pg0 + (int64_t)m * S) * 64) + lane;
+      float vs[RG];
+#pragma unroll
+      for (int r = 0; r < RG; r++) vs[r] = logits[(row0 + r) * stride + s];
+#pragma unroll
+      for (int r = 0; r < RG; r++)
+        if (s <= prow[r] && vs[r] > -INFINITY && vs[r] >= thr_f[r]) stage(r, s, key_of(vs[r]));
     }
     if (kRange && md.range != nullptr) {
       __shared__ uint32_t red[kWaves][2];
@@ -372,30 +373,23 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       }
     }
     if (KIND == kLogitsFilter) {
-      // one append per row: reserve room in the row's candidate list for every wave's staged
-      // entries (the overflow went to the list directly), then each wave copies its own
-      __shared__ int st_off[kF ? RG : 1][kF ? kWaves : 1];
-      if (lane == 0) {
-#pragma unroll
-        for (int r = 0; r < RG; r++) st_n[r][wave] = min(wcnt[r], kWS);
-      }
+      // one append per row: reserve room in the row's candidate list, then copy
+      __shared__ int st_base[RG];
       __syncthreads();
       if (tid < RG) {
-        int tot = 0;
-#pragma unroll
-        for (int w2 = 0; w2 < kWaves; w2++) tot += st_n[tid][w2];
-        int base = tot == 0 ? 0 : atomicAdd(&md.fcnt[row0 + tid], tot);
-#pragma unroll
-        for (int w2 = 0; w2 < kWaves; w2++) { st_off[tid][w2] = base; base += st_n[tid][w2]; }
+        const int n = st_n[tid];
+        // only the staged entries: the overflow went to the list directly
+        const int ns = min(n, kStage);
+        st_base[tid] = ns == 0 ? 0 : atomicAdd(&md.fcnt[row0 + tid], ns);
       }
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < RG; r++) {
-        const int n = st_n[r][wave], base = st_off[r][wave];
-        for (int i = lane; i < n; i += 64)
+        const int n = min(st_n[r], kStage), base = st_base[r];
+        for (int i = tid; i < n; i += 256)
           if (base + i < md.fcap) {
-            md.fkey[(row0 + r) * md.fcap + base + i] = st_key[r][wave][i];
-            md.fpos[(row0 + r) * md.fcap + base + i] = s_chunk0 + st_lpos[r][wave][i];
+            md.fkey[(row0 + r) * md.fcap + base + i] = st_key[r][i];
+            md.fpos[(row0 + r) * md.fcap + base + i] = st_pos[r][i];
           }
       }
     }
