@@ -387,16 +387,22 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
     for (int ks = 0; ks < 2; ks++) qr_raw[ks] = *reinterpret_cast<const DSA_GLOBAL bf16x8*>(qh + kVal + 32 * ks + 8 * g);
   }
 
-  // resolve record addresses (physical token index) of this split's keys: every thread's
-  // index loads, then every page-table load, so the segment waits two memory round trips
+  // resolve record addresses (physical token index) of this split's keys: every index load,
+  // then every page-table load, so the lookups wait two memory round trips.  The PV waves do
+  // them while the QK waves turn their q rows into MFMA operands: the conversion (about 8K
+  // cycles of dependent VALU work per wave) then overlaps the lookups instead of following them
+  // (one 128-key split: 9.8K cycles from entry to the barrier below, 6.1K + 8.1K before).
   for (int t = tid; t < ntiles; t += kThreads) tile_bad[t] = 0;
   __syncthreads();
-  {
-    constexpr int kPer = kMaxSplitKeys / kThreads;
+  QkOps Q;
+  if (!is_qk) {
+    constexpr int kResolvers = kThreads / 2;
+    constexpr int kPer = kMaxSplitKeys / kResolvers;
+    const int rt = tid - kResolvers;
     int sv[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; u++) {
-      const int j = tid + u * kThreads;
+      const int j = rt + u * kResolvers;
       sv[u] = j < nkeys ? idx[(int64_t)r * k + j0 + j] : -1;
     }
     // unconditional page-table reads (slot 0 stands in for keys that need none), range
@@ -423,56 +429,18 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
     for (int u = 0; u < kPer; u++) {
       if (want[u] && !col_ok[u]) raise_device_error(kErrRequest);
       if (want[u] && col_ok[u] && (pv[u] < 0 || pv[u] >= num_pages)) { raise_device_error(kErrPageId); pv[u] = -1; }
-      const int j = tid + u * kThreads;
+      const int j = rt + u * kResolvers;
       if (j < ntiles * kTile) {
         const int ph = want[u] && pv[u] >= 0 ? (int)(pv[u] * kPage + (sv[u] & 63)) : -1;
         phys[j] = ph;
         if (ph < 0) tile_bad[j / kTile] = 1;
       }
     }
-  }
-
-  __syncthreads();                              // phys ready
-  int phn[kDmaPerWave];                          // QK waves: record ids of the next tile to copy
-  if (is_qk) {
-    // every lookup before the first copy, so no LDS read waits for the copies in flight
-    // The first kDepth tiles are always copied (tiles past the segment copy the pool's first
-    // record into their unused buffer), so the number of copies after the q loads is fixed
-    // and the q operands wait for the q loads only.
-    int ph0[kDepth][kDmaPerWave];
-#pragma unroll
-    for (int t = 0; t < kDepth; t++) {
-      read_tile_phys(phl, t * kTile, wave, lane, ph0[t]);      // t * kTile + 31 < kMaxSplitKeys
-#pragma unroll
-      for (int u = 0; u < kDmaPerWave; u++) ph0[t][u] = t < ntiles ? ph0[t][u] : -1;
-    }
-    if (kDepth < ntiles) read_tile_phys(phl, kDepth * kTile, wave, lane, phn);
-#pragma unroll
-    for (int t = 0; t < kDepth; t++) issue_tile_ph(cache, ph0[t], tl + t * kTileBytes, wave, lane);
-  }
-
-  // Start of every iteration (both roles, same barriers in the same order): wait for this
-  // wave's copies of tile `it`, then a barrier so that all of tile `it` is in LDS and every
-  // wave is done with QK(it-1) and PV(it-2) (whose buffers are refilled next).
-  auto wait_tile = [&](int it) {
-    if (is_qk && it < ntiles) {
-      // tiles it+1 .. it+kDepth-1 (those that exist) may stay in flight
-      const int ahead = min(kDepth - 1, ntiles - 1 - it);
-      if (ahead >= 3) wait_vmcnt<3 * kDmaPerWave>();
-      else if (ahead >= 2) wait_vmcnt<2 * kDmaPerWave>();
-      else if (ahead == 1) wait_vmcnt<kDmaPerWave>();
-      else wait_vmcnt<0>();
-    }
-    lds_barrier();
-  };
-
-  if (is_qk) {
-    // ======================= QK waves: heads 16qw..16qw+15, full 576 contraction dims
+  } else {
     // q of heads 16qw..16qw+15 as MFMA B operands.  The 512 latent dims are split into two
     // FP8 terms per 128-dim block, q = hi * 2^e_hi + lo * 2^e_lo (lo quantises the residual
     // of hi), which carries bf16's 8 significant bits; the 64 rope dims stay bf16.  Lane
     // holds head 16qw + c16, dims 128b + [16g, 16g+16) and 128b + 64 + [16g, 16g+16).
-    QkOps Q;
     {
 #pragma unroll
       for (int b = 0; b < 4; b++) {
@@ -519,6 +487,45 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
 #pragma unroll
       for (int ks = 0; ks < 2; ks++) Q.qr[ks] = qr_raw[ks];
     }
+  }
+
+  __syncthreads();                              // phys ready
+  int phn[kDmaPerWave];                          // QK waves: record ids of the next tile to copy
+  if (is_qk) {
+    // every lookup before the first copy, so no LDS read waits for the copies in flight
+    // The first kDepth tiles are always copied (tiles past the segment copy the pool's first
+    // record into their unused buffer), so the number of copies after the q loads is fixed
+    // and the q operands wait for the q loads only.
+    int ph0[kDepth][kDmaPerWave];
+#pragma unroll
+    for (int t = 0; t < kDepth; t++) {
+      read_tile_phys(phl, t * kTile, wave, lane, ph0[t]);      // t * kTile + 31 < kMaxSplitKeys
+#pragma unroll
+      for (int u = 0; u < kDmaPerWave; u++) ph0[t][u] = t < ntiles ? ph0[t][u] : -1;
+    }
+    if (kDepth < ntiles) read_tile_phys(phl, kDepth * kTile, wave, lane, phn);
+#pragma unroll
+    for (int t = 0; t < kDepth; t++) issue_tile_ph(cache, ph0[t], tl + t * kTileBytes, wave, lane);
+  }
+
+  // Start of every iteration (both roles, same barriers in the same order): wait for this
+  // wave's copies of tile `it`, then a barrier so that all of tile `it` is in LDS and every
+  // wave is done with QK(it-1) and PV(it-2) (whose buffers are refilled next).
+  auto wait_tile = [&](int it) {
+    if (is_qk && it < ntiles) {
+      // tiles it+1 .. it+kDepth-1 (those that exist) may stay in flight
+      const int ahead = min(kDepth - 1, ntiles - 1 - it);
+      if (ahead >= 3) wait_vmcnt<3 * kDmaPerWave>();
+      else if (ahead >= 2) wait_vmcnt<2 * kDmaPerWave>();
+      else if (ahead == 1) wait_vmcnt<kDmaPerWave>();
+      else wait_vmcnt<0>();
+    }
+    lds_barrier();
+  };
+
+  if (is_qk) {
+    // ======================= QK waves: heads 16qw..16qw+15, full 576 contraction dims
+    // (their q operands Q were formed above, while the PV waves resolved the records)
     float m_run = -INFINITY, l_part = 0.f;      // for head 16qw + c16
     for (int it = 0; it < ntiles; it++) {
       wait_tile(it);
