@@ -348,15 +348,15 @@ def mtp_carry_saved_fraction(draft_steps: int = 5, n_full: int = 21) -> float:
     return mtp_carry_saved_read_bytes(1, draft_steps) / read_bytes_per_step(1, n_full)
 
 
-def chunked_prefill_indexer_read_bytes(L: int = 1 << 20, rows_per_read: int = 32, n_full: int = 21) -> int:
+def chunked_prefill_indexer_read_bytes(L: int, rows_per_read: int, n_full: int = 21) -> int:
     """Index-K bytes the prefill of an L-token prompt reads when each block of `rows_per_read`
     consecutive query rows reads the keys visible to its last row once, 132 B per token, per
     full layer.  A kernel that reads the cache once per 32K-row chunk reads `rows_per_read` =
-    32768's worth.  Parity unpinned for the default: the page's 1M prefill figure ([IDXC], the
-    cross-layer section: about 47 TB, an accounting the page calls simplified) does not say
-    how often a key is read; 32-row blocks is the granularity that reproduces it, a fitted
-    reading, so that figure pins nothing.  The formula itself is pinned by its two limits
-    (one row per block: every row reads its own prefix; one block: one read of the prompt)."""
+    32768's worth.  The read granularity is an argument with no default: the page's 1M prefill
+    figure ([IDXC], the cross-layer section: about 47 TB, an accounting the page calls
+    simplified) does not say how often a key is read, so no value of it is the page's.  The
+    formula is pinned by its two limits (one row per block: every row reads its own prefix; one
+    block: one read of the prompt) and by brute force on a tiny prompt."""
     n = (L + rows_per_read - 1) // rows_per_read
     return n_full * index_k_bytes_per_token() * sum(min(L, (b + 1) * rows_per_read) for b in range(n))
 
