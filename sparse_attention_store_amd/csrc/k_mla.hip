@@ -137,7 +137,7 @@ __device__ __forceinline__ void chunk_src(int c, int& key, int& rc) {
 // kDmaPerWave copies so that per-tile vmcnt accounting is uniform; lanes past the tile or of
 // invalid keys copy from the first record of the pool into the buffer (the records of
 // invalid keys are zeroed before use).  The record lookups (read_tile_phys) are done a tile
-// ahead of the copies (issue_tile_ph), so the copies never wait for LDS.
+// ahead of the copies (issue_copies), so the copies never wait for LDS.
 __device__ __forceinline__ void read_tile_phys(const DSA_LDS int* __restrict__ phys, int tile_base, int wave, int lane,
                                                int (&ph)[kDmaPerWave]) {
 #pragma unroll
@@ -148,10 +148,13 @@ __device__ __forceinline__ void read_tile_phys(const DSA_LDS int* __restrict__ p
     ph[u] = phys[tile_base + key];   // < ntiles * kTile <= kMaxSplitKeys
   }
 }
-__device__ __forceinline__ void issue_tile_ph(const uint8_t* cache, const int (&ph)[kDmaPerWave], DSA_LDS uint8_t* buf,
-                                              int wave, int lane) {
+// Copies U0 .. U1-1 of this wave's share of a tile.
+template <int U0, int U1>
+__device__ __forceinline__ void issue_copies(const uint8_t* cache, const int (&ph)[kDmaPerWave], DSA_LDS uint8_t* buf,
+                                             int wave, int lane) {
+  static_assert(0 <= U0 && U0 <= U1 && U1 <= kDmaPerWave, "copy range");
 #pragma unroll
-  for (int u = 0; u < kDmaPerWave; u++) {
+  for (int u = U0; u < U1; u++) {
     const int c = (wave * kDmaPerWave + u) * 64 + lane;
     int key, rc;
     chunk_src(min(c, kTileChunks - 1), key, rc);
@@ -208,10 +211,16 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
                                         DSA_LDS int* __restrict__ resc_p, const QkOps& Q, float sm_log2, float& m_run, float& l_part, int qw, int wave,
                                         int lane, int tid, int (&phn)[kDmaPerWave]) {
   const int g = lane >> 4, c16 = lane & 15;
-  if (it + kDepth < ntiles) {
-    issue_tile_ph(cache, phn, dst, wave, lane);                  // record ids read a tile ago
-    if (it + kDepth + 1 < ntiles) read_tile_phys(phys, (it + kDepth + 1) * kTile, wave, lane, phn);
-  }
+  // The copies of tile it + kDepth (record ids read a tile ago) go out in three groups: before
+  // the first pair of 16-key blocks and after each pair's MFMAs.  A copy instruction waits for
+  // room among the CU's outstanding misses; issued all at once, that wait held the wave for
+  // about as long as its MFMA and softmax work that followed.  Spread out, the waits overlap
+  // the MFMAs already in flight and the memory pipe is fed through the tile (c2: 198 -> 183 us
+  // per launch).  The scheduling barriers keep the compiler from regrouping them.
+  const bool more = it + kDepth < ntiles;
+  constexpr int kCopyA = (kDmaPerWave + 2) / 3, kCopyB = kMT == 2 ? kDmaPerWave : 2 * kCopyA;
+  if (more) issue_copies<0, kCopyA>(cache, phn, dst, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
   if (bad) {
     zero_bad_records(T, phys, it * kTile, tid);
     lds_barrier();
@@ -259,7 +268,14 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
       for (int u = 0; u < 2; u++) c2[u] = mfma_bf16(ar[u][ks], Q.qr[ks], c2[u]);
     acc[m0] = c2[0];
     acc[m0 + 1] = c2[1];
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      if (m0 == 0) issue_copies<kCopyA, kCopyB>(cache, phn, dst, wave, lane);
+      else issue_copies<kCopyB, kDmaPerWave>(cache, phn, dst, wave, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
+  static_assert(kMT == 2 || kMT == 4, "one or two pairs of 16-key blocks per tile");
 
   float sv[kMT][4];
 #pragma unroll
@@ -298,6 +314,7 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
       psum += p[mt][i];
     }
   l_part = l_part * alpha + psum;
+  if (more && it + kDepth + 1 < ntiles) read_tile_phys(phys, (it + kDepth + 1) * kTile, wave, lane, phn);
   const int hh = 16 * qw + c16;
   if (g == 0) alpha_p[hh] = alpha;
   const bool any_resc = __any(alpha != 1.f);     // wave-uniform: tells the PV waves to rescale
@@ -505,7 +522,7 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
     }
     if (kDepth < ntiles) read_tile_phys(phl, kDepth * kTile, wave, lane, phn);
 #pragma unroll
-    for (int t = 0; t < kDepth; t++) issue_tile_ph(cache, ph0[t], tl + t * kTileBytes, wave, lane);
+    for (int t = 0; t < kDepth; t++) issue_copies<0, kDmaPerWave>(cache, ph0[t], tl + t * kTileBytes, wave, lane);
   }
 
   // Start of every iteration (both roles, same barriers in the same order): wait for this
