@@ -337,9 +337,21 @@ __device__ __forceinline__ void qk_step(const uint8_t* cache, const DSA_LDS int*
 __device__ __forceinline__ void store_coherent(DSA_GLOBAL float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_coherent(const float* p) {
+__device__ __forceinline__ float load_coherent(const DSA_GLOBAL float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// A row of the stream-K schedule cut between two work-groups: each part knows where both
+// parts' partials go and the slot's tag word (tag null: a split of the split kernel, whose
+// partial always goes to the workspace for k_mla_combine).
+struct CutRow {
+  float* part_o;                 // this part's un-normalised O [64][512] ...
+  float* part_ml;                // ... and per head (m, l); null: a whole row
+  const float* other_o;          // the other part's
+  const float* other_ml;
+  unsigned long long* tag;
+  unsigned long long launch;
+};
 
 // Attention of query row r over keys [j0, j0 + nkeys) of its selection (one segment), as a
 // warp-specialised pipeline: in iteration `it`, waves 0-3 (QK) score tile `it`, run the
@@ -347,15 +359,22 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 // one iteration earlier.  One barrier per iteration.
 //  * QK wave q owns heads 16q..16q+15 over the full 576 contraction dims (q in registers).
 //  * PV wave v owns value dims 128v..128v+127 (value block v) for all 64 heads.
-// The result goes to the bf16 output (and lse) when part_o is null; otherwise it is written
-// as a partial: un-normalised O [64][512], and per head the running max m (log2 units) and
-// the sum l, to part_o / part_ml.  All threads of the work-group call it together.
+// The result goes to the bf16 output (and lse) when cut.part_o is null.  Otherwise the
+// segment is part of a row: its partial is un-normalised O [64][512] and, per head, the running
+// max m (log2 units) and the sum l.  Without a tag it is written to part_o / part_ml.  With a
+// tag (a row cut by the stream-K schedule) the part that finishes second merges: if the
+// slot's tag already holds the launch, the other part is stored and this one combines it with
+// its own O, still in registers, writing no partial of its own; otherwise this part stores its
+// partial, waits for the stores to complete and swaps the launch into the tag, and if the
+// swap returns the launch the other part got in meanwhile and this one merges after all.  The
+// merger clears the tag.  No work-group waits for another.  All threads of the work-group
+// call it together.
 __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, const int32_t* __restrict__ req_in,
                                             const int32_t* __restrict__ pos_in, const DevPages& pg,
                                             const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx_in,
                                             int32_t k, float sm_log2, int r, int j0, int nkeys,
                                             uint16_t* __restrict__ out_in, float* __restrict__ lse_in,
-                                            float* __restrict__ part_o_in, float* __restrict__ part_ml_in) {
+                                            const CutRow& cut) {
   // The stream kernel runs this body out of line, where pointer arguments arrive as generic
   // (flat) pointers; flat accesses count against the LDS counter as well, so every wait for
   // them would also wait for LDS.  Global data is therefore reached through global-space
@@ -366,8 +385,12 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
   const DSA_GLOBAL int32_t* __restrict__ idx = (const DSA_GLOBAL int32_t*)idx_in;
   DSA_GLOBAL uint16_t* __restrict__ out = (DSA_GLOBAL uint16_t*)out_in;
   DSA_GLOBAL float* __restrict__ lse = (DSA_GLOBAL float*)lse_in;
-  DSA_GLOBAL float* __restrict__ part_o = (DSA_GLOBAL float*)part_o_in;
-  DSA_GLOBAL float* __restrict__ part_ml = (DSA_GLOBAL float*)part_ml_in;
+  DSA_GLOBAL float* __restrict__ part_o = (DSA_GLOBAL float*)cut.part_o;
+  DSA_GLOBAL float* __restrict__ part_ml = (DSA_GLOBAL float*)cut.part_ml;
+  const DSA_GLOBAL float* __restrict__ other_o = (const DSA_GLOBAL float*)cut.other_o;
+  const DSA_GLOBAL float* __restrict__ other_ml = (const DSA_GLOBAL float*)cut.other_ml;
+  unsigned long long* const tag = cut.tag;
+  const unsigned long long launch = cut.launch;
   const DSA_GLOBAL int32_t* __restrict__ pt = (const DSA_GLOBAL int32_t*)pg.pt;
   const int64_t pt_stride = pg.pt_stride, num_pages = pg.num_pages;
   const int32_t num_reqs = pg.num_reqs;
@@ -378,6 +401,8 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
   __shared__ float m_s[kHeads], l_s[kHeads];
   __shared__ __attribute__((aligned(16))) int phys[kMaxSplitKeys];
   __shared__ int tile_bad[kMaxSplitKeys / kTile];
+  __shared__ int cut_s[2];                      // cut row: the other part was in / came in
+  __shared__ float wgt_s[kHeads][3];            // merge: weight of this part, of the other, 1 / sum
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -556,15 +581,48 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
     const float l_tot = rows_sum(l_part);
     if (g == 0) { m_s[16 * qw + c16] = m_run; l_s[16 * qw + c16] = l_tot; }
     __syncthreads();
-    if (tid < kHeads) {
-      if (part_o == nullptr) {
-        if (lse != nullptr) {
-          const float l = l_s[tid];
-          lse[(int64_t)r * kHeads + tid] = l > 0.f ? (m_s[tid] + log2f(l)) * 0.69314718055994531f : -INFINITY;
-        }
-      } else {
+    if (part_o == nullptr) {
+      if (tid < kHeads && lse != nullptr) {
+        const float l = l_s[tid];
+        lse[(int64_t)r * kHeads + tid] = l > 0.f ? (m_s[tid] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+      }
+    } else if (tag == nullptr) {
+      if (tid < kHeads) {
         store_coherent(&part_ml[2 * tid], m_s[tid]);
         store_coherent(&part_ml[2 * tid + 1], l_s[tid]);
+      }
+    } else {
+      // the barriers below pair one for one with the PV waves' in the same branches
+      if (tid == 0) cut_s[0] = __hip_atomic_load(tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == launch;
+      __syncthreads();
+      bool merge = cut_s[0] != 0;
+      if (!merge) {
+        if (tid < kHeads) {
+          store_coherent(&part_ml[2 * tid], m_s[tid]);
+          store_coherent(&part_ml[2 * tid + 1], l_s[tid]);
+        }
+        wait_vmcnt<0>();                        // this thread's stores are complete ...
+        __syncthreads();
+        if (tid == 0)                           // ... before the part is tagged
+          cut_s[1] = __hip_atomic_exchange(tag, launch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == launch;
+        __syncthreads();
+        merge = cut_s[1] != 0;
+      }
+      if (merge) {
+        if (tid < kHeads) {
+          const float m0 = m_s[tid], l0 = l_s[tid];
+          const float m1 = load_coherent(&other_ml[2 * tid]), l1 = load_coherent(&other_ml[2 * tid + 1]);
+          const float M = fmaxf(m0, m1);
+          const float f0 = m0 == -INFINITY ? 0.f : exp2f(m0 - M), f1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
+          const float L = l0 * f0 + l1 * f1;
+          wgt_s[tid][0] = f0;
+          wgt_s[tid][1] = f1;
+          wgt_s[tid][2] = L > 0.f ? 1.f / L : 0.f;
+          if (lse != nullptr)
+            lse[(int64_t)r * kHeads + tid] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+        }
+        if (tid == 0) __hip_atomic_store(tag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();                        // weights ready
       }
     }
   } else {
@@ -660,14 +718,51 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
           for (int dt = 0; dt < 8; dt++) orow[16 * dt] = f32_to_bf16_bits(O[ht][dt][i] * inv);
         }
     } else {
+      auto store_part = [&]() {
 #pragma unroll
-      for (int ht = 0; ht < 4; ht++)
+        for (int ht = 0; ht < 4; ht++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int h = 16 * ht + 4 * g + i;
+          for (int i = 0; i < 4; i++) {
+            const int h = 16 * ht + 4 * g + i;
 #pragma unroll
-          for (int dt = 0; dt < 8; dt++) store_coherent(&part_o[(int64_t)h * kVal + 128 * qw + 16 * dt + c16], O[ht][dt][i]);
+            for (int dt = 0; dt < 8; dt++)
+              store_coherent(&part_o[(int64_t)h * kVal + 128 * qw + 16 * dt + c16], O[ht][dt][i]);
+          }
+      };
+      if (tag == nullptr) {
+        store_part();
+      } else {
+        __syncthreads();
+        bool merge = cut_s[0] != 0;
+        if (!merge) {
+          store_part();
+          wait_vmcnt<0>();
+          __syncthreads();
+          __syncthreads();
+          merge = cut_s[1] != 0;
         }
+        if (merge) {
+          __syncthreads();                      // weights ready
+          // head tile by head tile: its 32 coherent loads are issued before any is used
+#pragma unroll
+          for (int ht = 0; ht < 4; ht++) {
+            float ov[4][8];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+              for (int dt = 0; dt < 8; dt++)
+                ov[i][dt] = load_coherent(&other_o[(int64_t)(16 * ht + 4 * g + i) * kVal + 128 * qw + 16 * dt + c16]);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int h = 16 * ht + 4 * g + i;
+              const float f0 = wgt_s[h][0], f1 = wgt_s[h][1], inv = wgt_s[h][2];
+              DSA_GLOBAL uint16_t* orow = out + ((int64_t)r * kHeads + h) * kVal + 128 * qw + c16;
+#pragma unroll
+              for (int dt = 0; dt < 8; dt++) orow[16 * dt] = f32_to_bf16_bits((O[ht][dt][i] * f0 + ov[i][dt] * f1) * inv);
+            }
+          }
+        }
+      }
     }
   }
 }
@@ -682,45 +777,12 @@ k_sparse_mla(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, co
   const int r = blockIdx.y, split = blockIdx.x, nsplit = gridDim.x;
   const int j0 = split * keys_per_split;
   const int nkeys = max(0, min(keys_per_split, k - j0));
-  float* po = nsplit > 1 ? ws_o + ((int64_t)r * nsplit + split) * kHeads * kVal : nullptr;
-  float* pml = nsplit > 1 ? ws_ml + ((int64_t)r * nsplit + split) * kHeads * 2 : nullptr;
-  mla_segment(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse, po, pml);
-}
-
-// Merges the two partials of one row (po: [2][64][512], pml: [2][64][2]) into the bf16
-// output and lse.  512 threads: thread t handles value dim t of every head, so each wave's
-// coherent loads read 256 contiguous bytes; the per-head weights are formed once in LDS.
-__device__ __forceinline__ void merge_two_parts(const float* po, const float* pml, int r, uint16_t* __restrict__ out,
-                                                float* __restrict__ lse) {
-  __shared__ float wgt[kHeads][3];             // per head: weight of part 0, of part 1, 1 / sum
-  const int t = threadIdx.x;
-  if (t < kHeads) {
-    const float m0 = load_coherent(&pml[2 * t]), l0 = load_coherent(&pml[2 * t + 1]);
-    const float m1 = load_coherent(&pml[2 * kHeads + 2 * t]), l1 = load_coherent(&pml[2 * kHeads + 2 * t + 1]);
-    const float M = fmaxf(m0, m1);
-    const float f0 = m0 == -INFINITY ? 0.f : exp2f(m0 - M), f1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
-    const float L = l0 * f0 + l1 * f1;
-    wgt[t][0] = f0;
-    wgt[t][1] = f1;
-    wgt[t][2] = L > 0.f ? 1.f / L : 0.f;
-    if (lse != nullptr) lse[(int64_t)r * kHeads + t] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  CutRow part{};
+  if (nsplit > 1) {
+    part.part_o = ws_o + ((int64_t)r * nsplit + split) * kHeads * kVal;
+    part.part_ml = ws_ml + ((int64_t)r * nsplit + split) * kHeads * 2;
   }
-  __syncthreads();                             // wgt ready
-  uint16_t* ocol = out + (int64_t)r * kHeads * kVal + t;
-  // in two halves of 32 heads: every coherent load of a half is issued before any result is
-  // used or stored, so they are in flight together (atomics keep their order with the stores)
-#pragma unroll
-  for (int h0 = 0; h0 < kHeads; h0 += kHeads / 2) {
-    float va[kHeads / 2], vb[kHeads / 2];
-#pragma unroll
-    for (int h = 0; h < kHeads / 2; h++) va[h] = load_coherent(po + (h0 + h) * kVal + t);
-#pragma unroll
-    for (int h = 0; h < kHeads / 2; h++) vb[h] = load_coherent(po + (kHeads + h0 + h) * kVal + t);
-#pragma unroll
-    for (int h = 0; h < kHeads / 2; h++)
-      ocol[(h0 + h) * kVal] =
-          f32_to_bf16_bits((va[h] * wgt[h0 + h][0] + vb[h] * wgt[h0 + h][1]) * wgt[h0 + h][2]);
-  }
+  mla_segment(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse, part);
 }
 
 // mla_segment as a call: the stream-K kernel runs several segments in a loop, and an
@@ -728,27 +790,28 @@ __device__ __forceinline__ void merge_two_parts(const float* po, const float* pm
 __device__ __attribute__((noinline)) void mla_segment_call(const uint16_t* q, const int32_t* req, const int32_t* pos,
                                                           const DevPages& pg, const uint8_t* cache, const int32_t* idx,
                                                           int32_t k, float sm_log2, int r, int j0, int nkeys,
-                                                          uint16_t* out, float* lse, float* part_o, float* part_ml) {
-  mla_segment(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse, part_o, part_ml);
+                                                          uint16_t* out, float* lse, float* part_o, float* part_ml,
+                                                          const float* other_o, const float* other_ml,
+                                                          unsigned long long* tag, unsigned long long launch) {
+  mla_segment(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse,
+              CutRow{part_o, part_ml, other_o, other_ml, tag, launch});
 }
 
 // Stream-K schedule for R >= gridDim.x: the R x T tiles (T = tiles per row) are cut into
 // gridDim.x equal consecutive ranges, one per work-group, each covering at least one full
 // row; a work-group runs its range as row segments.  A row cut between work-groups g-1 and
-// g (never more than two parts) leaves one partial from each in slot g; each writer waits
-// for its coherent partial stores to complete, then swaps the launch's tag into the slot's
-// tag word, and the writer that gets the tag back is the second: it merges both parts (no
-// work-group ever waits for another) and clears the word again.  Every launch so leaves its
-// slots cleared, which keeps a captured graph correct on every replay (its tag is fixed at
-// capture), and the tag is a random 64-bit value, never 0, so a word left in recycled memory
-// matches it only with probability 2^-64: the workspace needs no initialisation.
+// g (never more than two parts) meets in slot g: the part that finishes second merges the
+// other's stored partial into its own registers (mla_segment) and clears the slot's tag
+// word.  Every launch so leaves its slots cleared, which keeps a captured graph correct on
+// every replay (its tag is fixed at capture), and the tag is a random 64-bit value, never 0,
+// so a word left in recycled memory matches it only with probability 2^-64: the workspace
+// needs no initialisation.
 __global__ void __launch_bounds__(kThreads)
 k_sparse_mla_stream(const uint16_t* __restrict__ q, const int32_t* __restrict__ req, const int32_t* __restrict__ pos,
                     DevPages pg, const uint8_t* __restrict__ cache, const int32_t* __restrict__ idx, int32_t k,
                     int32_t R, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
                     float* __restrict__ ws_o, float* __restrict__ ws_ml, unsigned long long* __restrict__ tag,
                     unsigned long long launch) {
-  __shared__ int s_old;
   const int G = gridDim.x, gi = blockIdx.x;
   const int T = (k + kTile - 1) / kTile;
   const int64_t U = (int64_t)R * T;
@@ -757,30 +820,16 @@ k_sparse_mla_stream(const uint16_t* __restrict__ q, const int32_t* __restrict__ 
     const int r = (int)(u / T), t0 = (int)(u % T);
     const int t1 = (int)(t0 + (u1 - u) < T ? t0 + (u1 - u) : T);
     const int j0 = t0 * kTile, nkeys = min(t1 * kTile, k) - j0;
-    if (t0 == 0 && t1 == T) {
-      mla_segment_call(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse, nullptr, nullptr);
-    } else {
+    CutRow cut{};
+    if (t0 != 0 || t1 != T) {
       const int slot = t0 == 0 ? gi + 1 : gi, part = t0 == 0 ? 0 : 1;
       float* po = ws_o + (int64_t)slot * 2 * kHeads * kVal;
       float* pml = ws_ml + (int64_t)slot * 2 * kHeads * 2;
-      mla_segment_call(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse,
-                       po + (int64_t)part * kHeads * kVal, pml + part * kHeads * 2);
-      wait_vmcnt<0>();                          // this thread's part of the partial is stored ...
-      __syncthreads();
-      if (threadIdx.x == 0) {                   // ... before the part is tagged
-        // exactly two parts per cut row and launch: the first writer swaps the tag in and gets
-        // the slot's old word back; the second gets the tag
-        const unsigned long long old =
-            __hip_atomic_exchange(&tag[slot], launch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_old = old == launch;
-      }
-      __syncthreads();
-      if (s_old) {                              // both parts are in: merge them, clear the slot
-        merge_two_parts(po, pml, r, out, lse);
-        if (threadIdx.x == 0) __hip_atomic_store(&tag[slot], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();
+      cut = CutRow{po + (int64_t)part * kHeads * kVal, pml + part * kHeads * 2,
+                   po + (int64_t)(1 - part) * kHeads * kVal, pml + (1 - part) * kHeads * 2, &tag[slot], launch};
     }
+    mla_segment_call(q, req, pos, pg, cache, idx, k, sm_log2, r, j0, nkeys, out, lse, cut.part_o, cut.part_ml,
+                     cut.other_o, cut.other_ml, cut.tag, cut.launch);
     u += t1 - t0;
   }
 }
