@@ -210,17 +210,30 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
     auto scored_page = [&](int j) -> int64_t { return pg0 + (skip ? (j / (S - 1)) * S + 1 + j % (S - 1) : j); };
     const int nscored = nchunk - nsamp;
     const int nw = nscored > wave ? (nscored - wave + kWaves - 1) / kWaves : 0;
-    int my_id = -1;
-    if (lane < nw) my_id = (int)page_of(pg, rq, scored_page(wave + kWaves * lane) * step * 64);
     // stage q (RG x 32 heads x 128 B, 16-B chunks swizzled by row) and w*q_scale in LDS; the
     // MFMA A operands and head weights are re-read from LDS for every page, which keeps the
-    // register file small enough for four waves per SIMD
-    for (int i = tid; i < RG * kIdxHeads * kIdxDim / 16; i += 256) {
-      const int row = i >> 3, c = i & 7;
-      *reinterpret_cast<i32x4*>(q_lds + qswz(row, c)) =
-          reinterpret_cast<const i32x4*>(q8 + row0 * kIdxHeads * kIdxDim)[i];
+    // register file small enough for four waves per SIMD.  Every load of the staging (RG
+    // chunks of q per thread, one weight and one scale) and the page-table loads are issued
+    // before any of them is used, so the prologue waits one memory round trip, not one per
+    // chunk.
+    constexpr int kQPer = RG * kIdxHeads * kIdxDim / 16 / 256;
+    static_assert(kQPer * 256 * 16 == RG * kIdxHeads * kIdxDim && RG * kIdxHeads <= 256, "staging shares");
+    i32x4 qv[kQPer];
+#pragma unroll
+    for (int u = 0; u < kQPer; u++) qv[u] = reinterpret_cast<const i32x4*>(q8 + row0 * kIdxHeads * kIdxDim)[tid + 256 * u];
+    float wq = 0.f, sq = 0.f;
+    if (tid < RG * kIdxHeads) {
+      wq = w[row0 * kIdxHeads + tid];
+      sq = qs[row0 * kIdxHeads + tid];
     }
-    for (int i = tid; i < RG * kIdxHeads; i += 256) w_lds[i] = w[row0 * kIdxHeads + i] * qs[row0 * kIdxHeads + i];
+    int my_id = -1;
+    if (lane < nw) my_id = (int)page_of(pg, rq, scored_page(wave + kWaves * lane) * step * 64);
+#pragma unroll
+    for (int u = 0; u < kQPer; u++) {
+      const int i = tid + 256 * u, row = i >> 3, c = i & 7;
+      *reinterpret_cast<i32x4*>(q_lds + qswz(row, c)) = qv[u];
+    }
+    if (tid < RG * kIdxHeads) w_lds[tid] = wq * sq;
     __syncthreads();
 
     // running min / max of the order-preserving key of this lane's visible logits over the
