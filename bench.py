@@ -547,6 +547,36 @@ def cpu_baselines(threads):
 
 
 # ----------------------------------------------------------------------------- sections
+def measured_references(torch, dsa, timer, D, n):
+    """Reference rates measured on this device for the access patterns of the two hot kernels:
+    a streaming read of the step's index-K cache (the indexer's scan) and a gather of the 656-B
+    latent records at the positions the step's top-k selected (the sparse MLA's reads), both by
+    the library's probe kernels."""
+    sink = torch.empty(dsa.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    cache = D.index_cache[0]
+    read_b = cache.numel()
+    read_us = timer.calls(lambda i: dsa.dsa_probe_stream_read(cache, sink), n)
+    # physical record index of every selected position: page id * 64 + position within the page
+    pt = D.pages.page_table.long()
+    req = D.rows.req.long()[:, None].expand_as(D.idx)
+    sel = D.idx.long()
+    ok = sel >= 0
+    phys = pt[req, torch.where(ok, sel, 0) >> 6] * 64 + (torch.where(ok, sel, 0) & 63)
+    ids = phys[ok].to(torch.int32).contiguous()
+    pool = D.latent_cache[0]
+    gather_b = ids.numel() * 656
+    gather_us = timer.calls(lambda i: dsa.dsa_probe_gather_records(pool, 656, ids, sink), n)
+    return {"stream_read": {"about": "dsa_probe_stream_read over the step's index-K cache (one full layer)",
+                            "bytes": read_b, "us": round(read_us, 2),
+                            "GBps": round(read_b / (read_us * 1e-6) / 1e9, 1),
+                            "frac_of_nominal": frac(read_b / (read_us * 1e-6) / 1e9)},
+            "record_gather": {"about": "dsa_probe_gather_records: the 656-B latent records at the step's selected "
+                                       "positions (one sparse-MLA launch's reads), each read whole",
+                              "records": int(ids.numel()), "bytes": gather_b, "us": round(gather_us, 2),
+                              "GBps": round(gather_b / (gather_us * 1e-6) / 1e9, 1),
+                              "frac_of_nominal": frac(gather_b / (gather_us * 1e-6) / 1e9)}}
+
+
 def run_c2(torch, dsa, timer, a, stream):
     """The timed step: one c2 layer group per step (K steps after W warm-up steps)."""
     import numpy as np
@@ -611,6 +641,12 @@ def run_c2(torch, dsa, timer, a, stream):
                 "frac": frac(ib / (per["indexer_topk"] * 1e-6) / 1e9), "traffic": None,
                 "algorithmic_bytes_per_launch": ib, "avg_launch_us": round(per["indexer_topk"], 2),
                 "share_of_step": round(per["indexer_topk"] / (ms_step * 1e3), 3)}
+    ref = measured_references(torch, dsa, timer, D, a.steps)
+    # the same kernels against those measured rates: the MLA's 656-B record reads per second
+    # against the record gather, the plain logits' index-K reads against the streaming read
+    mla_rec_gbps = R * 2048 * 656 / (mla_launch_us * 1e-6) / 1e9
+    roof_mla["records_GBps"] = round(mla_rec_gbps, 1)
+    roof_mla["frac_of_measured_gather"] = round(mla_rec_gbps / ref["record_gather"]["GBps"], 4)
     dominant = roof_mla if mla_total >= per["indexer_topk"] else roof_idx
     out = {
         "value": R / (full_us * 1e-6), "ms_per_step": ms_step,
@@ -629,6 +665,8 @@ def run_c2(torch, dsa, timer, a, stream):
                 "plain_logits": {"kernel": "k_logits_decode<6, 0, 0> (dsa_indexer_logits)", "us": round(logits_us, 2),
                                  "GBps": round(ib / (logits_us * 1e-6) / 1e9, 1),
                                  "frac": frac(ib / (logits_us * 1e-6) / 1e9),
+                                 "frac_of_measured_read": round(ib / (logits_us * 1e-6) / 1e9
+                                                                / ref["stream_read"]["GBps"], 4),
                                  "traffic": measured_traffic("c2", "k_logits_decode<6, 0, 0>")},
                 "fused_call": {"kernel": "dsa_indexer_topk (all its kernels)", "us": round(per["indexer_topk"], 2),
                                "GBps": roof_idx["achieved"], "frac": roof_idx["frac"]},
@@ -640,6 +678,7 @@ def run_c2(torch, dsa, timer, a, stream):
             },
             "roofline_mla": roof_mla,
             "roofline_indexer": roof_idx,
+            "measured_reference_rates": ref,
         },
         "_layer": D,
     }
@@ -788,6 +827,29 @@ def run_copy(torch):
             "frac_of_nominal": frac(gbps)}
 
 
+def run_read(torch):
+    """A plain streaming read: torch's sum over 2 GiB of fp32 (bytes read per second), the practical
+    read rate beside the nominal peak (the indexer's index-K scan is a read of this kind)."""
+    x = torch.ones((2 << 30) // 4, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        s = x.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        s = x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    assert abs(float(s) - x.numel()) <= 1e-3 * x.numel()
+    del x
+    torch.cuda.empty_cache()
+    gbps = (2 << 30) / (us * 1e-6) / 1e9
+    return {"about": "torch sum over 2 GiB of fp32, bytes read per second", "GBps": round(gbps, 1),
+            "frac_of_nominal": frac(gbps)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -898,6 +960,7 @@ def main():
               flush=True)
     if "copy" in secs:
         out["hbm_measured_copy"] = run_copy(torch)
+        out["hbm_measured_read"] = run_read(torch)
     if not a.no_cpu_baseline and "c2" in secs:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
         threads = _omp_threads()

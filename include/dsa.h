@@ -331,6 +331,29 @@ dsa_status dsa_sparse_mla_decode_noalloc(const uint16_t* q_bf16, const dsa_rows*
                                          const uint8_t* latent_cache, const int32_t* idx, int32_t k,
                                          float sm_scale, uint16_t* out_bf16, float* lse, void* stream);
 
+/* ---------------------------------------------------------------- reference-rate probes
+ * Not steps of the layer: they measure, on the device at hand, the plain access patterns the
+ * hot kernels perform, so that a kernel's rate can be stated beside a measured one as well as
+ * beside the nominal HBM peak.  Both read every byte they are given once, with non-temporal
+ * 16-B loads, and write the XOR of the words each work-group read to sink[0 ..
+ * DSA_PROBE_SINK_WORDS) (device uint32; every word is written), so that no load is optimised
+ * away: the XOR of the sink's words is the XOR of every word read.  Errors: DSA_ERR_ARG for
+ * sizes or pointers as stated; DSA_ERR_HIP for launch failures.
+ *
+ * dsa_probe_stream_read: `bytes` (a multiple of 16) of device memory at buf (16-B aligned),
+ * as a grid-stride stream of 16-B loads, several in flight per thread: the shape of the
+ * indexer's index-K scan ("GLM-5.3 推理全链路(十一)", section on the read bandwidth).
+ *
+ * dsa_probe_gather_records: the n records of rec_bytes (a multiple of 16) at record indices
+ * ids[0..n) (device int32; values outside [0, pool_records) are clamped into the pool) of
+ * pool (device, 16-B aligned), each read whole: the shape of the sparse MLA's gather of its
+ * selected 656-B latent records ("vLLM 推理链路概览: 以 GLM-5.2 为例", section Sparse MLA
+ * Attention). */
+#define DSA_PROBE_SINK_WORDS 2048
+dsa_status dsa_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+dsa_status dsa_probe_gather_records(const uint8_t* pool, int64_t pool_records, int32_t rec_bytes,
+                                    const int32_t* ids, int64_t n, uint32_t* sink, void* stream);
+
 /* ---------------------------------------------------------------- diagnostics */
 
 /* Synchronises the current device and reports (then clears) the device error flag

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libdsa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["dsa_abi.hip", "k_store.hip", "k_indexer.hip", "k_topk.hip", "k_mla.hip"]
+SOURCES = ["dsa_abi.hip", "k_store.hip", "k_indexer.hip", "k_topk.hip", "k_mla.hip", "k_probe.hip"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-mllvm", "-amdgpu-mfma-vgpr-form=1",     # MFMA results in VGPRs: no AGPR read-back

@@ -384,6 +384,25 @@ dsa_status dsa_sparse_mla_decode_noalloc(const uint16_t* q, const dsa_rows* rows
                     what);
 }
 
+dsa_status dsa_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(DSA_ERR_ARG, "dsa_probe_stream_read: bytes %lld not a multiple of 16", (long long)bytes);
+  if (!buf || !sink) return fail(DSA_ERR_ARG, "dsa_probe_stream_read: NULL pointer");
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(DSA_ERR_ARG, "dsa_probe_stream_read: misaligned pointer");
+  return hip_status(dsa::launch_probe_stream_read(buf, bytes, sink, (hipStream_t)stream), "dsa_probe_stream_read");
+}
+
+dsa_status dsa_probe_gather_records(const uint8_t* pool, int64_t pool_records, int32_t rec_bytes, const int32_t* ids,
+                                    int64_t n, uint32_t* sink, void* stream) {
+  if (n < 0 || pool_records < 1 || rec_bytes < 16 || rec_bytes % 16)
+    return fail(DSA_ERR_ARG, "dsa_probe_gather_records: n %lld, pool_records %lld, rec_bytes %d", (long long)n,
+                (long long)pool_records, rec_bytes);
+  if (!pool || !ids || !sink) return fail(DSA_ERR_ARG, "dsa_probe_gather_records: NULL pointer");
+  if (!aligned(pool, 16) || !aligned(ids, 4) || !aligned(sink, 4))
+    return fail(DSA_ERR_ARG, "dsa_probe_gather_records: misaligned pointer");
+  return hip_status(dsa::launch_probe_gather_records(pool, pool_records, rec_bytes, ids, n, sink, (hipStream_t)stream),
+                    "dsa_probe_gather_records");
+}
+
 dsa_status dsa_check_device_errors(void) {
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_status(e, "dsa_check_device_errors");

@@ -111,6 +111,11 @@ hipError_t launch_sparse_mla(const uint16_t* q, RowsView rows, PagesView pg, con
                              const int32_t* idx, int32_t k, float sm_scale, uint16_t* out, float* lse,
                              void* ws, size_t ws_bytes, bool prefill, hipStream_t s);
 
+// Reference-rate probes of the benchmark (k_probe.hip).
+hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_gather_records(const uint8_t* pool, int64_t pool_records, int32_t rec_bytes,
+                                       const int32_t* ids, int64_t n, uint32_t* sink, hipStream_t s);
+
 // Read-and-clear of each translation unit's device error flag (synchronous).
 int take_device_errors_store();
 int take_device_errors_indexer();

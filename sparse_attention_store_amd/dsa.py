@@ -21,6 +21,7 @@ INDEX_PAGE_BYTES = 8448
 INDEX_MXFP4_PAGE_BYTES = 4352
 LATENT_PAGE_BYTES = 41984
 TOPK_MAX = 2048
+PROBE_SINK_WORDS = 2048
 
 _STATUS = {0: "DSA_OK", 1: "DSA_ERR_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
            4: "DSA_ERR_HIP", 5: "DSA_ERR_DEVICE_CHECK"}
@@ -80,6 +81,8 @@ def _load():
         "dsa_sparse_mla_decode": ([p, R, P, p, p, i32, f32, p, p, p, sz, p], ctypes.c_int),
         "dsa_sparse_mla_prefill": ([p, R, P, p, p, i32, f32, p, p, p, sz, p], ctypes.c_int),
         "dsa_sparse_mla_decode_noalloc": ([p, R, P, p, p, i32, f32, p, p, p], ctypes.c_int),
+        "dsa_probe_stream_read": ([p, i64, p, p], ctypes.c_int),
+        "dsa_probe_gather_records": ([p, i64, i32, p, i64, p, p], ctypes.c_int),
         "dsa_check_device_errors": ([], ctypes.c_int),
     }
     for name, (args, ret) in sigs.items():
@@ -97,7 +100,7 @@ EXPORTED = ("dsa_abi_version", "dsa_last_error", "dsa_layer_is_shared", "dsa_mtp
             "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_mxfp4", "dsa_set_topk_direct_limit",
             "dsa_sparse_mla_workspace_size",
             "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_sparse_mla_decode_noalloc",
-            "dsa_check_device_errors")
+            "dsa_probe_stream_read", "dsa_probe_gather_records", "dsa_check_device_errors")
 
 
 def _check(st: int):
@@ -278,6 +281,16 @@ def dsa_sparse_mla_decode_noalloc(q, rows: Rows, pages: Pages, latent_cache, idx
     r, p = rows.c(), pages.c()
     _check(_lib.dsa_sparse_mla_decode_noalloc(_ptr(q), ctypes.byref(r), ctypes.byref(p), _ptr(latent_cache), _ptr(idx),
                                               idx.shape[-1], sm_scale, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def dsa_probe_stream_read(buf, sink, stream=None):
+    _check(_lib.dsa_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def dsa_probe_gather_records(pool, rec_bytes: int, ids, sink, stream=None):
+    nbytes = pool.numel() * pool.element_size()
+    _check(_lib.dsa_probe_gather_records(_ptr(pool), nbytes // rec_bytes, rec_bytes, _ptr(ids), ids.numel(), _ptr(sink),
+                                         _stream(stream)))
 
 
 def dsa_check_device_errors():

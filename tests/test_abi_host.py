@@ -147,6 +147,12 @@ def test_argument_errors(lib):
     _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000), q_pe=_Fake(0x10000, (4, 64, 64), 2, (64 * 48, 48, 1)))
     _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000), rms_eps=-1.0)
     _expect(lib, 1, fused, kv, rows, pt, _Fake(0xA000), index_rope_theta=0.0)
+    # reference-rate probes: sizes that are not whole 16-B chunks, misaligned or null pointers
+    _expect(lib, 1, lib.dsa_probe_stream_read, _Fake(0x1000, (20,), 1), _Fake(0x2000))
+    _expect(lib, 1, lib.dsa_probe_stream_read, _Fake(0x1008, (64,), 1), _Fake(0x2000))
+    _expect(lib, 1, lib.dsa_probe_stream_read, _Fake(0x1000, (64,), 1), _Fake(0))
+    _expect(lib, 1, lib.dsa_probe_gather_records, _Fake(0x1000, (6560,), 1), 650, _Fake(0x2000, (4,), 4), _Fake(0x3000))
+    _expect(lib, 1, lib.dsa_probe_gather_records, _Fake(0x1000, (6560,), 1), 656, _Fake(0x2002, (4,), 4), _Fake(0x3000))
     # a shared layer (no index-K cache) makes store and logits a successful no-op
     lib.dsa_index_k_store(_Fake(0x9000), rows, pt, None)
     lib.dsa_indexer_logits(_Fake(0x7000), _Fake(0x7100), _Fake(0x7200), rows, pt, None, logits)
