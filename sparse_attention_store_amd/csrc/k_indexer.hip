@@ -340,7 +340,26 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
       int ida = page_id(0);
       load_page(pa, page_addr(ida), lane);
       int i = 0;
+      // The filter pass runs its work-groups in at most two rounds (four resident per CU).
+      // Issue arbitration favours the oldest waves, so the four groups on a CU used to finish
+      // staggered (page loops of 57-113 us for the same 60 pages in the first round) and the
+      // last second-round groups ran alone at the end: a 39-us tail on a 214-us pass.  A wave's
+      // priority now falls in four steps as it gets through its pages, so the groups started
+      // together finish together (span 205 us; the fused call at c2 -1.6%).  Passes of more
+      // rounds balance by dispatch and keep the default priority.
+      const bool fair = KIND == kLogitsFilter && gridDim.x * gridDim.y <= 2 * 4 * 256;
+      int level = 3;
+      if (fair) __builtin_amdgcn_s_setprio(3);
       for (; i + 1 < nw; i += 2) {
+        if (fair) {
+          const int want = 3 - (4 * i) / nw;
+          if (want != level) {
+            level = want;
+            if (want == 2) __builtin_amdgcn_s_setprio(2);
+            else if (want == 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+          }
+        }
         const int idb = page_id(i + 1);
         load_page(pb, page_addr(idb), lane);
         process(pa, page_vi(i), ida);
@@ -349,6 +368,7 @@ k_logits_decode(const uint8_t* __restrict__ q8, const float* __restrict__ qs, co
         process(pb, page_vi(i + 1), idb);
       }
       if (i < nw) process(pa, page_vi(i), ida);     // an odd page count: the last page
+      if (fair) __builtin_amdgcn_s_setprio(0);
     }
     // the sampled pages of the chunk: their stored scores against the threshold (a page of a
     // bad id holds -inf: a visible key's score is finite, and the scored path never stages those,
