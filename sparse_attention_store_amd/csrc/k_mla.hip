@@ -742,23 +742,31 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
           merge = cut_s[1] != 0;
         }
         if (merge) {
-          __syncthreads();                      // weights ready
-          // head tile by head tile: its 32 coherent loads are issued before any is used
-#pragma unroll
-          for (int ht = 0; ht < 4; ht++) {
-            float ov[4][8];
+          // the other part's partial, head tile by head tile (32 coherent loads each) with two
+          // tiles in flight; the first is requested before the weights are ready (this side of
+          // that barrier waits for LDS only, so the loads stay in flight across it)
+          float ov[2][4][8];
+          auto load_other = [&](int ht, float (&dst)[4][8]) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
               for (int dt = 0; dt < 8; dt++)
-                ov[i][dt] = load_coherent(&other_o[(int64_t)(16 * ht + 4 * g + i) * kVal + 128 * qw + 16 * dt + c16]);
+                dst[i][dt] = load_coherent(&other_o[(int64_t)(16 * ht + 4 * g + i) * kVal + 128 * qw + 16 * dt + c16]);
+          };
+          load_other(0, ov[0]);
+          lds_barrier();                        // weights ready
+          __asm__ volatile("" ::: "memory");    // (for the compiler: the weight reads stay below)
+#pragma unroll
+          for (int ht = 0; ht < 4; ht++) {
+            if (ht + 1 < 4) load_other(ht + 1, ov[(ht + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < 4; i++) {
               const int h = 16 * ht + 4 * g + i;
               const float f0 = wgt_s[h][0], f1 = wgt_s[h][1], inv = wgt_s[h][2];
               DSA_GLOBAL uint16_t* orow = out + ((int64_t)r * kHeads + h) * kVal + 128 * qw + c16;
 #pragma unroll
-              for (int dt = 0; dt < 8; dt++) orow[16 * dt] = f32_to_bf16_bits((O[ht][dt][i] * f0 + ov[i][dt] * f1) * inv);
+              for (int dt = 0; dt < 8; dt++)
+                orow[16 * dt] = f32_to_bf16_bits((O[ht][dt][i] * f0 + ov[ht & 1][i][dt] * f1) * inv);
             }
           }
         }
