@@ -706,6 +706,15 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
     }
     __syncthreads();                            // m_s / l_s written by the QK waves
     if (part_o == nullptr) {
+      // the row's output goes through LDS (the tile buffers are idle once every PV step is
+      // done): this wave's 64 heads x 128 dims as bf16 at a 272-B row pitch (the four head
+      // groups of a store land in different banks), then 16-B pieces, 16 lanes to a head row,
+      // instead of one 2-B global store per value.  The wave reads back only what it wrote, and
+      // its LDS accesses complete in order, so no barrier is needed.  (The merging part of a cut
+      // row keeps its direct stores: staged, it measured slower.)
+      constexpr int kPitch = 272;
+      static_assert(4 * kHeads * kPitch <= kBufs * kTileBytes, "the staging fits the tile buffers");
+      DSA_LDS uint8_t* st = tl + qw * (kHeads * kPitch);
 #pragma unroll
       for (int ht = 0; ht < 4; ht++)
 #pragma unroll
@@ -713,10 +722,17 @@ __device__ __forceinline__ void mla_segment(const uint16_t* __restrict__ q_in, c
           const int h = 16 * ht + 4 * g + i;
           const float l = l_s[h];
           const float inv = l > 0.f ? 1.f / l : 0.f;
-          DSA_GLOBAL uint16_t* orow = out + ((int64_t)r * kHeads + h) * kVal + 128 * qw + c16;
 #pragma unroll
-          for (int dt = 0; dt < 8; dt++) orow[16 * dt] = f32_to_bf16_bits(O[ht][dt][i] * inv);
+          for (int dt = 0; dt < 8; dt++)
+            *reinterpret_cast<DSA_LDS uint16_t*>(st + h * kPitch + 2 * (16 * dt + c16)) =
+                f32_to_bf16_bits(O[ht][dt][i] * inv);
         }
+#pragma unroll
+      for (int kk = 0; kk < kHeads / 4; kk++) {
+        const int h = 4 * kk + (lane >> 4);
+        const i32x4 v = *reinterpret_cast<const DSA_LDS i32x4*>(st + h * kPitch + 16 * (lane & 15));
+        *reinterpret_cast<DSA_GLOBAL i32x4*>(out + ((int64_t)r * kHeads + h) * kVal + 128 * qw + 8 * (lane & 15)) = v;
+      }
     } else {
       auto store_part = [&]() {
 #pragma unroll
